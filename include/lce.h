@@ -1,0 +1,125 @@
+/*
+ * lce.h -- C ABI of the MI355X (gfx950) vocabulary cross-entropy library.
+ *
+ * Every entry point takes plain pointers and sizes.  "device" pointers are
+ * HIP device memory owned by the caller; the library allocates nothing, keeps
+ * no state between calls apart from the thread-local error text, and never
+ * synchronises the host: work is enqueued on `stream` and its outputs are
+ * valid once that stream has been synchronised.  Calls on different streams
+ * are independent as long as their buffers do not overlap.
+ *
+ * Errors: arguments are checked before any HIP call.  A bad argument returns
+ * LCE_ERR_INVALID_ARG, a valid but unsupported combination returns
+ * LCE_ERR_UNSUPPORTED (the message names the constraint), a failed launch
+ * returns LCE_ERR_HIP.  No exception crosses this boundary.  lce_last_error()
+ * explains the most recent failure on the calling thread.
+ *
+ * The operations follow these pages (cited by title and section):
+ *  [P1] Liger-Kernel PR "Add Megatron-LM cross-entropy integration": Summary
+ *       (ignore_index=-100, label_smoothing, online softmax with the gradient
+ *       written in place and no full softmax kept) and Test setup (the same
+ *       operation as torch.nn.functional.cross_entropy).
+ *  [P2] Megatron-LM PR "Add opt-in Liger vocab-parallel cross entropy": "What
+ *       does this PR do?" (fp32 per-token losses, any upstream gradient,
+ *       original argmax with smallest-index ties) and Performance (the input
+ *       is consumed, so benchmarks clone it outside the timed region).
+ *  [P5] Liger-Kernel PR "Add Liger Kernel support for Muse Glimmer": Summary
+ *       (fused linear cross-entropy that never forms the [tokens, V] logits;
+ *       token accuracy), Details/Softcap (T*tanh(x/T), the output multiplier
+ *       folded into hidden by the caller) and Memory (grad_weight kept in fp32).
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LCE_OK = 0,
+    LCE_ERR_INVALID_ARG = 1,
+    LCE_ERR_UNSUPPORTED = 2,
+    LCE_ERR_HIP = 3
+} lce_status;
+
+typedef enum { LCE_F32 = 0, LCE_BF16 = 1 } lce_dtype;
+
+typedef enum { LCE_RED_NONE = 0, LCE_RED_MEAN = 1, LCE_RED_SUM = 2 } lce_reduction;
+
+/*
+ * Bytes of device workspace lce_ce_fwd_bwd needs for n rows of V columns.
+ * Always > 0 (it holds the completion counter of the final reduction).
+ */
+size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
+
+/*
+ * Cross-entropy forward + backward over a [n, V] logits matrix, gradient
+ * written in place [P1 Summary; P2 "What does this PR do?"; P5 Details].
+ *
+ * For row i with label y_i (valid iff y_i != ignore_index and 0 <= y_i < V),
+ * z = softcap > 0 ? softcap*tanh(x/softcap) : x, eps = label_smoothing:
+ *   loss_i = LSE(z_i) - (1-eps) z_{i,y_i} - (eps/V) sum_j z_ij  (0 if invalid)
+ *   dx_ij  = s_i (softmax(z_i)_j - (1-eps)[j==y_i] - eps/V) dz_ij/dx_ij (0 if invalid)
+ * with s_i = g/n_valid (MEAN; 0 when n_valid == 0), g (SUM) or g_i (NONE),
+ * g = grad_out (1.0 when grad_out is NULL).
+ *
+ *   logits_inout  device, [n, ld] row-major, dtype F32 or BF16.  Read as the
+ *                 logits and overwritten with dx, rounded to nearest-even in
+ *                 the same dtype.  Columns [V, ld) are neither read nor
+ *                 written.  The buffer is consumed: request the argmax in
+ *                 this same call if it is wanted.
+ *   ld            row stride in elements, >= V.
+ *   labels        device int64 [n].  Labels outside [0, V) other than
+ *                 ignore_index are treated as ignored and counted in counts[2].
+ *   label_smoothing  eps in [0, 1].    softcap  T >= 0 (0 = off).
+ *   grad_out      device fp32: 1 element (MEAN/SUM) or [n] (NONE); NULL = 1.0.
+ *   loss_tok      device fp32 [n], required: per-token losses (0 if ignored).
+ *   loss_out      device fp32 scalar or NULL: mean over valid tokens (0 when
+ *                 there are none) or sum.  Written as 0 for NONE.
+ *   argmax_out    device int64 [n] or NULL: smallest index of the row maximum
+ *                 of the raw logits, for every row (ignored rows included).
+ *   counts        device int64 [3], required: {n_valid, n_correct, n_bad};
+ *                 n_correct = #{valid i : argmax_i == y_i} (0 when argmax_out
+ *                 is NULL).  Token accuracy = n_correct / n_valid.
+ *   workspace     device scratch of at least lce_ce_workspace_bytes(n, V)
+ *                 bytes, 16-byte aligned; clobbered.
+ * loss_tok, argmax_out, counts, workspace and loss_out must not overlap the
+ * logits or each other.  n == 0 is valid (counts and loss_out become 0).
+ */
+lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels,
+                          int64_t n, int64_t V, int64_t ignore_index, float label_smoothing,
+                          float softcap, lce_reduction reduction, const float *grad_out,
+                          float *loss_tok, float *loss_out, int64_t *argmax_out, int64_t *counts,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Read-only argmax sweep [P2 "What does this PR do?"; P5 Summary]: argmax_out[i]
+ * = smallest index of the maximum of row i of the raw logits, for every row.
+ *   logits      device [n, ld], F32 or BF16, not modified.
+ *   labels      device int64 [n] or NULL.  With labels, counts = {n_valid,
+ *               n_correct, n_bad}; without, counts = {0, 0, 0}.
+ *   argmax_out  device int64 [n], required.   counts  device int64 [3], required.
+ */
+lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const int64_t *labels,
+                         int64_t n, int64_t V, int64_t ignore_index, int64_t *argmax_out,
+                         int64_t *counts, hipStream_t stream);
+
+/*
+ * Text of the most recent error on the calling thread ("" if none).  Valid
+ * until the next lce_* call on the same thread.
+ */
+const char *lce_last_error(void);
+
+/* Library ABI version (bumped on any signature change). */
+int lce_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

@@ -29,8 +29,8 @@
  *
  * Readings where the pages are silent (each is also listed in the design
  * notes of the repository):
- *  - softcap T == 0 means "off"; its derivative is 1 - tanh^2(x/T) (chain rule
- *    on T*tanh(x/T)).
+ *  - softcap T == 0 means "off"; its derivative is sech^2(x/T) = 1 - tanh^2(x/T)
+ *    (chain rule on T*tanh(x/T)).
  *  - a label outside [0, V) that is not ignore_index is counted as "bad" and
  *    treated exactly like an ignored token.
  *  - mean over zero valid tokens gives loss 0 and all-zero gradients.
@@ -180,8 +180,10 @@ static void ce_row(const double *x, int64_t V, int64_t y, int valid, double eps,
         }
         double chain = 1.0;
         if (T > 0.0) {
-            double t = tanh(x[j] / T);
-            chain = 1.0 - t * t;            /* d(T tanh(x/T))/dx */
+            /* d(T tanh(x/T))/dx = sech^2(x/T) = 1 - tanh^2(x/T); the sech form keeps
+             * its value where 1 - tanh^2 would cancel to 0 (|x/T| > ~19) */
+            double c = cosh(x[j] / T);
+            chain = 1.0 / (c * c);
         }
         grad[j] = scale * dz * chain;
     }

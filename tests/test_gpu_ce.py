@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Every case is seeded and synthetic.  Small cases compare every output; the full-size
+workloads compare sampled rows (the oracle regenerates them) plus the reduced loss over all
+rows and properties that hold at any size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import check_bf16_grad, check_f32_grad, check_loss, row_scales, smoothing_allowance
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible to torch", allow_module_level=True)
+
+import vocabulary_cross_entropy_row_amd as lce  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(x: np.ndarray):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def from_dev(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def make_logits(rng, n, V, ld, dtype, sigma=2.0):
+    x = (rng.standard_normal((n, ld)) * sigma).astype(np.float32)
+    return synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def run_and_check(x: np.ndarray, y: np.ndarray, V: int, *, eps=0.0, T=0.0, red="mean", grad_out=None,
+                  want_argmax=False, rows=None, full_loss=True):
+    """Run the GPU op on a copy of x ([n, ld]) and compare with the oracle."""
+    n, ld = x.shape
+    dt = "bf16" if x.dtype == np.uint16 else "f32"
+    buf = to_dev(x)
+    view = buf[:, :V]
+    lab = torch.from_numpy(y.astype(np.int64)).to(DEV)
+    g_dev = None
+    if grad_out is not None:
+        g_dev = torch.from_numpy(np.asarray(grad_out, dtype=np.float32).reshape(-1)).to(DEV)
+    res = lce.lce_ce_fwd_bwd(view, lab, label_smoothing=eps, softcap=T, reduction=red, grad_out=g_dev,
+                             want_argmax=want_argmax)
+    torch.cuda.synchronize()
+    out = from_dev(buf)
+    loss_tok = res.loss_tok.cpu().numpy()
+    loss_out = float(res.loss_out.cpu().numpy()[0])
+    counts = res.counts.cpu().numpy()
+    amax = res.argmax.cpu().numpy() if want_argmax else None
+
+    orc = oracle.default()
+    o = orc.ce(x, y, V=V, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out, rows=rows,
+               want_grad=True)
+    idx = np.arange(n) if rows is None else np.asarray(rows)
+    check_loss(loss_tok[idx], o["loss_tok"], "loss_tok")
+    nv, nb = orc.count(y, V)
+    assert counts[0] == nv and counts[2] == nb, f"counts {counts} vs n_valid={nv} n_bad={nb}"
+    if full_loss:
+        full = o if rows is None else orc.ce(x, y, V=V, label_smoothing=eps, softcap=T, reduction=red,
+                                             grad_out=grad_out, want_grad=False)
+        want = full["loss_out"] if red != "none" else 0.0
+        check_loss(loss_out, want, "loss_out")
+    if want_argmax:
+        assert np.array_equal(amax[idx], o["argmax"]), "argmax differs"
+        if rows is None:
+            assert counts[1] == o["counts"][1], f"n_correct {counts[1]} vs {o['counts'][1]}"
+    else:
+        assert counts[1] == 0
+    g = out[idx, :V]
+    if dt == "bf16":
+        allow = smoothing_allowance(row_scales(red, grad_out, y, V)[idx], eps, V)
+        n_allow = check_bf16_grad(g, o["grad"], orc, allow=allow)
+        # the cancellation allowance is for isolated elements with p_j ~ eps/V only
+        assert n_allow <= max(4, g.size // 1000), f"{n_allow} of {g.size} entries needed the allowance"
+    else:
+        check_f32_grad(g, o["grad"], row_scales(red, grad_out, y, V)[idx])
+    if ld > V:   # padding columns are never touched
+        assert np.array_equal(out[:, V:].view(np.uint8), x[:, V:].view(np.uint8)), "padding modified"
+    return res, out
+
+
+# ----------------------------------------------------------------------------- small matrix
+
+def _labels(rng, n, V, ignore_frac=0.1, bad=0):
+    y = rng.integers(0, V, n).astype(np.int64)
+    k = int(round(ignore_frac * n))
+    y[rng.permutation(n)[:k]] = -100
+    if bad:
+        pos = rng.permutation(n)[:bad]
+        y[pos[::2]] = V + 3
+        y[pos[1::2]] = -7
+    return y
+
+
+SHAPES = [  # (n, V, ld, dtype): register path with full / partial last round, K > 16, generic path
+    (64, 4096, 4096, "f32"),
+    (64, 4096, 4096, "bf16"),
+    (32, 8 * 1024 + 8 * 37, 8 * 1024 + 8 * 37, "bf16"),
+    (16, 32768, 32768 + 64, "bf16"),
+    (8, 131072, 131072, "bf16"),
+    (6, 8 * 1024 * 18 + 8 * 5, 8 * 1024 * 18 + 8 * 5, "bf16"),    # K=19 (template 20)
+    (4, 202048, 202048, "bf16"),                                    # K=25 (template 26)
+    (16, 4099, 4099, "bf16"),                                       # generic (V odd)
+    (16, 4096, 4100, "f32"),                                        # fast: ld multiple of 4
+    (16, 4096, 4098, "bf16"),                                       # generic (ld not a multiple of 8)
+    (16, 1000, 1000, "f32"),
+    (8, 60000, 60000, "f32"),                                       # f32 K=15
+    (4, 120000, 120000, "f32"),                                     # f32 too wide -> generic
+]
+
+
+@pytest.mark.parametrize("n,V,ld,dt", SHAPES, ids=[f"{s[0]}x{s[1]}ld{s[2]}{s[3]}" for s in SHAPES])
+@pytest.mark.parametrize("feat", ["plain", "smooth_sum", "cap_argmax_none", "all"])
+def test_small_matrix(n, V, ld, dt, feat):
+    rng = np.random.default_rng([n, V, ld, len(feat)])
+    x = make_logits(rng, n, V, ld, dt, sigma=4.0 if "cap" in feat or feat == "all" else 2.0)
+    if ld > V:
+        x[:, V:] = np.uint16(0x7FC1) if dt == "bf16" else np.float32(np.nan)
+    y = _labels(rng, n, V, bad=2 if feat == "all" else 0)
+    kw = dict(plain=dict(), smooth_sum=dict(eps=0.1, red="sum", grad_out=[0.5]),
+              cap_argmax_none=dict(T=5.0, red="none", grad_out=rng.normal(size=n), want_argmax=True),
+              all=dict(eps=0.2, T=30.0, red="mean", grad_out=[1.5], want_argmax=True))[feat]
+    run_and_check(x, y, V, **kw)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def test_c1_full():
+    w = synth.C1
+    y = synth.labels(w)
+    x = synth.logits(w, y)
+    run_and_check(x, y, w.V)
+
+
+def test_n_zero():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    lab = torch.zeros(0, dtype=torch.int64, device=DEV)
+    res = lce.lce_ce_fwd_bwd(x, lab)
+    torch.cuda.synchronize()
+    assert res.counts.cpu().tolist() == [0, 0, 0]
+    assert float(res.loss_out.cpu()[0]) == 0.0
+
+
+def test_single_row_and_v1_v2():
+    rng = np.random.default_rng(5)
+    for V in (1, 2, 3, 8, 16):
+        for dt in ("f32", "bf16"):
+            x = make_logits(rng, 1, V, V, dt)
+            run_and_check(x, np.array([V - 1]), V, want_argmax=True)
+            run_and_check(x, np.array([0]), V, eps=0.3, T=2.0, red="sum")
+
+
+def test_all_ignored_mean_is_zero():
+    rng = np.random.default_rng(6)
+    x = make_logits(rng, 8, 4096, 4096, "bf16")
+    res, out = run_and_check(x, np.full(8, -100), 4096, want_argmax=True)
+    assert np.all(out.view(np.int16) & 0x7FFF == 0)
+
+
+def test_label_dominated_rows():
+    """p_y -> 1: the target gradient -(1 - p_y) s must keep its relative precision."""
+    rng = np.random.default_rng(7)
+    V = 8192
+    x = rng.standard_normal((6, V)).astype(np.float32)
+    y = np.array([5, 100, 4000, 8191, 0, 77])
+    for i, m in enumerate((20.0, 35.0, 50.0, 60.0, 70.0, 80.0)):
+        x[i, y[i]] = m
+    for dt in ("f32", "bf16"):
+        xx = x if dt == "f32" else synth.f32_to_bf16_bits(x)
+        run_and_check(xx, y, V, red="sum")
+        run_and_check(xx, y, V, red="sum", eps=0.05)
+
+
+def test_uniform_rows_give_log_v():
+    V = 131072
+    x = np.zeros((4, V), dtype=np.uint16)
+    x[1] = synth.f32_to_bf16_bits(np.full(V, 3.0, np.float32))
+    y = np.array([0, 5, V - 1, -100])
+    res, _ = run_and_check(x, y, V, eps=0.1, want_argmax=True)
+    lt = res.loss_tok.cpu().numpy()
+    assert np.allclose(lt[:3], np.log(V), rtol=1e-6)
+
+
+def test_bad_labels_counted():
+    rng = np.random.default_rng(8)
+    x = make_logits(rng, 32, 2048, 2048, "bf16")
+    y = _labels(rng, 32, 2048, bad=6)
+    res, _ = run_and_check(x, y, 2048, want_argmax=True)
+    assert int(res.counts.cpu()[2]) == 6
+
+
+def test_argmax_ties_quantised():
+    rng = np.random.default_rng(9)
+    V = 202048
+    x = np.clip(np.rint(rng.normal(0, 10, size=(6, V))), -4, 4).astype(np.float32)
+    y = np.argmax(x, axis=1)
+    y[1] = 5
+    xb = synth.f32_to_bf16_bits(x)
+    run_and_check(xb, y, V, T=30.0, want_argmax=True)
+    am, counts = lce.lce_ce_argmax(to_dev(xb), torch.from_numpy(y).to(DEV))
+    torch.cuda.synchronize()
+    want = np.array([np.flatnonzero(r == r.max())[0] for r in x])
+    assert np.array_equal(am.cpu().numpy(), want)
+    assert counts.cpu().tolist() == [6, 5, 0]
+
+
+@pytest.mark.parametrize("dt,V,ld", [("bf16", 131072, 131072), ("bf16", 4099, 4101), ("f32", 4096, 4096),
+                                     ("f32", 1001, 1003)])
+def test_argmax_entry_point(dt, V, ld):
+    rng = np.random.default_rng([V, ld])
+    x = make_logits(rng, 24, V, ld, dt)
+    x[3, :V] = x[3, 0]   # a constant row: index 0
+    y = _labels(rng, 24, V, bad=2)
+    buf = to_dev(x)
+    am, counts = lce.lce_ce_argmax(buf[:, :V], torch.from_numpy(y).to(DEV))
+    torch.cuda.synchronize()
+    o = oracle.ce(x, y, V=V, want_grad=False)
+    assert np.array_equal(am.cpu().numpy(), o["argmax"])
+    assert counts.cpu().tolist() == o["counts"].tolist()
+    assert np.array_equal(from_dev(buf).view(np.uint8), x.view(np.uint8)), "argmax must not write the logits"
+
+
+def test_deterministic_replay():
+    w = synth.C2
+    rng = np.random.default_rng(10)
+    x = make_logits(rng, 256, w.V, w.V, "bf16")
+    y = _labels(rng, 256, w.V)
+    outs = []
+    for _ in range(2):
+        buf = to_dev(x)
+        res = lce.lce_ce_fwd_bwd(buf, torch.from_numpy(y).to(DEV), want_argmax=True)
+        torch.cuda.synchronize()
+        outs.append((from_dev(buf), res.loss_tok.cpu().numpy(), res.loss_out.cpu().numpy(), res.argmax.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def _sample_rows(w, y, k=24, seed=0):
+    rng = np.random.default_rng(seed)
+    ign = np.flatnonzero(y == -100)
+    rows = set(rng.choice(w.n, size=k, replace=False).tolist())
+    rows.update(ign[:2].tolist())
+    rows.update([0, w.n - 1])
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("w", [synth.C2, synth.C3, synth.C4], ids=lambda w: w.name)
+def test_full_size_workload(w):
+    """The full workload in the launch configuration the bench times; sampled rows compared
+    element by element, the reduced loss over every row, and the accuracy counts exactly."""
+    y = synth.labels(w)
+    x = synth.logits(w, y)
+    rows = _sample_rows(w, y)
+    res, out = run_and_check(x, y, w.V, eps=w.label_smoothing, T=w.softcap, red=w.reduction,
+                             grad_out=[w.grad_out], want_argmax=w.want_argmax, rows=rows)
+    if w.want_argmax:
+        o = oracle.ce(x, y, V=w.V, label_smoothing=w.label_smoothing, softcap=w.softcap, want_grad=False)
+        assert np.array_equal(res.argmax.cpu().numpy(), o["argmax"])
+        assert int(res.counts.cpu()[1]) == int(o["counts"][1])
+    if w.softcap == 0:
+        # property at any size: every valid row's gradient sums to ~0 (no cap)
+        g = torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).to(DEV).float()
+        rs = g.sum(dim=1).abs().max().item()
+        assert rs < 1e-5, rs

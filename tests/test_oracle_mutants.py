@@ -25,7 +25,8 @@ MUTANTS = [
      "dz = (s_other / s) + eps - eps / (double)V;"),
     ("drop eps/V from the off-target gradient", "dz = exp(z[j] - lse) - eps / (double)V;",
      "dz = exp(z[j] - lse);"),
-    ("drop the softcap chain factor", "chain = 1.0 - t * t;", "chain = 1.0;"),
+    ("drop the softcap chain factor", "chain = 1.0 / (c * c);", "chain = 1.0;"),
+    ("chain factor sech instead of sech^2", "chain = 1.0 / (c * c);", "chain = 1.0 / c;"),
     ("softcap without the T multiplier", "T > 0.0 ? T * tanh(x[j] / T) : x[j]", "T > 0.0 ? tanh(x[j] / T) : x[j]"),
     ("argmax keeps the last tied index", "if (x[j] > x[am]) am = j;", "if (x[j] >= x[am]) am = j;"),
     ("mean forgets to divide by n_valid", "return n_valid > 0 ? g / (double)n_valid : 0.0;",

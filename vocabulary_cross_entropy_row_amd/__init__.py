@@ -1,0 +1,153 @@
+"""Python binding of liblce.so, the MI355X vocabulary cross-entropy library.
+
+The functions carry the names of the C entry points in include/lce.h and only
+marshal arguments: every step of the computation runs in the HIP kernels of
+liblce.so.  PyTorch supplies device memory and the current HIP stream.  There
+is no CPU fallback: if the library is missing this module raises on import of
+the function table (``lib()``), and every call goes to the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblce.so")
+
+LCE_OK, LCE_ERR_INVALID_ARG, LCE_ERR_UNSUPPORTED, LCE_ERR_HIP = 0, 1, 2, 3
+LCE_F32, LCE_BF16 = 0, 1
+LCE_RED_NONE, LCE_RED_MEAN, LCE_RED_SUM = 0, 1, 2
+REDUCTIONS = {"none": LCE_RED_NONE, "mean": LCE_RED_MEAN, "sum": LCE_RED_SUM}
+
+_lib = None
+
+
+class LCEError(RuntimeError):
+    """A nonzero lce_status; the message is lce_last_error()."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded liblce.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m vocabulary_cross_entropy_row_amd.build` (there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    L.lce_abi_version.restype = ctypes.c_int
+    L.lce_abi_version.argtypes = []
+    L.lce_last_error.restype = ctypes.c_char_p
+    L.lce_last_error.argtypes = []
+    L.lce_ce_workspace_bytes.restype = ctypes.c_size_t
+    L.lce_ce_workspace_bytes.argtypes = [i64, i64]
+    L.lce_ce_fwd_bwd.restype = ctypes.c_int
+    L.lce_ce_fwd_bwd.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, f32, f32, ctypes.c_int, p, p, p, p, p,
+                                 p, ctypes.c_size_t, p]
+    L.lce_ce_argmax.restype = ctypes.c_int
+    L.lce_ce_argmax.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, p, p, p]
+    if L.lce_abi_version() != 1:
+        raise ImportError("liblce.so ABI version mismatch; rebuild it")
+    _lib = L
+    return L
+
+
+def lce_last_error() -> str:
+    return lib().lce_last_error().decode()
+
+
+def lce_ce_workspace_bytes(n: int, V: int) -> int:
+    return int(lib().lce_ce_workspace_bytes(int(n), int(V)))
+
+
+def _check(status: int) -> None:
+    if status != LCE_OK:
+        raise LCEError(status, lce_last_error())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LCE_BF16
+    if t.dtype == torch.float32:
+        return LCE_F32
+    raise TypeError(f"logits must be bfloat16 or float32, not {t.dtype}")
+
+
+@dataclass
+class CEResult:
+    loss_tok: object      # fp32 [n]
+    loss_out: object      # fp32 [1]
+    argmax: object        # int64 [n] or None
+    counts: object        # int64 [3] {n_valid, n_correct, n_bad}
+
+
+def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
+                   softcap: float = 0.0, reduction: str = "mean", grad_out=None, want_argmax: bool = False,
+                   loss_tok=None, loss_out=None, argmax_out=None, counts=None, workspace=None,
+                   stream=None) -> CEResult:
+    """Cross-entropy forward + backward; ``logits`` ([n, V] view, unit column stride, row
+    stride ld >= V) is overwritten with the gradient.  Outputs not passed in are allocated."""
+    import torch
+    if logits.dim() != 2 or (logits.size(1) > 1 and logits.stride(1) != 1):
+        raise ValueError("logits must be a 2-D view with unit column stride")
+    n, V = logits.shape
+    ld = logits.stride(0) if n > 1 else V
+    dev = logits.device
+    if grad_out is not None and not torch.is_tensor(grad_out):
+        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=dev)
+    elif grad_out is not None and grad_out.dtype != torch.float32:
+        grad_out = grad_out.float()
+    if loss_tok is None:
+        loss_tok = torch.empty(n, dtype=torch.float32, device=dev)
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if argmax_out is None and want_argmax:
+        argmax_out = torch.empty(n, dtype=torch.int64, device=dev)
+    if counts is None:
+        counts = torch.empty(3, dtype=torch.int64, device=dev)
+    wsb = lce_ce_workspace_bytes(n, V)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = lib().lce_ce_fwd_bwd(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V, int(ignore_index),
+                              float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
+                              _ptr(loss_tok), _ptr(loss_out), _ptr(argmax_out), _ptr(counts), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+    return CEResult(loss_tok, loss_out, argmax_out, counts)
+
+
+def lce_ce_argmax(logits, labels=None, *, ignore_index: int = -100, argmax_out=None, counts=None,
+                  stream=None):
+    """Read-only argmax sweep.  Returns (argmax int64 [n], counts int64 [3])."""
+    import torch
+    if logits.dim() != 2 or (logits.size(1) > 1 and logits.stride(1) != 1):
+        raise ValueError("logits must be a 2-D view with unit column stride")
+    n, V = logits.shape
+    ld = logits.stride(0) if n > 1 else V
+    dev = logits.device
+    if argmax_out is None:
+        argmax_out = torch.empty(n, dtype=torch.int64, device=dev)
+    if counts is None:
+        counts = torch.empty(3, dtype=torch.int64, device=dev)
+    st = lib().lce_ce_argmax(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V, int(ignore_index),
+                             _ptr(argmax_out), _ptr(counts), _stream(stream))
+    _check(st)
+    return argmax_out, counts

@@ -1,0 +1,132 @@
+// C-ABI entry points (include/lce.h): argument validation, then kernel launch.
+// Validation runs before any HIP call, so every argument error is reported
+// without touching the device.  No exception crosses the ABI.
+#include "../../include/lce.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "lce_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lce_status fail(lce_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+lce_status ok() {
+    g_err[0] = '\0';
+    return LCE_OK;
+}
+
+lce_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(LCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kCeWorkspaceBytes = 256;   // completion counter (+ room, 256-B granule)
+
+}  // namespace
+
+extern "C" {
+
+int lce_abi_version(void) { return 1; }
+
+const char *lce_last_error(void) { return g_err; }
+
+size_t lce_ce_workspace_bytes(int64_t n, int64_t V) {
+    (void)n;
+    (void)V;
+    return kCeWorkspaceBytes;
+}
+
+lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                          int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                          lce_reduction reduction, const float *grad_out, float *loss_tok, float *loss_out,
+                          int64_t *argmax_out, int64_t *counts, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: n must be >= 0 (got %lld)", (long long)n);
+    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: V must be >= 1 (got %lld)", (long long)V);
+    if (ld < V) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: ld (%lld) must be >= V (%lld)", (long long)ld,
+                            (long long)V);
+    if (dtype != LCE_F32 && dtype != LCE_BF16)
+        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: unknown dtype %d", (int)dtype);
+    if (reduction != LCE_RED_NONE && reduction != LCE_RED_MEAN && reduction != LCE_RED_SUM)
+        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: unknown reduction %d", (int)reduction);
+    if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
+        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: label_smoothing must be in [0, 1] (got %g)",
+                    (double)label_smoothing);
+    if (!(softcap >= 0.0f) || isinf(softcap))
+        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: softcap must be finite and >= 0 (got %g)", (double)softcap);
+    if (!counts) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: counts is required");
+    if (!workspace) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: workspace is required");
+    if (workspace_bytes < lce_ce_workspace_bytes(n, V))
+        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: workspace_bytes %zu < required %zu", workspace_bytes,
+                    lce_ce_workspace_bytes(n, V));
+    if (!is_aligned(workspace, 16)) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: workspace must be 16-byte aligned");
+    if (n > 0) {
+        if (!logits_inout) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: logits is required");
+        if (!labels) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: labels is required");
+        if (!loss_tok) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: loss_tok is required");
+        const size_t esz = dtype == LCE_BF16 ? 2 : 4;
+        if (!is_aligned(logits_inout, esz))
+            return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: logits must be aligned to its element size");
+    }
+    if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "lce_ce_fwd_bwd: n > 2^31-1 rows is not supported");
+    if (V > 0x7fffffffLL / 16)
+        return fail(LCE_ERR_UNSUPPORTED, "lce_ce_fwd_bwd: V > 2^27 columns is not supported");
+
+    lce::CEArgs a;
+    a.logits = logits_inout;
+    a.ld = ld;
+    a.n = n;
+    a.V = V;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.eps = label_smoothing;
+    a.softcap = softcap;
+    a.reduction = static_cast<int>(reduction);
+    a.grad_out = grad_out;
+    a.loss_tok = loss_tok;
+    a.loss_out = loss_out;
+    a.argmax_out = argmax_out;
+    a.counts = counts;
+    a.ticket = static_cast<unsigned *>(workspace);
+    return hip_status(lce::launch_ce_fwd_bwd(a, dtype == LCE_BF16, stream), "lce_ce_fwd_bwd launch");
+}
+
+lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                         int64_t V, int64_t ignore_index, int64_t *argmax_out, int64_t *counts,
+                         hipStream_t stream) {
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: n must be >= 0 (got %lld)", (long long)n);
+    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: V must be >= 1 (got %lld)", (long long)V);
+    if (ld < V) return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: ld (%lld) must be >= V (%lld)", (long long)ld,
+                            (long long)V);
+    if (dtype != LCE_F32 && dtype != LCE_BF16)
+        return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: unknown dtype %d", (int)dtype);
+    if (!counts) return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: counts is required");
+    if (n > 0) {
+        if (!logits) return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: logits is required");
+        if (!argmax_out) return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: argmax_out is required");
+        const size_t esz = dtype == LCE_BF16 ? 2 : 4;
+        if (!is_aligned(logits, esz))
+            return fail(LCE_ERR_INVALID_ARG, "lce_ce_argmax: logits must be aligned to its element size");
+    }
+    if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "lce_ce_argmax: n > 2^31-1 rows is not supported");
+    if (V > 0x7fffffffLL / 16) return fail(LCE_ERR_UNSUPPORTED, "lce_ce_argmax: V > 2^27 columns is not supported");
+    return hip_status(lce::launch_ce_argmax(logits, ld, dtype == LCE_BF16, labels, n, V, ignore_index, argmax_out,
+                                            counts, stream),
+                      "lce_ce_argmax launch");
+}
+
+}  // extern "C"
