@@ -91,7 +91,7 @@ def main() -> int:
     loss_out = torch.empty(1, dtype=torch.float32, device=dev)
     argmax = torch.empty(w.n, dtype=torch.int64, device=dev) if w.want_argmax else None
     counts = torch.empty(3, dtype=torch.int64, device=dev)
-    ws = torch.empty(lce.lce_ce_workspace_bytes(w.n, w.V), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lce.lce_ce_workspace_bytes(w.n, w.V), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(buf):

@@ -52,8 +52,9 @@ typedef enum { LCE_F32 = 0, LCE_BF16 = 1 } lce_dtype;
 typedef enum { LCE_RED_NONE = 0, LCE_RED_MEAN = 1, LCE_RED_SUM = 2 } lce_reduction;
 
 /*
- * Bytes of device workspace lce_ce_fwd_bwd needs for n rows of V columns.
- * Always > 0 (it holds the completion counter of the final reduction).
+ * Bytes of device workspace lce_ce_fwd_bwd needs for n rows of V columns
+ * (256 + 16 * min(n, 4096); always > 0).  The workspace holds the completion
+ * counter of the final reduction and per-workgroup partial sums.
  */
 size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
 
@@ -87,7 +88,10 @@ size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
  *                 n_correct = #{valid i : argmax_i == y_i} (0 when argmax_out
  *                 is NULL).  Token accuracy = n_correct / n_valid.
  *   workspace     device scratch of at least lce_ce_workspace_bytes(n, V)
- *                 bytes, 16-byte aligned; clobbered.
+ *                 bytes, 16-byte aligned.  Its first 4 bytes must be zero
+ *                 before the first call (zero-fill it once at allocation);
+ *                 every call leaves them zero again.  Calls that share a
+ *                 workspace must not run concurrently.
  * loss_tok, argmax_out, counts, workspace and loss_out must not overlap the
  * logits or each other.  n == 0 is valid (counts and loss_out become 0).
  */

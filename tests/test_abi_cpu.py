@@ -43,7 +43,7 @@ ALIGNED_WS = 0x20000
 def call_fwd_bwd(**over):
     args = dict(logits=FAKE, ld=8, dtype=lce.LCE_BF16, labels=FAKE, n=4, V=8, ignore_index=-100,
                 eps=0.0, softcap=0.0, red=lce.LCE_RED_MEAN, grad_out=None, loss_tok=FAKE, loss_out=None,
-                argmax=None, counts=FAKE, ws=ALIGNED_WS, wsb=256, stream=None)
+                argmax=None, counts=FAKE, ws=ALIGNED_WS, wsb=4096, stream=None)
     args.update(over)
     a = args
     st = lce.lib().lce_ce_fwd_bwd(a["logits"], a["ld"], a["dtype"], a["labels"], a["n"], a["V"], a["ignore_index"],
@@ -80,7 +80,7 @@ def test_fwd_bwd_rejects_bad_arguments(over, needle):
 
 
 def test_fwd_bwd_unsupported_sizes():
-    st, msg = call_fwd_bwd(n=2 ** 31, ld=8)
+    st, msg = call_fwd_bwd(n=2 ** 31, ld=8, wsb=1 << 20)
     assert st == lce.LCE_ERR_UNSUPPORTED and "n > 2^31-1" in msg
 
 

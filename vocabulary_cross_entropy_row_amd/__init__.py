@@ -125,7 +125,7 @@ def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing:
         counts = torch.empty(3, dtype=torch.int64, device=dev)
     wsb = lce_ce_workspace_bytes(n, V)
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     st = lib().lce_ce_fwd_bwd(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V, int(ignore_index),
                               float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                               _ptr(loss_tok), _ptr(loss_out), _ptr(argmax_out), _ptr(counts), _ptr(workspace),

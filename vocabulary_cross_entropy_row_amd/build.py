@@ -18,7 +18,12 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblce.so")
 
 ARCH = "gfx950"
-SOURCES = ["ce_kernels.hip", "lce_api.cpp"]
+# (source, extra flags, object name).  ce_rows_inst.hip is compiled once per
+# (dtype, rounds in VGPRs, rounds in LDS) family of the resident row kernel.
+FAMILIES = [(1, 0), (2, 0), (4, 0), (8, 0), (12, 0), (16, 0), (16, 3), (16, 6), (16, 9)]
+UNITS = [("ce_kernels.hip", [], "ce_kernels"), ("lce_api.cpp", ["-x", "hip"], "lce_api")] + [
+    ("ce_rows_inst.hip", [f"-DLCE_BF16={b}", f"-DLCE_KR={kr}", f"-DLCE_KL={kl}"], f"ce_rows_{b}_{kr}_{kl}")
+    for b in (1, 0) for kr, kl in FAMILIES]
 
 # Packed-fp32 VALU ops are switched off for every device pass: hipcc -O3 would
 # otherwise form v_pk_fma/add/mul_f32 on its own.
@@ -34,12 +39,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblce.so)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON]
-    if src.endswith(".cpp"):
-        cmd += ["-x", "hip"]
-    cmd += ["-c", os.path.join(CSRC, src), "-o", out]
+def _compile(unit, verbose: bool) -> str:
+    src, flags, name = unit
+    out = os.path.join(OBJ, name + ".o")
+    cmd = [_hipcc(), *COMMON, *flags, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +53,9 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    jobs = max(1, min(len(UNITS), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:

@@ -1,0 +1,208 @@
+// Device helpers shared by the cross-entropy kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "lce_internal.h"
+
+namespace lce {
+namespace dev {
+
+// 16-byte vector as a clang vector type (usable with the non-temporal builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = kRowThreads;
+constexpr int NWAVE = NT / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float t) { return __builtin_amdgcn_exp2f(t); }
+__device__ __forceinline__ float rcp_fast(float t) { return __builtin_amdgcn_rcpf(t); }
+
+// Hide register-resident data from the optimiser at a pass boundary.  Without
+// this the compiler keeps every widened (fp32) element of one pass alive for
+// reuse in the next, doubling the row's register footprint and spilling.
+template <int K>
+__device__ __forceinline__ void opaque_regs(u32x4 (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) asm volatile("" : "+v"(v[k]));
+}
+
+// Wait for every outstanding vector-memory operation of this wave (including
+// loads that write LDS directly, which the compiler does not track).
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Softcap support.  With u = x / T:  tanh(u) = 1 - 2 r,  r = 1 / (1 + e^{2u}),
+// so z = T - 2 T r and dz/dx = 1 - tanh^2(u) = 4 r (1 - r).  r comes from the
+// hardware base-2 exponential and reciprocal.
+struct Cap {
+    float c2;   // 2 log2(e) / T
+    float T;
+    __device__ __forceinline__ float r_of(float x) const { return rcp_fast(1.0f + exp2_fast(x * c2)); }
+    __device__ __forceinline__ float z_of_r(float r) const { return fmaf(-2.0f * T, r, T); }
+    __device__ __forceinline__ static float chain_of_r(float r) { return 4.0f * r * (1.0f - r); }
+};
+
+// ---- element access ---------------------------------------------------------
+
+template <bool BF16> struct Elt;
+
+template <> struct Elt<true> {
+    static constexpr int E = 8;       // bf16 per 16-byte vector
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static uint32_t word(const u32x4 &v, int w) {
+        return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+    }
+    // element e of the vector, widened exactly to fp32 (e is a compile-time constant after unrolling)
+    __device__ __forceinline__ static float get(const u32x4 &v, int e) {
+        const uint32_t w = word(v, e >> 1);
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    }
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        f2 f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf2));   // RNE
+    }
+    __device__ __forceinline__ static u32x4 pack(const float (&g)[8]) {
+        return (u32x4){pack2(g[0], g[1]), pack2(g[2], g[3]), pack2(g[4], g[5]), pack2(g[6], g[7])};
+    }
+    __device__ __forceinline__ static float load_one(const void *base, int64_t idx) {
+        const uint16_t b = static_cast<const uint16_t *>(base)[idx];
+        return __uint_as_float(static_cast<uint32_t>(b) << 16);
+    }
+    __device__ __forceinline__ static void store_one(void *base, int64_t idx, float g) {
+        static_cast<__bf16 *>(base)[idx] = static_cast<__bf16>(g);   // RNE
+    }
+};
+
+template <> struct Elt<false> {
+    static constexpr int E = 4;       // fp32 per 16-byte vector
+    static constexpr int bytes = 4;
+    __device__ __forceinline__ static float get(const u32x4 &v, int e) {
+        return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+    }
+    __device__ __forceinline__ static u32x4 pack(const float (&g)[4]) {
+        return (u32x4){__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
+                       __float_as_uint(g[3])};
+    }
+    __device__ __forceinline__ static float load_one(const void *base, int64_t idx) {
+        return static_cast<const float *>(base)[idx];
+    }
+    __device__ __forceinline__ static void store_one(void *base, int64_t idx, float g) {
+        static_cast<float *>(base)[idx] = g;
+    }
+};
+
+// ---- reductions -------------------------------------------------------------
+// Butterfly (xor) shuffles: every lane ends with the same value because each
+// step combines the same two operands (IEEE max/add are commutative).
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// (value, index) order: larger value first, then smaller index.
+__device__ __forceinline__ void argmax_combine(float &v, int &i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(v, o, 64);
+        const int i2 = __shfl_xor(i, o, 64);
+        argmax_combine(v, i, v2, i2);
+    }
+}
+
+// Block reductions: one LDS slot per wave, then every thread folds the slots
+// in wave order, so all threads hold the same result without a second
+// barrier.  A call site must not reuse its LDS array before another barrier
+// has separated the reads from the next writes.
+__device__ __forceinline__ float block_max(float v, float *sh) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) r = fmaxf(r, sh[w]);
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *sh) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) r += sh[w];
+    return r;
+}
+
+__device__ __forceinline__ void block_argmax(float &v, int &i, float *shv, int *shi) {
+    wave_argmax(v, i);
+    if ((threadIdx.x & 63) == 0) {
+        shv[threadIdx.x >> 6] = v;
+        shi[threadIdx.x >> 6] = i;
+    }
+    __syncthreads();
+    v = shv[0];
+    i = shi[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) argmax_combine(v, i, shv[w], shi[w]);
+}
+
+// Valid-label and bad-label counts over all n labels, by one workgroup.
+__device__ __forceinline__ void block_count_labels(const CEArgs &a, long long (*sh)[NWAVE], long long &nv,
+                                                   long long &nb) {
+    long long v = 0, b = 0;
+    for (int64_t i = threadIdx.x; i < a.n; i += NT) {
+        const int64_t y = a.labels[i];
+        if (y != a.ignore_index) {
+            if (y >= 0 && y < a.V) ++v;
+            else ++b;
+        }
+    }
+    v = wave_sum_ll(v);
+    b = wave_sum_ll(b);
+    if ((threadIdx.x & 63) == 0) {
+        sh[0][threadIdx.x >> 6] = v;
+        sh[1][threadIdx.x >> 6] = b;
+    }
+    __syncthreads();
+    nv = 0;
+    nb = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+        nv += sh[0][w];
+        nb += sh[1][w];
+    }
+}
+
+}  // namespace dev
+}  // namespace lce

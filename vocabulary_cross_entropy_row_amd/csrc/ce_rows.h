@@ -1,0 +1,388 @@
+// Persistent, software-pipelined cross-entropy row kernel (gfx950).
+//
+// Per row i, label y, eps = label smoothing, T = softcap:
+//   z = T > 0 ? T tanh(x / T) : x
+//   loss_i = LSE(z) - (1 - eps) z_y - (eps / V) sum_j z_j
+//   dx_ij  = s_i (softmax(z)_j - (1 - eps)[j == y] - eps / V) dz_j / dx_j
+// (Liger-Kernel PR "Add Megatron-LM cross-entropy integration", Summary and
+// Test setup; Megatron-LM PR "Add opt-in Liger vocab-parallel cross entropy",
+// "What does this PR do?"; Liger-Kernel PR "Add Liger Kernel support for Muse
+// Glimmer", Details/Softcap.)
+//
+// Layout of the work: one 1024-thread workgroup per CU walks rows
+// blockIdx.x, blockIdx.x + G, ...  A row is split into K rounds of 1024
+// 16-byte vectors; thread t owns vector (k * 1024 + t) of every round.  The
+// first KR rounds live in VGPRs, the next KL rounds in thread-private LDS
+// slots filled by direct global->LDS loads, so the row is read from HBM once.
+// Three passes run over the resident row: max (+ argmax), sum of
+// exponentials, gradient.  While pass 3 stores the gradient of round k it
+// already issues the load of round k of the workgroup's next row into the
+// same registers / LDS slot, so HBM traffic of the next row overlaps the
+// arithmetic of this one.
+//
+// The workgroups count the labels themselves (the mean scale needs n_valid
+// before any gradient is written), keep per-workgroup loss / n_correct
+// partials in the workspace, and the last workgroup to finish folds them in
+// workgroup order, so every reduction is deterministic.
+#pragma once
+
+#include "ce_device.h"
+
+namespace lce {
+namespace dev {
+
+// Workspace layout: [0,4) completion counter (zero between calls), [256, 256 + 8G)
+// fp64 loss partials, then G int64 n_correct partials.
+constexpr size_t kWsPartials = 256;
+
+// Word 3 of a gfx9-family buffer descriptor: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy bit of buffer loads/stores: non-temporal (streamed once).
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ unsigned *ws_ticket(void *ws) { return static_cast<unsigned *>(ws); }
+__device__ __forceinline__ double *ws_loss(void *ws) {
+    return reinterpret_cast<double *>(static_cast<char *>(ws) + kWsPartials);
+}
+__device__ __forceinline__ long long *ws_correct(void *ws, int G) {
+    return reinterpret_cast<long long *>(static_cast<char *>(ws) + kWsPartials + 8 * static_cast<size_t>(G));
+}
+
+template <bool BF16, int KR, int KL, bool SOFTCAP, bool ARGMAX, bool SMOOTH>
+__global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
+    using EL = Elt<BF16>;
+    constexpr int E = EL::E;
+    constexpr int K = KR + KL;
+    constexpr int KRV = KR > 0 ? KR : 1;
+    __shared__ u32x4 lds_rows[KL > 0 ? KL * NT : 1];
+    __shared__ float sh_m[NWAVE], sh_s[NWAVE], sh_z[NWAVE];
+    __shared__ int sh_i[NWAVE];
+    __shared__ long long sh_c[2][NWAVE];
+    __shared__ double sh_d[NWAVE];
+    __shared__ float sh_xy;
+    __shared__ int sh_flag;
+
+    const int tid = threadIdx.x;
+    const int wave_base = tid & ~63;
+    const int nvec = static_cast<int>(a.V / E);
+    const int G = gridDim.x;
+    const int64_t n = a.n;
+    const float eps = a.eps;
+    const float invV = 1.0f / static_cast<float>(a.V);
+    const Cap cap{SOFTCAP ? 2.0f * kLog2e / a.softcap : 0.0f, a.softcap};
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // Labels and the upstream gradient are read-only for the kernel's lifetime:
+    // read them through the constant address space, i.e. with scalar loads,
+    // which wait on their own counter instead of on the row's vector loads.
+    typedef const __attribute__((address_space(4))) int64_t *clabels_t;
+    typedef const __attribute__((address_space(4))) float *cfloat_t;
+    const clabels_t lab = (clabels_t)a.labels;
+    const cfloat_t gout = (cfloat_t)a.grad_out;
+
+    long long n_valid, n_bad;
+    block_count_labels(a, sh_c, n_valid, n_bad);
+    const float g_all = (a.reduction != 0 && gout) ? gout[0] : 1.0f;
+    const float red_scale =
+        a.reduction == 1 ? (n_valid > 0 ? g_all / static_cast<float>(n_valid) : 0.0f) : g_all;
+
+    auto valid_label = [&](int64_t y) { return y != a.ignore_index && y >= 0 && y < a.V; };
+    // the next row >= r of this workgroup's sequence that takes the full path:
+    // every row when the argmax is wanted, otherwise only rows with a valid label
+    auto next_row = [&](int64_t r) {
+        if constexpr (!ARGMAX)
+            while (r < n && !valid_label(lab[r])) r += G;
+        return r;
+    };
+
+    // Row memory goes through buffer instructions: the row base sits in a
+    // uniform descriptor (SGPRs), every round shares one VGPR offset
+    // (tid * 16) plus a scalar round offset, and the descriptor's range check
+    // (num_records = the row's V * b bytes) drops the lanes of a partial last
+    // round, so loads and stores need no exec masking.  When there is no row
+    // to prefetch the descriptor is empty (num_records = 0): loads through it
+    // return zeros without touching memory.  Reloading unconditionally lets
+    // each register round die right after its last use.
+    const uint32_t row_bytes = static_cast<uint32_t>(nvec) * 16u;
+    auto row_rsrc = [&](int64_t r, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.logits) + (live ? r : 0) * a.ld * EL::bytes,
+                                                 0, live ? row_bytes : 0u, kBufferWord3);
+    };
+    const int voff = tid * 16;
+
+    u32x4 v[KRV];
+    auto issue_round = [&](int k, __amdgpu_buffer_rsrc_t src) {
+        if (k < KR) {
+            v[k < KR ? k : 0] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, k * NT * 16, kNonTemporal);
+        } else {
+            // 16 bytes per lane, written to LDS at (wave-uniform base) + lane * 16
+            typedef __attribute__((address_space(3))) void *lptr;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lptr)(&lds_rows[(k - KR) * NT + wave_base]), 16, voff,
+                                                     k * NT * 16, 0, kNonTemporal);
+        }
+    };
+    auto store_round = [&](int k, __amdgpu_buffer_rsrc_t dst, u32x4 val) {
+        __builtin_amdgcn_raw_buffer_store_b128(val, dst, voff, k * NT * 16, kNonTemporal);
+    };
+    // a round of the resident row as a 16-byte vector
+    auto round_vec = [&](int k) -> u32x4 { return k < KR ? v[k < KR ? k : 0] : lds_rows[(k - KR) * NT + tid]; };
+
+    int64_t row = next_row(blockIdx.x);
+    {
+        const __amdgpu_buffer_rsrc_t src = row_rsrc(row, row < n);
+#pragma unroll
+        for (int k = 0; k < K; ++k) issue_round(k, src);
+    }
+
+    double loss_acc = 0.0;
+    long long correct = 0;
+
+    for (int64_t nxt; row < n; row = nxt) {
+        nxt = next_row(row + G);
+        const __amdgpu_buffer_rsrc_t rn = row_rsrc(nxt, nxt < n);
+        const __amdgpu_buffer_rsrc_t rp = row_rsrc(row, true);
+        const int64_t y64 = lab[row];
+        const bool valid = valid_label(y64);     // always true unless ARGMAX
+        const int y = valid ? static_cast<int>(y64) : 0;
+        // an ignored row on the argmax path is carried through with scale 0, so
+        // its gradient comes out as zeros
+        const float scale = !valid ? 0.0f : (a.reduction == 0 ? (gout ? gout[row] : 1.0f) : red_scale);
+
+        // where the target element lives: round ky, thread ty, element ey
+        const int vy = y / E, ey = y % E, ky = vy / NT, ty = vy % NT;
+        const bool owner = tid == ty;
+
+        // ---- pass 1: row maximum of the raw logits (and its first index); the
+        // owner of the target element publishes x_y through LDS
+        float m = -INFINITY;
+        int am = 0x7fffffff;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (k == KR && KL > 0) wait_vmem_all();   // LDS rounds have landed
+            const int idx = k * NT + tid;
+            if (idx < nvec) {
+                const u32x4 vk = round_vec(k);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = EL::get(vk, e);
+                    if constexpr (ARGMAX) {
+                        if (x > m) {
+                            m = x;
+                            am = idx * E + e;
+                        }
+                    } else {
+                        m = fmaxf(m, x);
+                    }
+                }
+                if (k == ky && owner) {
+                    float sel = EL::get(vk, 0);
+#pragma unroll
+                    for (int e = 1; e < E; ++e)
+                        if (e == ey) sel = EL::get(vk, e);
+                    sh_xy = sel;
+                }
+            }
+        }
+        if constexpr (ARGMAX) {
+            block_argmax(m, am, sh_m, sh_i);
+            if (tid == 0) {
+                a.argmax_out[row] = am;
+                if (valid && am == y) ++correct;
+            }
+        } else {
+            m = block_max(m, sh_m);
+        }
+        const float xy = sh_xy;
+        float Mz, zy;
+        if constexpr (SOFTCAP) {
+            Mz = cap.z_of_r(cap.r_of(m));   // tanh is increasing: max z = cap(max x)
+            zy = cap.z_of_r(cap.r_of(xy));
+        } else {
+            Mz = m;
+            zy = xy;
+        }
+
+        // ---- pass 2: s = sum_{j != y} exp(z_j - Mz), zs = sum_j z_j
+        const float MzL = Mz * kLog2e;
+        const float capk = -2.0f * a.softcap * kLog2e;   // d(z log2 e)/dr
+        const float capb = (a.softcap - Mz) * kLog2e;    // (T - Mz) log2 e
+        float s = 0.0f, zs = 0.0f;
+        opaque_regs(v);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int idx = k * NT + tid;
+            if (idx < nvec) {
+                const u32x4 vk = round_vec(k);
+                float ex[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = EL::get(vk, e);
+                    if constexpr (SOFTCAP) {
+                        const float r = cap.r_of(x);
+                        ex[e] = exp2_fast(fmaf(r, capk, capb));
+                        if constexpr (SMOOTH) zs += cap.z_of_r(r);
+                    } else {
+                        ex[e] = exp2_fast(fmaf(x, kLog2e, -MzL));
+                        if constexpr (SMOOTH) zs += x;
+                    }
+                }
+                if (k == ky) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (owner && e == ey) ex[e] = 0.0f;
+                }
+                float part = ex[0];
+#pragma unroll
+                for (int e = 1; e < E; ++e) part += ex[e];
+                s += part;
+            }
+        }
+        s = block_sum(s, sh_s);
+        if constexpr (SMOOTH) zs = block_sum(zs, sh_z);
+
+        const float e_y = exp2_fast(fmaf(zy, kLog2e, -MzL));
+        const float S = s + e_y;
+        const float lse = Mz + logf(S);
+        if (tid == 0) {
+            float loss = lse - (1.0f - eps) * zy;
+            if constexpr (SMOOTH) loss -= eps * invV * zs;
+            if (!valid) loss = 0.0f;
+            a.loss_tok[row] = loss;
+            loss_acc += static_cast<double>(loss);
+        }
+
+        // ---- pass 3: gradient over the logits; round k of the next row is
+        // requested as soon as round k of this row has been consumed
+        const float epsV = SMOOTH ? eps * invV : 0.0f;
+        const float lseL = lse * kLog2e;
+        const float capb2 = (a.softcap - lse) * kLog2e;
+        float gy = scale * (eps - s / S - epsV);          // p_y - (1 - eps) - eps/V
+        if constexpr (SOFTCAP) gy *= Cap::chain_of_r(cap.r_of(xy));
+        opaque_regs(v);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int idx = k * NT + tid;
+            if (idx < nvec) {
+                const u32x4 vk = round_vec(k);
+                float g[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = EL::get(vk, e);
+                    if constexpr (SOFTCAP) {
+                        const float r = cap.r_of(x);
+                        const float p = exp2_fast(fmaf(r, capk, capb2));
+                        g[e] = scale * (p - epsV) * Cap::chain_of_r(r);
+                    } else {
+                        const float p = exp2_fast(fmaf(x, kLog2e, -lseL));
+                        g[e] = scale * (p - epsV);
+                    }
+                }
+                if (k == ky) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (owner && e == ey) g[e] = gy;
+                }
+                store_round(k, rp, EL::pack(g));
+            }
+            issue_round(k, rn);
+            // keep round k's next-row load behind round k's gradient: hoisted
+            // earlier it would hold two rows in registers at once and spill
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- ignored tokens (when no argmax is wanted): zero gradient, no read
+    if constexpr (!ARGMAX) {
+        const __amdgpu_buffer_rsrc_t none = row_rsrc(0, false);
+        (void)none;
+        for (int64_t r = blockIdx.x; r < n; r += G) {
+            if (valid_label(lab[r])) continue;
+            const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
+#pragma unroll
+            for (int k = 0; k < K; ++k) store_round(k, rz, zero4);
+            if (tid == 0) a.loss_tok[r] = 0.0f;
+        }
+    }
+
+    // ---- publish this workgroup's partials; the last workgroup folds them
+    if (tid == 0) {
+        ws_loss(a.workspace)[blockIdx.x] = loss_acc;
+        ws_correct(a.workspace, G)[blockIdx.x] = correct;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const unsigned t = __hip_atomic_fetch_add(ws_ticket(a.workspace), 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const int last = t == static_cast<unsigned>(G) - 1u;
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sh_flag = last;
+    }
+    __syncthreads();
+    if (!sh_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    double acc = 0.0;
+    long long cor = 0;
+    for (int w = tid; w < G; w += NT) {
+        acc += ws_loss(a.workspace)[w];
+        cor += ws_correct(a.workspace, G)[w];
+    }
+    acc = wave_sum_d(acc);
+    cor = wave_sum_ll(cor);
+    if ((tid & 63) == 0) {
+        sh_d[tid >> 6] = acc;
+        sh_c[0][tid >> 6] = cor;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        long long c = 0;
+        for (int w = 0; w < NWAVE; ++w) {
+            tot += sh_d[w];
+            c += sh_c[0][w];
+        }
+        if (a.loss_out) {
+            float out = 0.0f;
+            if (a.reduction == 1) out = n_valid > 0 ? static_cast<float>(tot / static_cast<double>(n_valid)) : 0.0f;
+            else if (a.reduction == 2) out = static_cast<float>(tot);
+            *a.loss_out = out;
+        }
+        a.counts[0] = n_valid;
+        a.counts[1] = c;
+        a.counts[2] = n_bad;
+        *ws_ticket(a.workspace) = 0u;
+    }
+}
+
+// Host-side launch of one (dtype, KR, KL) family: picks the feature variant and
+// sizes the persistent grid to the workgroups the CUs hold at once.
+template <bool BF16, int KR, int KL, bool S, bool A, bool M>
+hipError_t launch_variant(const CEArgs &a, int max_groups, hipStream_t st) {
+    static int per_cu = 0;   // resident workgroups per CU (same for every gfx950 device)
+    if (per_cu == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ce_rows_kernel<BF16, KR, KL, S, A, M>, NT, 0) !=
+                hipSuccess || nb < 1)
+            nb = 1;
+        per_cu = nb;
+    }
+    int64_t grid = static_cast<int64_t>(max_groups) * per_cu;
+    if (grid > a.n) grid = a.n;
+    if (grid > kMaxRowGroups) grid = kMaxRowGroups;
+    hipLaunchKernelGGL((ce_rows_kernel<BF16, KR, KL, S, A, M>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, st,
+                       a);
+    return hipGetLastError();
+}
+
+template <bool BF16, int KR, int KL>
+hipError_t launch_rows(const CEArgs &a, int max_groups, hipStream_t st) {
+    const bool sc = a.softcap > 0.0f, am = a.argmax_out != nullptr, sm = a.eps != 0.0f;
+#define LCE_ROWS(S, A, M) return launch_variant<BF16, KR, KL, S, A, M>(a, max_groups, st)
+    if (sc) {
+        if (am) { if (sm) LCE_ROWS(true, true, true); else LCE_ROWS(true, true, false); }
+        else    { if (sm) LCE_ROWS(true, false, true); else LCE_ROWS(true, false, false); }
+    } else {
+        if (am) { if (sm) LCE_ROWS(false, true, true); else LCE_ROWS(false, true, false); }
+        else    { if (sm) LCE_ROWS(false, false, true); else LCE_ROWS(false, false, false); }
+    }
+#undef LCE_ROWS
+}
+
+}  // namespace dev
+}  // namespace lce

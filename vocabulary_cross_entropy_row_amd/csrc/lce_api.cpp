@@ -34,8 +34,6 @@ lce_status hip_status(hipError_t e, const char *what) {
 
 bool is_aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-constexpr size_t kCeWorkspaceBytes = 256;   // completion counter (+ room, 256-B granule)
-
 }  // namespace
 
 extern "C" {
@@ -45,9 +43,8 @@ int lce_abi_version(void) { return 1; }
 const char *lce_last_error(void) { return g_err; }
 
 size_t lce_ce_workspace_bytes(int64_t n, int64_t V) {
-    (void)n;
     (void)V;
-    return kCeWorkspaceBytes;
+    return lce::ce_workspace_bytes(n);
 }
 
 lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
@@ -101,7 +98,7 @@ lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const
     a.loss_out = loss_out;
     a.argmax_out = argmax_out;
     a.counts = counts;
-    a.ticket = static_cast<unsigned *>(workspace);
+    a.workspace = workspace;
     return hip_status(lce::launch_ce_fwd_bwd(a, dtype == LCE_BF16, stream), "lce_ce_fwd_bwd launch");
 }
 

@@ -23,14 +23,21 @@ struct CEArgs {
     float *loss_out;         // scalar or NULL
     int64_t *argmax_out;     // [n] or NULL
     int64_t *counts;         // [3]
-    unsigned *ticket;        // completion counter (workspace)
+    void *workspace;         // completion counter + per-workgroup partials
 };
 
 // Threads per row workgroup of the register-resident path.
 constexpr int kRowThreads = 1024;
-// Largest number of 16-byte vectors per thread the register-resident path
-// keeps (26 * 16 B = 416 B = 104 VGPRs per lane).
-constexpr int kMaxVecPerThread = 26;
+// Rounds (1024 x 16-byte vectors) of a row the resident path holds: up to 16
+// in VGPRs (64 per lane) plus up to 9 in LDS (144 KB of the 160 KB per CU).
+constexpr int kMaxRegRounds = 16;
+constexpr int kMaxLdsRounds = 9;
+// Upper bound on persistent workgroups (sizes the workspace partials).
+constexpr int kMaxRowGroups = 4096;
+// Workspace: 256-byte header (completion counter) + 16 bytes per workgroup.
+constexpr size_t ce_workspace_bytes(int64_t n) {
+    return 256 + 16 * static_cast<size_t>(n < kMaxRowGroups ? (n > 0 ? n : 1) : kMaxRowGroups);
+}
 
 // Enqueue count + row kernels.  is_bf16 selects the element type.
 hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream);
@@ -40,8 +47,8 @@ hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const 
                             int64_t n, int64_t V, int64_t ignore_index, int64_t *argmax_out,
                             int64_t *counts, hipStream_t stream);
 
-// Which row kernel a shape takes (exposed for tests / the bench report).
-// Returns the vectors-per-thread template chosen, or 0 for the generic path.
-int ce_fast_path_k(const void *logits, int64_t ld, bool is_bf16, int64_t V);
+// Which row kernel a shape takes: rounds in VGPRs (*kr) and LDS (*kl), or
+// false for the generic streaming kernel.
+bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl);
 
 }  // namespace lce
