@@ -1,6 +1,7 @@
 // Device helpers shared by the cross-entropy kernels (gfx950, wave64).
 #pragma once
 
+#include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -13,12 +13,16 @@
 // blockIdx.x, blockIdx.x + G, ...  A row is split into K rounds of 1024
 // 16-byte vectors; thread t owns vector (k * 1024 + t) of every round.  The
 // first KR rounds live in VGPRs, the next KL rounds in thread-private LDS
-// slots filled by direct global->LDS loads, so the row is read from HBM once.
-// Three passes run over the resident row: max (+ argmax), sum of
-// exponentials, gradient.  While pass 3 stores the gradient of round k it
-// already issues the load of round k of the workgroup's next row into the
-// same registers / LDS slot, so HBM traffic of the next row overlaps the
-// arithmetic of this one.
+// slots filled by direct buffer->LDS loads, so the row is read from HBM once.
+// Two passes run over the resident row:
+//   pass A, round by round as the data arrives: an online softmax (each
+//           thread keeps a running max m and the sum of exp(z - m) over its
+//           elements, rescaled when m grows), the argmax and sum z when asked;
+//   pass B, once the row's statistics are combined: the gradient.
+// While pass B stores the gradient of round k it already issues the load of
+// round k of the workgroup's next row into the same registers / LDS slot, and
+// pass A of that row starts on round 0 while later rounds are still on their
+// way, so the HBM traffic of one row overlaps the arithmetic of the next.
 //
 // The workgroups count the labels themselves (the mean scale needs n_valid
 // before any gradient is written), keep per-workgroup loss / n_correct
@@ -55,11 +59,14 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     constexpr int K = KR + KL;
     constexpr int KRV = KR > 0 ? KR : 1;
     __shared__ u32x4 lds_rows[KL > 0 ? KL * NT : 1];
-    __shared__ float sh_m[NWAVE], sh_s[NWAVE], sh_z[NWAVE];
-    __shared__ int sh_i[NWAVE];
+    // per-row combine slots, double-buffered by row parity: a wave still
+    // reading row r's slots is at most one barrier behind a wave writing row
+    // r+1's, never two
+    __shared__ float sh_m[2][NWAVE], sh_s[2][NWAVE], sh_z[2][NWAVE], sh_zs[2][NWAVE];
+    __shared__ int sh_i[2][NWAVE];
     __shared__ long long sh_c[2][NWAVE];
     __shared__ double sh_d[NWAVE];
-    __shared__ float sh_xy;
+    __shared__ float sh_xy[2];
     __shared__ int sh_flag;
 
     const int tid = threadIdx.x;
@@ -136,7 +143,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     double loss_acc = 0.0;
     long long correct = 0;
 
-    for (int64_t nxt; row < n; row = nxt) {
+    int pb = 0;   // parity of the row iteration (selects the combine slots)
+    for (int64_t nxt; row < n; row = nxt, pb ^= 1) {
         nxt = next_row(row + G);
         const __amdgpu_buffer_rsrc_t rn = row_rsrc(nxt, nxt < n);
         const __amdgpu_buffer_rsrc_t rp = row_rsrc(row, true);
@@ -151,9 +159,13 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const int vy = y / E, ey = y % E, ky = vy / NT, ty = vy % NT;
         const bool owner = tid == ty;
 
-        // ---- pass 1: row maximum of the raw logits (and its first index); the
-        // owner of the target element publishes x_y through LDS
-        float m = -INFINITY;
+        // ---- pass A: online softmax statistics, argmax, sum z; the target
+        // element is kept out of the sum (1 - p_y is then formed without
+        // cancellation) and its raw value is published through LDS
+        float m = -FLT_MAX;      // running max of z (finite start: no inf - inf)
+        float s = 0.0f;          // sum over this thread's elements j != y of exp(z_j - m)
+        float zs = 0.0f;         // sum of z (label smoothing)
+        float amv = -INFINITY;   // argmax: value and first index over the raw logits
         int am = 0x7fffffff;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -161,85 +173,119 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             const int idx = k * NT + tid;
             if (idx < nvec) {
                 const u32x4 vk = round_vec(k);
+                float x[E], z[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float x = EL::get(vk, e);
-                    if constexpr (ARGMAX) {
-                        if (x > m) {
-                            m = x;
-                            am = idx * E + e;
-                        }
+                    x[e] = EL::get(vk, e);
+                    z[e] = SOFTCAP ? cap.z_of_r(cap.r_of(x[e])) : x[e];
+                }
+                float rmax = z[0];
+#pragma unroll
+                for (int e = 1; e < E; ++e) rmax = fmaxf(rmax, z[e]);
+                if constexpr (ARGMAX) {
+                    float xmax = x[0];
+                    if constexpr (SOFTCAP) {
+#pragma unroll
+                        for (int e = 1; e < E; ++e) xmax = fmaxf(xmax, x[e]);
                     } else {
-                        m = fmaxf(m, x);
+                        xmax = rmax;
+                    }
+                    int first = E - 1;
+#pragma unroll
+                    for (int e = E - 2; e >= 0; --e)
+                        if (x[e] == xmax) first = e;
+                    if (xmax > amv) {                 // rounds come in index order: keep the first
+                        amv = xmax;
+                        am = idx * E + first;
                     }
                 }
-                if (k == ky && owner) {
-                    float sel = EL::get(vk, 0);
+                if constexpr (SMOOTH) {
 #pragma unroll
-                    for (int e = 1; e < E; ++e)
-                        if (e == ey) sel = EL::get(vk, e);
-                    sh_xy = sel;
+                    for (int e = 0; e < E; ++e) zs += z[e];
                 }
-            }
-        }
-        if constexpr (ARGMAX) {
-            block_argmax(m, am, sh_m, sh_i);
-            if (tid == 0) {
-                a.argmax_out[row] = am;
-                if (valid && am == y) ++correct;
-            }
-        } else {
-            m = block_max(m, sh_m);
-        }
-        const float xy = sh_xy;
-        float Mz, zy;
-        if constexpr (SOFTCAP) {
-            Mz = cap.z_of_r(cap.r_of(m));   // tanh is increasing: max z = cap(max x)
-            zy = cap.z_of_r(cap.r_of(xy));
-        } else {
-            Mz = m;
-            zy = xy;
-        }
-
-        // ---- pass 2: s = sum_{j != y} exp(z_j - Mz), zs = sum_j z_j
-        const float MzL = Mz * kLog2e;
-        const float capk = -2.0f * a.softcap * kLog2e;   // d(z log2 e)/dr
-        const float capb = (a.softcap - Mz) * kLog2e;    // (T - Mz) log2 e
-        float s = 0.0f, zs = 0.0f;
-        opaque_regs(v);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int idx = k * NT + tid;
-            if (idx < nvec) {
-                const u32x4 vk = round_vec(k);
+                const float mn = fmaxf(m, rmax);
+                const float mnL = mn * kLog2e;
+                float part = 0.0f;
                 float ex[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float x = EL::get(vk, e);
-                    if constexpr (SOFTCAP) {
-                        const float r = cap.r_of(x);
-                        ex[e] = exp2_fast(fmaf(r, capk, capb));
-                        if constexpr (SMOOTH) zs += cap.z_of_r(r);
-                    } else {
-                        ex[e] = exp2_fast(fmaf(x, kLog2e, -MzL));
-                        if constexpr (SMOOTH) zs += x;
+                for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], kLog2e, -mnL));
+                if (k == ky) {
+                    // the target's round (uniform branch, taken once per row); the
+                    // asm keeps it a branch instead of per-element selects everywhere
+                    asm volatile("");
+                    if (owner) {
+                        float sel = x[0];
+#pragma unroll
+                        for (int e = 1; e < E; ++e)
+                            if (e == ey) sel = x[e];
+                        sh_xy[pb] = sel;
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (e == ey) ex[e] = 0.0f;
                     }
                 }
-                if (k == ky) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if (owner && e == ey) ex[e] = 0.0f;
-                }
-                float part = ex[0];
+                part = ex[0];
 #pragma unroll
                 for (int e = 1; e < E; ++e) part += ex[e];
-                s += part;
+                s = fmaf(s, exp2_fast(fmaf(m, kLog2e, -mnL)), part);
+                m = mn;
             }
         }
-        s = block_sum(s, sh_s);
-        if constexpr (SMOOTH) zs = block_sum(zs, sh_z);
-
-        const float e_y = exp2_fast(fmaf(zy, kLog2e, -MzL));
+        // combine the threads' (m, s) pairs, then the argmax and sum z
+        {
+            float mw = m, sw = s;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float m2 = __shfl_xor(mw, o, 64), s2 = __shfl_xor(sw, o, 64);
+                const float mx = fmaxf(mw, m2);
+                sw = sw * exp2_fast((mw - mx) * kLog2e) + s2 * exp2_fast((m2 - mx) * kLog2e);
+                mw = mx;
+            }
+            if ((tid & 63) == 0) {
+                sh_m[pb][tid >> 6] = mw;
+                sh_s[pb][tid >> 6] = sw;
+            }
+            if constexpr (ARGMAX) {
+                wave_argmax(amv, am);
+                if ((tid & 63) == 0) {
+                    sh_z[pb][tid >> 6] = amv;
+                    sh_i[pb][tid >> 6] = am;
+                }
+            }
+            if constexpr (SMOOTH) {
+                zs = wave_sum(zs);
+                if ((tid & 63) == 0) sh_zs[pb][tid >> 6] = zs;
+            }
+            __syncthreads();
+            float M = sh_m[pb][0];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, sh_m[pb][w]);
+            float S0 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) S0 += sh_s[pb][w] * exp2_fast((sh_m[pb][w] - M) * kLog2e);
+            m = M;
+            s = S0;
+            if constexpr (ARGMAX) {
+                amv = sh_z[pb][0];
+                am = sh_i[pb][0];
+#pragma unroll
+                for (int w = 1; w < NWAVE; ++w) argmax_combine(amv, am, sh_z[pb][w], sh_i[pb][w]);
+                if (tid == 0) {
+                    a.argmax_out[row] = am;
+                    if (valid && am == y) ++correct;
+                }
+            }
+            if constexpr (SMOOTH) {
+                float t = sh_zs[pb][0];
+#pragma unroll
+                for (int w = 1; w < NWAVE; ++w) t += sh_zs[pb][w];
+                zs = t;
+            }
+        }
+        const float xy = sh_xy[pb];
+        const float Mz = m;
+        const float zy = SOFTCAP ? cap.z_of_r(cap.r_of(xy)) : xy;
+        const float e_y = exp2_fast(fmaf(zy, kLog2e, -Mz * kLog2e));
         const float S = s + e_y;
         const float lse = Mz + logf(S);
         if (tid == 0) {
@@ -250,12 +296,18 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             loss_acc += static_cast<double>(loss);
         }
 
-        // ---- pass 3: gradient over the logits; round k of the next row is
-        // requested as soon as round k of this row has been consumed
-        const float epsV = SMOOTH ? eps * invV : 0.0f;
-        const float lseL = lse * kLog2e;
-        const float capb2 = (a.softcap - lse) * kLog2e;
-        float gy = scale * (eps - s / S - epsV);          // p_y - (1 - eps) - eps/V
+        // ---- pass B: gradient over the logits.  |s_i| is folded into the
+        // exponent (exp(z - lse + ln|s_i|)), its sign applied to the packed
+        // result; round k of the next row is requested as soon as round k of
+        // this row has been consumed
+        const float ascale = fabsf(scale);
+        const bool negate = scale < 0.0f;
+        const float l2s = log2f(ascale);                  // -inf when the scale is 0
+        const float epsV = SMOOTH ? eps * invV * ascale : 0.0f;
+        const float lseL = lse * kLog2e - l2s;
+        const float capk = -2.0f * a.softcap * kLog2e;   // d(z log2 e)/dr
+        const float capb2 = (a.softcap - lse) * kLog2e + l2s;
+        float gy = scale * (eps - s / S - (SMOOTH ? eps * invV : 0.0f));   // s_i (p_y - (1 - eps) - eps/V)
         if constexpr (SOFTCAP) gy *= Cap::chain_of_r(cap.r_of(xy));
         opaque_regs(v);
 #pragma unroll
@@ -269,17 +321,25 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                     const float x = EL::get(vk, e);
                     if constexpr (SOFTCAP) {
                         const float r = cap.r_of(x);
-                        const float p = exp2_fast(fmaf(r, capk, capb2));
-                        g[e] = scale * (p - epsV) * Cap::chain_of_r(r);
+                        const float p = exp2_fast(fmaf(r, capk, capb2));        // |s_i| p_j
+                        g[e] = (SMOOTH ? p - epsV : p) * Cap::chain_of_r(r);
                     } else {
-                        const float p = exp2_fast(fmaf(x, kLog2e, -lseL));
-                        g[e] = scale * (p - epsV);
+                        const float p = exp2_fast(fmaf(x, kLog2e, -lseL));      // |s_i| p_j
+                        g[e] = SMOOTH ? p - epsV : p;
                     }
                 }
-                if (k == ky) {
+                if (negate) {
+                    asm volatile("");
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if (owner && e == ey) g[e] = gy;
+                    for (int e = 0; e < E; ++e) g[e] = -g[e];
+                }
+                if (k == ky) {
+                    asm volatile("");
+                    if (owner) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (e == ey) g[e] = gy;
+                    }
                 }
                 store_round(k, rp, EL::pack(g));
             }
