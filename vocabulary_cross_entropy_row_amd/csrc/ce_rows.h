@@ -19,10 +19,10 @@
 //           thread keeps a running max m and the sum of exp(z - m) over its
 //           elements, rescaled when m grows), the argmax and sum z when asked;
 //   pass B, once the row's statistics are combined: the gradient.
-// While pass B stores the gradient of round k it already issues the load of
-// round k of the workgroup's next row into the same registers / LDS slot, and
-// pass A of that row starts on round 0 while later rounds are still on their
-// way, so the HBM traffic of one row overlaps the arithmetic of the next.
+// As soon as pass B has stored the gradient, the loads of the workgroup's
+// next row go out into the same registers / LDS slots, and pass A of that row
+// starts on round 0 while later rounds are still on their way, so the HBM
+// traffic of one row overlaps the arithmetic of the next.
 //
 // The workgroups count the labels themselves (the mean scale needs n_valid
 // before any gradient is written), keep per-workgroup loss / n_correct
@@ -297,9 +297,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         }
 
         // ---- pass B: gradient over the logits.  |s_i| is folded into the
-        // exponent (exp(z - lse + ln|s_i|)), its sign applied to the packed
-        // result; round k of the next row is requested as soon as round k of
-        // this row has been consumed
+        // exponent (exp(z - lse + ln|s_i|)) and its sign applied afterwards
         const float ascale = fabsf(scale);
         const bool negate = scale < 0.0f;
         const float l2s = log2f(ascale);                  // -inf when the scale is 0
@@ -343,11 +341,15 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 }
                 store_round(k, rp, EL::pack(g));
             }
-            issue_round(k, rn);
-            // keep round k's next-row load behind round k's gradient: hoisted
-            // earlier it would hold two rows in registers at once and spill
+            // keep the rounds in order: hoisted loads or conversions of later
+            // rounds would hold extra row data in registers
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the next row is requested once this row's stores are all out: HBM
+        // turns between reads and writes less often than with per-round
+        // interleaving, and pass A of the next row consumes round 0 first
+#pragma unroll
+        for (int k = 0; k < K; ++k) issue_round(k, rn);
     }
 
     // ---- ignored tokens (when no argmax is wanted): zero gradient, no read

@@ -1,7 +1,7 @@
 // C-ABI entry points (include/lce.h): argument validation, then kernel launch.
 // Validation runs before any HIP call, so every argument error is reported
 // without touching the device.  No exception crosses the ABI.
-#include "../../include/lce.h"
+#include "lce.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>
