@@ -114,6 +114,42 @@ lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const 
                          int64_t *counts, hipStream_t stream);
 
 /*
+ * Bytes of device workspace lce_flce_fwd_bwd needs (0 for invalid sizes).  It
+ * holds W^T [H, V] and one chunk of logits / their transpose / split-K
+ * partials: about 2 H V + 4 C V + 2 H C + 32 C H bytes with C = min(chunk, n).
+ */
+size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens);
+
+/*
+ * Fused linear cross-entropy [P5 Summary, Memory; Details/Softcap]: the loss
+ * and gradients of cross-entropy over the logits Z = hidden * weight^T,
+ * processed in chunks of chunk_tokens tokens so only one chunk of logits
+ * exists at a time.  The row operation (ignore_index, label_smoothing,
+ * softcap, reduction, grad_out) is exactly that of lce_ce_fwd_bwd applied to Z;
+ * the mean's denominator counts every token's label.
+ *
+ *   hidden       device bf16 [n, H] row-major; any output multiplier is
+ *                already folded in by the caller [P5 Details/Softcap].
+ *   weight       device bf16 [V, H] row-major.
+ *   labels       device int64 [n].        grad_out  as for lce_ce_fwd_bwd.
+ *   loss_tok     device fp32 [n] (per-token losses of the bf16-rounded logits).
+ *   loss_out     device fp32 scalar or NULL.
+ *   grad_hidden  device bf16 [n, H]: dL/dhidden.
+ *   grad_weight  device fp32 [V, H]: dL/dweight, overwritten (not accumulated
+ *                across calls), accumulated in fp32 over the chunks [P5 Memory].
+ *   counts       device int64 [3] {n_valid, 0, n_bad}.
+ *   workspace    device, >= lce_flce_workspace_bytes(n, H, V, chunk_tokens)
+ *                bytes, 256-byte aligned; clobbered.
+ * Logits are formed in fp32 by bf16 MFMA and stored as bf16 for the row
+ * kernel.  H and V must be multiples of 8 (LCE_ERR_UNSUPPORTED otherwise).
+ */
+lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
+                            int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                            lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, float *loss_tok,
+                            float *loss_out, void *grad_hidden, float *grad_weight, int64_t *counts,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Text of the most recent error on the calling thread ("" if none).  Valid
  * until the next lce_* call on the same thread.
  */

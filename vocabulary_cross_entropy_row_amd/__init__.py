@@ -52,6 +52,11 @@ def lib() -> ctypes.CDLL:
                                  p, ctypes.c_size_t, p]
     L.lce_ce_argmax.restype = ctypes.c_int
     L.lce_ce_argmax.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, p, p, p]
+    L.lce_flce_workspace_bytes.restype = ctypes.c_size_t
+    L.lce_flce_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.lce_flce_fwd_bwd.restype = ctypes.c_int
+    L.lce_flce_fwd_bwd.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, i64, p, p, p, p, p, p,
+                                   ctypes.c_size_t, p]
     if L.lce_abi_version() != 1:
         raise ImportError("liblce.so ABI version mismatch; rebuild it")
     _lib = L
@@ -151,3 +156,55 @@ def lce_ce_argmax(logits, labels=None, *, ignore_index: int = -100, argmax_out=N
                              _ptr(argmax_out), _ptr(counts), _stream(stream))
     _check(st)
     return argmax_out, counts
+
+
+def lce_flce_workspace_bytes(n: int, H: int, V: int, chunk_tokens: int) -> int:
+    return int(lib().lce_flce_workspace_bytes(int(n), int(H), int(V), int(chunk_tokens)))
+
+
+@dataclass
+class FLCEResult:
+    loss_tok: object      # fp32 [n]
+    loss_out: object      # fp32 [1]
+    grad_hidden: object   # bf16 [n, H]
+    grad_weight: object   # fp32 [V, H]
+    counts: object        # int64 [3]
+
+
+def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
+                     softcap: float = 0.0, reduction: str = "mean", grad_out=None, chunk_tokens: int = 1024,
+                     loss_tok=None, loss_out=None, grad_hidden=None, grad_weight=None, counts=None, workspace=None,
+                     stream=None) -> FLCEResult:
+    """Fused linear cross-entropy of hidden [n, H] (bf16) and weight [V, H] (bf16), chunked over
+    tokens.  Outputs not passed in are allocated."""
+    import torch
+    for t, nm in ((hidden, "hidden"), (weight, "weight")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous 2-D bfloat16 tensor")
+    n, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if grad_out is not None and not torch.is_tensor(grad_out):
+        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=dev)
+    elif grad_out is not None and grad_out.dtype != torch.float32:
+        grad_out = grad_out.float()
+    if loss_tok is None:
+        loss_tok = torch.empty(n, dtype=torch.float32, device=dev)
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if grad_hidden is None:
+        grad_hidden = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    if grad_weight is None:
+        grad_weight = torch.empty((V, H), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(3, dtype=torch.int64, device=dev)
+    wsb = lce_flce_workspace_bytes(n, H, V, chunk_tokens)
+    if workspace is None:
+        workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    st = lib().lce_flce_fwd_bwd(_ptr(hidden), _ptr(weight), _ptr(labels), n, H, V, int(ignore_index),
+                                float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
+                                int(chunk_tokens), _ptr(loss_tok), _ptr(loss_out), _ptr(grad_hidden),
+                                _ptr(grad_weight), _ptr(counts), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+    return FLCEResult(loss_tok, loss_out, grad_hidden, grad_weight, counts)

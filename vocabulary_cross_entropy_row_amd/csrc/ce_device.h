@@ -178,12 +178,12 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *shv, int *
     for (int w = 1; w < NWAVE; ++w) argmax_combine(v, i, shv[w], shi[w]);
 }
 
-// Valid-label and bad-label counts over all n labels, by one workgroup.
+// Valid-label and bad-label counts over the count labels, by one workgroup.
 __device__ __forceinline__ void block_count_labels(const CEArgs &a, long long (*sh)[NWAVE], long long &nv,
                                                    long long &nb) {
     long long v = 0, b = 0;
-    for (int64_t i = threadIdx.x; i < a.n; i += NT) {
-        const int64_t y = a.labels[i];
+    for (int64_t i = threadIdx.x; i < a.count_n; i += NT) {
+        const int64_t y = a.count_labels[i];
         if (y != a.ignore_index) {
             if (y >= 0 && y < a.V) ++v;
             else ++b;

@@ -337,11 +337,18 @@ hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream) 
         // one launch: the persistent kernel counts labels and reduces on its own
         return launch_resident(a, is_bf16, kr, kl, stream);
     }
-    hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, a.labels, a.n, a.V, a.ignore_index,
-                       a.counts, static_cast<unsigned *>(a.workspace), a.loss_out);
+    hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, a.count_labels, a.count_n, a.V,
+                       a.ignore_index, a.counts, static_cast<unsigned *>(a.workspace), a.loss_out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.n == 0) return err;
     return is_bf16 ? launch_generic<true>(a, stream) : launch_generic<false>(a, stream);
+}
+
+hipError_t launch_ce_count(const int64_t *labels, int64_t n, int64_t V, int64_t ignore_index, int64_t *counts,
+                           unsigned *ticket, float *loss_out, hipStream_t stream) {
+    hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, labels, n, V, ignore_index, counts, ticket,
+                       loss_out);
+    return hipGetLastError();
 }
 
 hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n,

@@ -1,0 +1,264 @@
+// Fused linear cross-entropy for gfx950 (Liger-Kernel PR "Add Liger Kernel
+// support for Muse Glimmer": Summary -- the loss of hidden x weight^T without
+// forming the [tokens, V] logits; Memory -- grad_weight accumulated in fp32;
+// Details/Softcap -- T tanh(x / T), output multiplier already folded into
+// hidden by the caller).
+//
+// The tokens are processed in chunks of `chunk` rows.  Per chunk c:
+//   Z_c  = H_c W^T           bf16 MFMA GEMM, fp32 accumulate, stored bf16 [chunk, V]
+//   G_c  = CE(Z_c)           the resident row kernel, in place, with the mean
+//                            scale of all n tokens; per-token losses
+//   dH_c = G_c W             split-K MFMA GEMM into fp32 partials, folded to bf16
+//   dW  += G_c^T H_c         MFMA GEMM, fp32 read-modify-write (written on chunk 0)
+// Every GEMM runs in the one "A K-contiguous, B K-contiguous" form, so W^T
+// (once per call), H_c^T and G_c^T are produced by a bandwidth-bound
+// transpose first.  Only one chunk of logits exists at a time.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ce_device.h"
+#include "gemm_mfma.h"
+#include "lce_internal.h"
+
+namespace lce {
+namespace {
+
+using gemm::GemmArgs;
+
+// out[c][r] = in[r][c] for a [rows, cols] bf16 matrix (strides in elements);
+// output columns [rows, rows_pad) are written as zeros, so a GEMM may run its
+// K loop over whole 8-element chunks.  64 x 64 tiles through LDS; 16-byte
+// loads and stores where aligned.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *in, int64_t ld_in, uint16_t *out,
+                                                             int64_t ld_out, int rows, int rows_pad, int cols) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ uint16_t tile[64][64 + 8];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const int t = threadIdx.x;
+    const bool vin = ((ld_in & 7) == 0) && ((reinterpret_cast<uintptr_t>(in) & 15) == 0);
+    const bool vout = ((ld_out & 7) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+    // load: 64 rows x 8 chunks of 8 columns; 2 chunks per thread
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = t + h * 256;
+        const int r = idx >> 3, ch = idx & 7;
+        const int gr = r0 + r, gc = c0 + ch * 8;
+        if (vin && gr < rows && gc + 7 < cols) {
+            const u32x4 q = *reinterpret_cast<const u32x4 *>(in + static_cast<int64_t>(gr) * ld_in + gc);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                tile[r][ch * 8 + 2 * w] = static_cast<uint16_t>(q[w] & 0xffffu);
+                tile[r][ch * 8 + 2 * w + 1] = static_cast<uint16_t>(q[w] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tile[r][ch * 8 + e] =
+                    (gr < rows && gc + e < cols) ? in[static_cast<int64_t>(gr) * ld_in + gc + e] : uint16_t(0);
+        }
+    }
+    __syncthreads();
+    // store: output rows are input columns
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = t + h * 256;
+        const int orow = idx >> 3, ch = idx & 7;     // orow = input column, ch = chunk of input rows
+        const int gc = c0 + orow, gr = r0 + ch * 8;
+        if (gc >= cols) continue;
+        if (vout && gr + 7 < rows_pad) {
+            u32x4 q;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                q[w] = static_cast<uint32_t>(tile[ch * 8 + 2 * w][orow]) |
+                       (static_cast<uint32_t>(tile[ch * 8 + 2 * w + 1][orow]) << 16);
+            *reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(gc) * ld_out + gr) = q;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gr + e < rows_pad) out[static_cast<int64_t>(gc) * ld_out + gr + e] = tile[ch * 8 + e][orow];
+        }
+    }
+}
+
+// out[m][n] = bf16(sum_s part[s][m][n])   (part rows of stride N, splits of stride split_stride)
+__global__ __launch_bounds__(256) void splitk_fold_kernel(const float *part, int64_t split_stride, int splits,
+                                                          uint16_t *out, int64_t ld_out, int M, int N) {
+    const int64_t total = static_cast<int64_t>(M) * N;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += static_cast<int64_t>(gridDim.x) * 256) {
+        float s = 0.0f;
+        for (int k = 0; k < splits; ++k) s += part[k * split_stride + i];
+        const int64_t m = i / N, n = i - m * N;
+        reinterpret_cast<__bf16 *>(out)[m * ld_out + n] = static_cast<__bf16>(s);
+    }
+}
+
+// loss_out from all per-token losses (fixed-order fp64 sum): mean over the
+// valid count, or sum; 0 for 'none'
+__global__ __launch_bounds__(1024) void loss_fold_kernel(const float *loss_tok, int64_t n, const int64_t *counts,
+                                                         int reduction, float *loss_out) {
+    __shared__ double sh[16];
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) acc += static_cast<double>(loss_tok[i]);
+    acc = dev::wave_sum_d(acc);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < 16; ++w) tot += sh[w];
+        float out = 0.0f;
+        if (reduction == 1) out = counts[0] > 0 ? static_cast<float>(tot / static_cast<double>(counts[0])) : 0.0f;
+        else if (reduction == 2) out = static_cast<float>(tot);
+        *loss_out = out;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_f32_kernel(float *p, int64_t n) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) p[i] = 0.0f;
+}
+
+int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, int rows, int rows_pad, int cols,
+                     hipStream_t st) {
+    if (rows_pad <= 0 || cols <= 0) return hipSuccess;
+    const dim3 grid(ceil_div(cols, 64), ceil_div(rows_pad, 64));
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t *>(in), ld_in,
+                       static_cast<uint16_t *>(out), ld_out, rows, rows_pad, cols);
+    return hipGetLastError();
+}
+
+// C (+)= A B^T over [M, N] with K split into `splits` ranges
+hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, int M,
+                   int N, int K, int splits, int64_t c_split_stride, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if ((K & 7) || (lda & 7) || (ldb & 7) || (reinterpret_cast<uintptr_t>(A) & 15) ||
+        (reinterpret_cast<uintptr_t>(B) & 15))
+        return hipErrorInvalidValue;
+    GemmArgs g;
+    g.A = static_cast<const uint16_t *>(A);
+    g.B = static_cast<const uint16_t *>(B);
+    g.C = C;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = ldc;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.splits = splits;
+    g.c_split_stride = c_split_stride;
+    g.tiles_m = ceil_div(M, gemm::BM);
+    g.tiles_n = ceil_div(N, gemm::BN);
+    const int64_t total = static_cast<int64_t>(g.tiles_m) * g.tiles_n * splits;
+    g.tiles_per_xcd = ceil_div(total, 8);
+    const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u);
+    if (mode == gemm::OUT_BF16)
+        hipLaunchKernelGGL(gemm::gemm_nt_kernel<gemm::OUT_BF16>, grid, dim3(gemm::NTHR), 0, st, g);
+    else if (mode == gemm::OUT_F32)
+        hipLaunchKernelGGL(gemm::gemm_nt_kernel<gemm::OUT_F32>, grid, dim3(gemm::NTHR), 0, st, g);
+    else
+        hipLaunchKernelGGL(gemm::gemm_nt_kernel<gemm::OUT_F32_ACC>, grid, dim3(gemm::NTHR), 0, st, g);
+    return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+int64_t round8(int64_t x) { return (x + 7) & ~static_cast<int64_t>(7); }
+
+}  // namespace
+
+FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk) {
+    FlceLayout L;
+    const int64_t C = chunk < n ? chunk : (n > 0 ? n : 1);
+    L.chunk = C;
+    L.splits = kFlceSplitK;
+    size_t off = 0;
+    L.off_wt = off;    off += align256(static_cast<size_t>(H) * V * 2);
+    L.off_z = off;     off += align256(static_cast<size_t>(C) * V * 2);
+    // the transposed chunk operands use a row stride of C rounded up to 8
+    // elements (16-byte rows for the direct-to-LDS loads)
+    L.off_gt = off;    off += align256(static_cast<size_t>(V) * round8(C) * 2);
+    L.off_ht = off;    off += align256(static_cast<size_t>(H) * round8(C) * 2);
+    L.off_part = off;  off += align256(static_cast<size_t>(L.splits) * C * H * 4);
+    L.off_ce = off;    off += align256(ce_workspace_bytes(C));
+    L.bytes = off;
+    return L;
+}
+
+hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
+    hipError_t e;
+    const FlceLayout L = flce_layout(f.n, f.H, f.V, f.chunk);
+    char *ws = static_cast<char *>(f.workspace);
+    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
+    uint16_t *z = reinterpret_cast<uint16_t *>(ws + L.off_z);
+    uint16_t *gt = reinterpret_cast<uint16_t *>(ws + L.off_gt);
+    uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.off_ht);
+    float *part = reinterpret_cast<float *>(ws + L.off_part);
+    void *ce_ws = ws + L.off_ce;
+    const int64_t C = L.chunk, Cp = round8(C), H = f.H, V = f.V;
+
+    // counts (and a zeroed completion counter for the chunk CE calls)
+    if ((e = launch_ce_count(f.labels, f.n, V, f.ignore_index, f.counts, static_cast<unsigned *>(ce_ws), f.loss_out,
+                             st)) != hipSuccess)
+        return e;
+    if (f.n == 0) {
+        const int64_t tot = V * H;
+        hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(2048), dim3(256), 0, st, f.grad_weight, tot);
+        return hipGetLastError();
+    }
+    // W^T [H, V]
+    if ((e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), st)) !=
+        hipSuccess)
+        return e;
+
+    for (int64_t c0 = 0; c0 < f.n; c0 += C) {
+        const int cn = static_cast<int>(f.n - c0 < C ? f.n - c0 : C);
+        const int cnp = static_cast<int>(round8(cn));   // K of the dW GEMM: zero-padded to whole chunks
+        const uint16_t *hc = static_cast<const uint16_t *>(f.hidden) + c0 * H;
+        // H_c^T [H, cnp] (row stride Cp)
+        if ((e = transpose(hc, H, ht, Cp, cn, cnp, static_cast<int>(H), st)) != hipSuccess) return e;
+        // Z_c = H_c W^T  -> bf16 [cn, V]
+        if ((e = gemm_nt(gemm::OUT_BF16, hc, H, f.weight, H, z, V, cn, static_cast<int>(V), static_cast<int>(H), 1, 0,
+                         st)) != hipSuccess)
+            return e;
+        // G_c = CE(Z_c) in place, mean scale over all n tokens
+        CEArgs a;
+        a.logits = z;
+        a.ld = V;
+        a.n = cn;
+        a.V = V;
+        a.labels = f.labels + c0;
+        a.count_labels = f.labels;
+        a.count_n = f.n;
+        a.ignore_index = f.ignore_index;
+        a.eps = f.eps;
+        a.softcap = f.softcap;
+        a.reduction = f.reduction;
+        a.grad_out = (f.reduction == 0 && f.grad_out) ? f.grad_out + c0 : f.grad_out;
+        a.loss_tok = f.loss_tok + c0;
+        a.loss_out = nullptr;
+        a.argmax_out = nullptr;
+        a.counts = f.counts;
+        a.workspace = ce_ws;
+        if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
+        // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
+        if ((e = gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H), static_cast<int>(V), L.splits,
+                         C * H, st)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(splitk_fold_kernel, dim3(1024), dim3(256), 0, st, part, C * H, L.splits,
+                           static_cast<uint16_t *>(f.grad_hidden) + c0 * H, H, cn, static_cast<int>(H));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        // G_c^T [V, cnp] (row stride Cp)
+        if ((e = transpose(z, V, gt, Cp, cn, cnp, static_cast<int>(V), st)) != hipSuccess) return e;
+        // dW (+)= G_c^T H_c
+        if ((e = gemm_nt(c0 == 0 ? gemm::OUT_F32 : gemm::OUT_F32_ACC, gt, Cp, ht, Cp, f.grad_weight, H,
+                         static_cast<int>(V), static_cast<int>(H), cnp, 1, 0, st)) != hipSuccess)
+            return e;
+    }
+    if (f.loss_out) {
+        hipLaunchKernelGGL(loss_fold_kernel, dim3(1), dim3(1024), 0, st, f.loss_tok, f.n, f.counts, f.reduction,
+                           f.loss_out);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace lce

@@ -89,6 +89,8 @@ lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const
     a.n = n;
     a.V = V;
     a.labels = labels;
+    a.count_labels = labels;
+    a.count_n = n;
     a.ignore_index = ignore_index;
     a.eps = label_smoothing;
     a.softcap = softcap;
@@ -124,6 +126,68 @@ lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const 
     return hip_status(lce::launch_ce_argmax(logits, ld, dtype == LCE_BF16, labels, n, V, ignore_index, argmax_out,
                                             counts, stream),
                       "lce_ce_argmax launch");
+}
+
+size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens) {
+    if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1) return 0;
+    return lce::flce_layout(n, H, V, chunk_tokens).bytes;
+}
+
+lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
+                            int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                            lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, float *loss_tok,
+                            float *loss_out, void *grad_hidden, float *grad_weight, int64_t *counts, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "lce_flce_fwd_bwd";
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "%s: n must be >= 0 (got %lld)", fn, (long long)n);
+    if (H < 1) return fail(LCE_ERR_INVALID_ARG, "%s: H must be >= 1 (got %lld)", fn, (long long)H);
+    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "%s: V must be >= 1 (got %lld)", fn, (long long)V);
+    if (chunk_tokens < 1) return fail(LCE_ERR_INVALID_ARG, "%s: chunk_tokens must be >= 1", fn);
+    if (reduction != LCE_RED_NONE && reduction != LCE_RED_MEAN && reduction != LCE_RED_SUM)
+        return fail(LCE_ERR_INVALID_ARG, "%s: unknown reduction %d", fn, (int)reduction);
+    if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
+        return fail(LCE_ERR_INVALID_ARG, "%s: label_smoothing must be in [0, 1] (got %g)", fn, (double)label_smoothing);
+    if (!(softcap >= 0.0f) || isinf(softcap))
+        return fail(LCE_ERR_INVALID_ARG, "%s: softcap must be finite and >= 0 (got %g)", fn, (double)softcap);
+    if (!weight || !grad_weight || !counts || !workspace)
+        return fail(LCE_ERR_INVALID_ARG, "%s: weight, grad_weight, counts and workspace are required", fn);
+    if (n > 0 && (!hidden || !labels || !loss_tok || !grad_hidden))
+        return fail(LCE_ERR_INVALID_ARG, "%s: hidden, labels, loss_tok and grad_hidden are required", fn);
+    const size_t need = lce_flce_workspace_bytes(n, H, V, chunk_tokens);
+    if (workspace_bytes < need)
+        return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < required %zu", fn, workspace_bytes, need);
+    if (!is_aligned(workspace, 256)) return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    if (H % 8 != 0 || V % 8 != 0)
+        return fail(LCE_ERR_UNSUPPORTED, "%s: requires H and V to be multiples of 8 (16-byte bf16 rows); got H=%lld V=%lld",
+                    fn, (long long)H, (long long)V);
+    if ((hidden && !is_aligned(hidden, 16)) || !is_aligned(weight, 16) || (grad_hidden && !is_aligned(grad_hidden, 16)) ||
+        !is_aligned(grad_weight, 16))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: hidden, weight, grad_hidden and grad_weight must be 16-byte aligned", fn);
+    const int64_t C = chunk_tokens < n ? chunk_tokens : n;
+    if (V > 0x7fffffffLL / 16 || H > 0x7fffffffLL / 16 || C > 0x7fffffffLL / 16 ||
+        static_cast<unsigned long long>(C) * V * 2 >= (1ull << 32) || 256ull * V * 2 >= (1ull << 32) ||
+        256ull * H * 2 >= (1ull << 32))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: a chunk of logits or a 256-row operand tile exceeds 4 GiB", fn);
+    lce::FlceArgs f;
+    f.hidden = hidden;
+    f.weight = weight;
+    f.labels = labels;
+    f.n = n;
+    f.H = H;
+    f.V = V;
+    f.chunk = chunk_tokens;
+    f.ignore_index = ignore_index;
+    f.eps = label_smoothing;
+    f.softcap = softcap;
+    f.reduction = static_cast<int>(reduction);
+    f.grad_out = grad_out;
+    f.loss_tok = loss_tok;
+    f.loss_out = loss_out;
+    f.grad_hidden = grad_hidden;
+    f.grad_weight = grad_weight;
+    f.counts = counts;
+    f.workspace = workspace;
+    return hip_status(lce::launch_flce(f, stream), "lce_flce_fwd_bwd launch");
 }
 
 }  // extern "C"

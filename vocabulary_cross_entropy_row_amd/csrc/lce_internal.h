@@ -14,6 +14,10 @@ struct CEArgs {
     int64_t n;
     int64_t V;
     const int64_t *labels;
+    // labels whose valid count is the mean's denominator (the rows' own labels
+    // for a plain call; every token's labels for a chunk of a fused-linear call)
+    const int64_t *count_labels;
+    int64_t count_n;
     int64_t ignore_index;
     float eps;               // label smoothing
     float softcap;           // 0 = off
@@ -50,5 +54,40 @@ hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const 
 // Which row kernel a shape takes: rounds in VGPRs (*kr) and LDS (*kl), or
 // false for the generic streaming kernel.
 bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl);
+
+// counts = {n_valid, 0, n_bad} over labels[0, n); zeroes *ticket and *loss_out when given.
+hipError_t launch_ce_count(const int64_t *labels, int64_t n, int64_t V, int64_t ignore_index, int64_t *counts,
+                           unsigned *ticket, float *loss_out, hipStream_t stream);
+
+// ---- fused linear cross-entropy ----------------------------------------------
+
+// K splits of the grad_hidden GEMM (K = V is long and M x N = chunk x H is small).
+constexpr int kFlceSplitK = 8;
+
+struct FlceArgs {
+    const void *hidden;      // bf16 [n, H]
+    const void *weight;      // bf16 [V, H]
+    const int64_t *labels;   // [n]
+    int64_t n, H, V, chunk;
+    int64_t ignore_index;
+    float eps, softcap;
+    int reduction;
+    const float *grad_out;   // NULL, scalar or [n]
+    float *loss_tok;         // [n]
+    float *loss_out;         // scalar or NULL
+    void *grad_hidden;       // bf16 [n, H]
+    float *grad_weight;      // fp32 [V, H], overwritten
+    int64_t *counts;         // [3]
+    void *workspace;
+};
+
+// Offsets (bytes) of the fused-linear workspace regions.
+struct FlceLayout {
+    int64_t chunk;
+    int splits;
+    size_t off_wt, off_z, off_gt, off_ht, off_part, off_ce, bytes;
+};
+FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk);
+hipError_t launch_flce(const FlceArgs &f, hipStream_t stream);
 
 }  // namespace lce
