@@ -1,6 +1,10 @@
 #!/usr/bin/env python3
 """Bench: cross-entropy forward+backward on MI355X through the C ABI.
 
+`--workload flce_bf16_4096x6656x202048` benches the fused linear variant instead (one step =
+one lce_flce_fwd_bwd call; value = 6 N H V flops per step over the step time, against the dense
+bf16 MFMA peak).
+
 One step = one lce_ce_fwd_bwd call (one persistent kernel launch: label count, per-token
 loss, reduced loss, argmax/accuracy when the workload asks for it, gradient written in
 place) over one batch of synthetic logits already resident in HBM.  The gradient
@@ -32,6 +36,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CE fwd+bwd ms and HBM GB/s (% peak), bf16 logits 2048×131072, 1 GPU"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
+FLCE_METRIC = "FLCE fwd+bwd ms and bf16 MFMA TFLOP/s (% peak), hidden 4096×6656, weight 202048×6656, 1 GPU"
 CSRC = os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -82,17 +88,24 @@ def cpu_baseline(w, x, y, nthreads: int, min_seconds: float = 10.0) -> dict:
 
 # ---------------------------------------------------------------- counter summaries
 
-def kernel_source_hash() -> str:
+# the sources each measured kernel is compiled from: the persistent row kernel, and for the
+# fused variant also its GEMM, transposes and driver
+CE_SOURCES = ("ce_device.h", "ce_rows.h", "ce_rows_inst.hip")
+FLCE_SOURCES = CE_SOURCES + ("lce_internal.h", "ce_kernels.hip", "gemm_mfma.h", "flce.hip")
+
+
+def kernel_source_hash(workload: str = "") -> str:
+    files = FLCE_SOURCES if workload.startswith("flce") else CE_SOURCES
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".h", ".hip", ".cpp")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
 def profile_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"ce_rows_kernel__{workload}.txt")
+    kind = "flce_gemm" if workload.startswith("flce") else "ce_rows_kernel"
+    return os.path.join(PROFILES, f"{kind}__{workload}.txt")
 
 
 def read_profile(workload: str) -> dict | None:
@@ -175,7 +188,198 @@ def collect_profiles(workload: str) -> int:
         f"write_scale: {wscale:.4f}",
         f"traffic_bytes_per_dispatch: {traffic:.0f}",
         f"algorithmic_bytes_per_dispatch: {algorithmic_bytes(w)}",
-        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"kernel_source_sha256_16: {kernel_source_hash(workload)}",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(profile_path(workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(profile_path(workload)).read(), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------- fused linear variant
+
+def flce_flops(w) -> int:
+    # Z = H W^T, dH = G W, dW = G^T H: three dense contractions of 2 N H V flops each
+    return 6 * w.n * w.H * w.V
+
+
+def flce_cpu_baseline(w, hb, wb, y, nthreads: int) -> dict:
+    """The oracle as it stands on a slice of the workload: the first `nthreads` tokens (one per host
+    thread) with the full H and V; it forms Z, the per-token CE and both gradients in fp64."""
+    import oracle
+    k = max(1, nthreads)
+    t0 = time.perf_counter()
+    oracle.default().flce(hb[:k], wb, y[:k], label_smoothing=w.label_smoothing, softcap=w.softcap,
+                          reduction=w.reduction, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": round(6 * k * w.H * w.V / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"first {k} tokens with the full H={w.H} and V={w.V} (6 k H V flops), fp64 loss, "
+                      f"grad_hidden and grad_weight"}
+
+
+def flce_setup(w, dev):
+    import numpy as np
+    import torch
+
+    import synth
+    hb = synth.flce_hidden_rows(w, np.arange(w.n))
+    wb = synth.flce_weight_rows(w, np.arange(w.V))
+    y = synth.labels(w)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    return hb, wb, y, up(hb), up(wb), torch.from_numpy(y).to(dev)
+
+
+def bench_flce(args, w) -> int:
+    import numpy as np
+    import torch
+
+    import vocabulary_cross_entropy_row_amd as lce
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hb, wb, y, hidden, weight, labels = flce_setup(w, dev)
+    print(f"# inputs resident: hidden {tuple(hidden.shape)}, weight {tuple(weight.shape)}", file=sys.stderr,
+          flush=True)
+    # a plain copy of known size: the reference that scales the traffic counters (untimed)
+    ref_src = torch.empty(256 << 20, dtype=torch.int32, device=dev)
+    torch.empty_like(ref_src).copy_(ref_src)
+    grad_out = torch.full((1,), w.grad_out, dtype=torch.float32, device=dev)
+    loss_tok = torch.empty(w.n, dtype=torch.float32, device=dev)
+    loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    grad_hidden = torch.empty((w.n, w.H), dtype=torch.bfloat16, device=dev)
+    grad_weight = torch.empty((w.V, w.H), dtype=torch.float32, device=dev)
+    counts = torch.empty(3, dtype=torch.int64, device=dev)
+    wsb = lce.lce_flce_workspace_bytes(w.n, w.H, w.V, w.chunk)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lce.lce_flce_fwd_bwd(hidden, weight, labels, label_smoothing=w.label_smoothing, softcap=w.softcap,
+                             reduction=w.reduction, grad_out=grad_out, chunk_tokens=w.chunk, loss_tok=loss_tok,
+                             loss_out=loss_out, grad_hidden=grad_hidden, grad_weight=grad_weight, counts=counts,
+                             workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+        print(f"# step {i} issued", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean(per_call_ms))
+    flops = flce_flops(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    prof = read_profile(w.name)
+    traffic = None
+    if prof and prof.get("kernel_source_sha256_16") == kernel_source_hash(w.name):
+        traffic = int(prof["traffic_bytes_per_dispatch"])
+    out = {
+        "metric": FLCE_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "H": w.H, "V": w.V, "chunk_tokens": w.chunk,
+                   "hidden_scale": w.hidden_scale, "w_sigma": w.w_sigma, "ignore_frac": w.ignore_frac,
+                   "softcap": w.softcap, "label_smoothing": w.label_smoothing, "reduction": w.reduction,
+                   "workspace_bytes": wsb, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "lce_flce_fwd_bwd call (all its GEMM, CE and transpose launches), HIP events per call",
+                     "call_ms_mean": round(call_ms, 4), "call_ms_min": round(min(per_call_ms), 4),
+                     "call_ms_max": round(max(per_call_ms), 4), "algorithmic_flops": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        nthr = len(os.sched_getaffinity(0))
+        if os.environ.get("OMP_NUM_THREADS"):
+            nthr = min(nthr, int(os.environ["OMP_NUM_THREADS"]))
+        out["cpu_baseline"] = flce_cpu_baseline(w, hb, wb, y, nthr)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def collect_profiles_flce(workload: str) -> int:
+    import synth
+    w = synth.FLCE_WORKLOADS[workload]
+    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", workload)
+    os.makedirs(raw, exist_ok=True)
+    base = ["--workload", workload, "--no-cpu-baseline"]
+    _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "3", "--warmup", "1"], 600)
+    _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "1", "--warmup", "1"], 600)
+    _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "1", "--warmup", "1"], 600)
+    stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
+    calls = 4   # warmup + steps of the trace run
+    ref_kib = (256 << 20) * 4 / 1024.0
+    ours = ("gemm_nt_kernel", "transpose_bf16_kernel", "splitk_fold_kernel", "ce_rows_kernel", "ce_count_kernel",
+            "loss_fold_kernel", "fill_zero_f32_kernel", "ce_row_generic")
+
+    def counter(sub: str, cname: str):
+        rows = list(csv.DictReader(open(os.path.join(raw, sub, "run_counter_collection.csv"))))
+        rows = [r for r in rows if r["Counter_Name"] == cname]
+        k = [float(r["Counter_Value"]) for r in rows if any(o in r["Kernel_Name"] for o in ours)]
+        c = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+             and int(r["Grid_Size"]) >= (1 << 20)]
+        # per call: the run makes 2 calls (1 warmup + 1 step); the reference copy is the largest copy
+        return sum(k) / 2.0, max(c), len(k)
+
+    fk, fc, nfk = counter("fetch", "FETCH_SIZE")
+    wk, wc, nwk = counter("write", "WRITE_SIZE")
+    fscale, wscale = ref_kib / fc, ref_kib / wc
+    traffic = (fk * fscale + wk * wscale) * 1024.0
+    b = " ".join(base)
+    total_ns = sum(float(r["TotalDurationNs"]) for r in stats if any(o in r["Name"] for o in ours)) / calls
+    lines = [
+        f"# rocprofv3 summary: fused linear cross-entropy, workload {workload}",
+        f"# (hidden {w.n} x {w.H}, weight {w.V} x {w.H} bf16, chunk {w.chunk}, softcap {w.softcap})",
+        f"# made by: python bench.py --collect-profiles --workload {workload}",
+        "# which runs, from /tmp with TMPDIR=/tmp:",
+        f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 3 --warmup 1",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <raw>/fetch -o run -- python bench.py {b} --steps 1 --warmup 1",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <raw>/write -o run -- python bench.py {b} --steps 1 --warmup 1",
+        "# Counter scale: what each counter reads for a plain 1 GiB device copy (__amd_rocclr_copyBuffer)",
+        "# made once before timing, divided into its known size.  Traffic is per lce_flce_fwd_bwd call,",
+        "# summed over all of its kernels.",
+        "#",
+        "# kernel trace (--stats), nanoseconds (per-call share = total / calls):",
+    ]
+    for r in stats:
+        lines.append(f"#   {r['Name'][:80]:<80} calls {r['Calls']:>5} avg {float(r['AverageNs']):>12.1f} "
+                     f"per-call-share {float(r['TotalDurationNs']) / calls / 1e6:>8.3f} ms")
+    gemm = [r for r in stats if "gemm_nt_kernel" in r["Name"]]
+    gemm_ns = sum(float(r["TotalDurationNs"]) for r in gemm) / calls
+    lines += [
+        f"call_kernel_ns: {total_ns:.0f}",
+        f"gemm_kernel_ns_per_call: {gemm_ns:.0f}",
+        f"gemm_tflops: {flce_flops(w) / (gemm_ns * 1e-9) / 1e12:.1f}",
+        f"call_tflops_kernels_only: {flce_flops(w) / (total_ns * 1e-9) / 1e12:.1f}",
+        f"fetch_kib_per_call: {fk:.1f}   ({nfk} dispatches)",
+        f"copy_fetch_kib: {fc:.1f}",
+        f"fetch_scale: {fscale:.4f}",
+        f"write_kib_per_call: {wk:.1f}   ({nwk} dispatches)",
+        f"copy_write_kib: {wc:.1f}",
+        f"write_scale: {wscale:.4f}",
+        f"traffic_bytes_per_dispatch: {traffic:.0f}",
+        f"algorithmic_flops_per_call: {flce_flops(w)}",
+        f"kernel_source_sha256_16: {kernel_source_hash(workload)}",
     ]
     os.makedirs(PROFILES, exist_ok=True)
     with open(profile_path(workload), "w") as f:
@@ -188,17 +392,23 @@ def collect_profiles(workload: str) -> int:
 
 def main() -> int:
     args = parse()
+    import synth
     if args.collect_profiles:
+        if args.workload in synth.FLCE_WORKLOADS:
+            return collect_profiles_flce(args.workload)
         return collect_profiles(args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (token rows would shard "
+              "across GPUs with no exchange but the valid count and the loss sum). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
+
+    if args.workload in synth.FLCE_WORKLOADS:
+        return bench_flce(args, synth.FLCE_WORKLOADS[args.workload])
 
     import numpy as np
     import torch
 
-    import synth
     import vocabulary_cross_entropy_row_amd as lce
 
     w = synth.WORKLOADS[args.workload]
@@ -248,7 +458,7 @@ def main() -> int:
     nbytes = algorithmic_bytes(w)
     prof = read_profile(w.name)
     traffic = None
-    if prof and prof.get("kernel_source_sha256_16") == kernel_source_hash():
+    if prof and prof.get("kernel_source_sha256_16") == kernel_source_hash(w.name):
         traffic = int(prof["traffic_bytes_per_dispatch"])
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (call_ms * 1e-3) / 1e9

@@ -114,11 +114,23 @@ lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const 
                          int64_t *counts, hipStream_t stream);
 
 /*
- * Bytes of device workspace lce_flce_fwd_bwd needs (0 for invalid sizes).  It
- * holds W^T [H, V] and one chunk of logits / their transpose / split-K
- * partials: about 2 H V + 4 C V + 2 H C + 32 C H bytes with C = min(chunk, n).
+ * Bytes of device workspace lce_flce_fwd_bwd uses by default (0 for invalid
+ * sizes).  It holds W^T [H, V], one chunk of logits [C, V], split-K partials
+ * [16, C, H] fp32, and the transposed gradients and hidden states of one
+ * grad_weight group, [V + H, G] bf16: about 2 H V + 2 C V + 64 C H + 2 (V + H) G
+ * bytes with C = min(chunk, n).  The default group G is as many chunks as
+ * 2 GiB holds (at least one, at most all n tokens); grad_weight is written once
+ * per group, so fewer groups mean less grad_weight traffic.
  */
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens);
+
+/*
+ * Bytes of workspace for grad_weight groups of group_chunks chunks (0 for
+ * invalid sizes); group_chunks = 1 is the smallest workspace
+ * lce_flce_fwd_bwd accepts.
+ */
+size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens,
+                                        int64_t group_chunks);
 
 /*
  * Fused linear cross-entropy [P5 Summary, Memory; Details/Softcap]: the loss
@@ -138,8 +150,11 @@ size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_t
  *   grad_weight  device fp32 [V, H]: dL/dweight, overwritten (not accumulated
  *                across calls), accumulated in fp32 over the chunks [P5 Memory].
  *   counts       device int64 [3] {n_valid, 0, n_bad}.
- *   workspace    device, >= lce_flce_workspace_bytes(n, H, V, chunk_tokens)
- *                bytes, 256-byte aligned; clobbered.
+ *   workspace    device, 256-byte aligned, clobbered; at least
+ *                lce_flce_workspace_bytes_grouped(n, H, V, chunk_tokens, 1)
+ *                bytes (LCE_ERR_INVALID_ARG otherwise).  The call uses the
+ *                largest grad_weight group, up to the default one, whose
+ *                layout fits workspace_bytes.
  * Logits are formed in fp32 by bf16 MFMA and stored as bf16 for the row
  * kernel.  H and V must be multiples of 8 (LCE_ERR_UNSUPPORTED otherwise).
  */

@@ -79,6 +79,7 @@ C5_SMALL = FLCEWorkload("flce_bf16_256x512x8192", 1005, 256, 512, 8192, 0.5, 0.0
                         softcap=30.0, chunk=64)
 
 WORKLOADS = {w.name: w for w in (C1, C2, C3, C4)}
+FLCE_WORKLOADS = {w.name: w for w in (C5, C5_SMALL)}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -101,3 +101,56 @@ def test_argmax_rejects_bad_arguments(over, needle):
                                  a["argmax"], a["counts"], a["stream"])
     assert st == lce.LCE_ERR_INVALID_ARG
     assert needle in lce.lce_last_error()
+
+
+def call_flce(**over):
+    wsb_default = lce.lce_flce_workspace_bytes(64, 64, 512, 32)
+    args = dict(hidden=FAKE, weight=FAKE, labels=FAKE, n=64, H=64, V=512, ignore_index=-100, eps=0.0, softcap=0.0,
+                red=lce.LCE_RED_MEAN, grad_out=None, chunk=32, loss_tok=FAKE, loss_out=None, grad_hidden=FAKE,
+                grad_weight=FAKE, counts=FAKE, ws=ALIGNED_WS, wsb=wsb_default, stream=None)
+    args.update(over)
+    a = args
+    st = lce.lib().lce_flce_fwd_bwd(a["hidden"], a["weight"], a["labels"], a["n"], a["H"], a["V"], a["ignore_index"],
+                                    a["eps"], a["softcap"], a["red"], a["grad_out"], a["chunk"], a["loss_tok"],
+                                    a["loss_out"], a["grad_hidden"], a["grad_weight"], a["counts"], a["ws"], a["wsb"],
+                                    a["stream"])
+    return st, lce.lce_last_error()
+
+
+@pytest.mark.parametrize("over,needle,status", [
+    (dict(n=-1), "n must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(H=0), "H must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(V=0), "V must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(chunk=0), "chunk_tokens", lce.LCE_ERR_INVALID_ARG),
+    (dict(red=7), "reduction", lce.LCE_ERR_INVALID_ARG),
+    (dict(eps=2.0), "label_smoothing", lce.LCE_ERR_INVALID_ARG),
+    (dict(softcap=float("nan")), "softcap", lce.LCE_ERR_INVALID_ARG),
+    (dict(weight=None), "weight", lce.LCE_ERR_INVALID_ARG),
+    (dict(grad_weight=None), "grad_weight", lce.LCE_ERR_INVALID_ARG),
+    (dict(hidden=None), "hidden", lce.LCE_ERR_INVALID_ARG),
+    (dict(wsb=1024), "minimum", lce.LCE_ERR_INVALID_ARG),
+    (dict(ws=ALIGNED_WS + 16), "aligned", lce.LCE_ERR_INVALID_ARG),
+    (dict(H=60, wsb=1 << 26), "multiples of 8", lce.LCE_ERR_UNSUPPORTED),
+    (dict(V=1004, wsb=1 << 26), "multiples of 8", lce.LCE_ERR_UNSUPPORTED),
+    (dict(hidden=FAKE + 8), "aligned", lce.LCE_ERR_UNSUPPORTED),
+])
+def test_flce_rejects_bad_arguments(over, needle, status):
+    st, msg = call_flce(**over)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_flce_workspace_groups():
+    """The default workspace holds every chunk's transposed gradient at this size (one grad_weight
+    pass); one-chunk groups need less, and any size between the two is accepted."""
+    n, H, V, C = 4096, 6656, 202048, 1024
+    full = lce.lce_flce_workspace_bytes(n, H, V, C)
+    one = lce.lce_flce_workspace_bytes_grouped(n, H, V, C, 1)
+    assert full == lce.lce_flce_workspace_bytes_grouped(n, H, V, C, 4) == lce.lce_flce_workspace_bytes_grouped(n, H, V, C, 9)
+    assert one < lce.lce_flce_workspace_bytes_grouped(n, H, V, C, 2) < full
+    # the transposed group buffers: (V + H) x tokens x 2 bytes
+    assert full - one == pytest.approx((V + H) * (n - C) * 2, rel=1e-3)
+    assert lce.lce_flce_workspace_bytes_grouped(n, H, V, C, 0) == 0
+    # one byte short of the one-chunk layout is rejected before any device work
+    st, msg = call_flce(n=n, H=H, V=V, chunk=C, wsb=one - 1)
+    assert st == lce.LCE_ERR_INVALID_ARG and "minimum" in msg

@@ -38,18 +38,23 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
 
 
-def run_flce(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64):
+def run_flce(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64, group_chunks=None):
     g = None
     if grad_out is not None:
         g = torch.from_numpy(np.asarray(grad_out, dtype=np.float32).reshape(-1)).to(DEV)
+    ws = None
+    if group_chunks is not None:
+        n, H = hb.shape
+        ws = torch.zeros(lce.lce_flce_workspace_bytes_grouped(n, H, wb.shape[0], chunk, group_chunks),
+                         dtype=torch.uint8, device=DEV)
     res = lce.lce_flce_fwd_bwd(bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV), label_smoothing=eps,
-                               softcap=T, reduction=red, grad_out=g, chunk_tokens=chunk)
+                               softcap=T, reduction=red, grad_out=g, chunk_tokens=chunk, workspace=ws)
     torch.cuda.synchronize()
     return res
 
 
-def check_flce(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64):
-    res = run_flce(hb, wb, y, eps=eps, T=T, red=red, grad_out=grad_out, chunk=chunk)
+def check_flce(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64, group_chunks=None):
+    res = run_flce(hb, wb, y, eps=eps, T=T, red=red, grad_out=grad_out, chunk=chunk, group_chunks=group_chunks)
     o = oracle.flce(hb, wb, y, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out)
     n = y.size
     assert res.counts.cpu().tolist() == [int(o["counts"][0]), 0, int(o["counts"][2])]
@@ -106,6 +111,18 @@ def test_flce_shapes(n, H, V, chunk, eps, T, red):
     hb, wb, y = gen(n, H, V, seed=n * 7 + H)
     g = np.random.default_rng(1).normal(size=n) if red == "none" else [0.75]
     check_flce(hb, wb, y, eps=eps, T=T, red=red, grad_out=g, chunk=chunk)
+
+
+@pytest.mark.parametrize("group_chunks", [1, 2])
+def test_flce_grad_weight_groups(group_chunks):
+    """A smaller workspace splits grad_weight into several passes (the later ones accumulate into it);
+    the result matches the oracle and the one-pass result."""
+    hb, wb, y = gen(300, 520, 1000, seed=21)
+    _, o, _, _ = check_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64, group_chunks=group_chunks)
+    one_pass = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64)
+    grouped = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64, group_chunks=group_chunks)
+    assert rel_l2(grouped.grad_weight.cpu().numpy(), one_pass.grad_weight.cpu().numpy()) < 1e-5
+    assert torch.equal(grouped.grad_hidden, one_pass.grad_hidden)
 
 
 def test_flce_chunk_invariance():

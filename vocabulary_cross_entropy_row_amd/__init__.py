@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.lce_ce_argmax.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, p, p, p]
     L.lce_flce_workspace_bytes.restype = ctypes.c_size_t
     L.lce_flce_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.lce_flce_workspace_bytes_grouped.restype = ctypes.c_size_t
+    L.lce_flce_workspace_bytes_grouped.argtypes = [i64, i64, i64, i64, i64]
     L.lce_flce_fwd_bwd.restype = ctypes.c_int
     L.lce_flce_fwd_bwd.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, i64, p, p, p, p, p, p,
                                    ctypes.c_size_t, p]
@@ -160,6 +162,10 @@ def lce_ce_argmax(logits, labels=None, *, ignore_index: int = -100, argmax_out=N
 
 def lce_flce_workspace_bytes(n: int, H: int, V: int, chunk_tokens: int) -> int:
     return int(lib().lce_flce_workspace_bytes(int(n), int(H), int(V), int(chunk_tokens)))
+
+
+def lce_flce_workspace_bytes_grouped(n: int, H: int, V: int, chunk_tokens: int, group_chunks: int) -> int:
+    return int(lib().lce_flce_workspace_bytes_grouped(int(n), int(H), int(V), int(chunk_tokens), int(group_chunks)))
 
 
 @dataclass

@@ -308,8 +308,7 @@ bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, i
     return false;
 }
 
-namespace {
-int device_cus() {
+int device_cu_count() {
     static int cus[64] = {0};
     int d = 0;
     if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 256;
@@ -321,8 +320,10 @@ int device_cus() {
     return cus[d];
 }
 
+namespace {
+
 hipError_t launch_resident(const CEArgs &a, bool bf16, int kr, int kl, hipStream_t st) {
-    const int cus = device_cus();
+    const int cus = device_cu_count();
 #define LCE_CASE(r, l)                                                                            \
     if (kr == r && kl == l) return bf16 ? launch_rows_1_##r##_##l(a, cus, st) : launch_rows_0_##r##_##l(a, cus, st);
     LCE_FAMILIES(LCE_CASE)

@@ -9,7 +9,10 @@
 //   G_c  = CE(Z_c)           the resident row kernel, in place, with the mean
 //                            scale of all n tokens; per-token losses
 //   dH_c = G_c W             split-K MFMA GEMM into fp32 partials, folded to bf16
-//   dW  += G_c^T H_c         MFMA GEMM, fp32 read-modify-write (written on chunk 0)
+//   G_c^T, H_c^T             appended to the current group's transposed buffers
+// and once per group of chunks (as many as kFlceGroupBytes holds):
+//   dW (+)= G_g^T H_g        MFMA GEMM over the group's tokens, fp32 (written
+//                            by the first group, read-modify-written by later ones)
 // Every GEMM runs in the one "A K-contiguous, B K-contiguous" form, so W^T
 // (once per call), H_c^T and G_c^T are produced by a bandwidth-bound
 // transpose first.  Only one chunk of logits exists at a time.
@@ -127,6 +130,13 @@ hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, i
     return hipGetLastError();
 }
 
+template <int MODE>
+void launch_gemm(const GemmArgs &g, bool ktail, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u), block(gemm::NTHR);
+    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true>), grid, block, 0, st, g);
+    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false>), grid, block, 0, st, g);
+}
+
 // C (+)= A B^T over [M, N] with K split into `splits` ranges
 hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, int M,
                    int N, int K, int splits, int64_t c_split_stride, hipStream_t st) {
@@ -134,6 +144,9 @@ hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t 
     if ((K & 7) || (lda & 7) || (ldb & 7) || (reinterpret_cast<uintptr_t>(A) & 15) ||
         (reinterpret_cast<uintptr_t>(B) & 15))
         return hipErrorInvalidValue;
+    // 32-bit buffer offsets: a tile's rows plus one step of K read ahead
+    const int64_t ldmax = lda > ldb ? lda : ldb;
+    if (256 * ldmax * 2 + (static_cast<int64_t>(K) + 2 * gemm::BK) * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     GemmArgs g;
     g.A = static_cast<const uint16_t *>(A);
     g.B = static_cast<const uint16_t *>(B);
@@ -150,34 +163,60 @@ hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t 
     g.tiles_n = ceil_div(N, gemm::BN);
     const int64_t total = static_cast<int64_t>(g.tiles_m) * g.tiles_n * splits;
     g.tiles_per_xcd = ceil_div(total, 8);
-    const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u);
-    if (mode == gemm::OUT_BF16)
-        hipLaunchKernelGGL(gemm::gemm_nt_kernel<gemm::OUT_BF16>, grid, dim3(gemm::NTHR), 0, st, g);
-    else if (mode == gemm::OUT_F32)
-        hipLaunchKernelGGL(gemm::gemm_nt_kernel<gemm::OUT_F32>, grid, dim3(gemm::NTHR), 0, st, g);
-    else
-        hipLaunchKernelGGL(gemm::gemm_nt_kernel<gemm::OUT_F32_ACC>, grid, dim3(gemm::NTHR), 0, st, g);
+    const bool ktail = (K % gemm::BK) != 0;
+    if (mode == gemm::OUT_BF16) launch_gemm<gemm::OUT_BF16>(g, ktail, st);
+    else if (mode == gemm::OUT_F32) launch_gemm<gemm::OUT_F32>(g, ktail, st);
+    else launch_gemm<gemm::OUT_F32_ACC>(g, ktail, st);
     return hipGetLastError();
+}
+
+// K splits for a GEMM of `tiles` output tiles: the count (at most kFlceMaxSplitK,
+// each split at least 8 K steps) whose workgroups fill the most of whole rounds
+// over the compute units; ties go to fewer splits.
+int choose_splits(int64_t tiles, int64_t K) {
+    const int64_t cus = device_cu_count();
+    const int64_t steps = (K + gemm::BK - 1) / gemm::BK;
+    int best = 1;
+    double best_eff = 0.0;
+    for (int s = 1; s <= kFlceMaxSplitK && steps / s >= 8; ++s) {
+        const int64_t wg = tiles * s;
+        const double eff = static_cast<double>(wg) / static_cast<double>(((wg + cus - 1) / cus) * cus);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = s;
+        }
+    }
+    return best;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 int64_t round8(int64_t x) { return (x + 7) & ~static_cast<int64_t>(7); }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
-FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk) {
+int64_t flce_default_group_chunks(int64_t n, int64_t H, int64_t V, int64_t chunk) {
+    const int64_t C = chunk < n ? chunk : (n > 0 ? n : 1);
+    const int64_t nchunks = n > 0 ? (n + C - 1) / C : 1;
+    const int64_t per_chunk = round_up(C, 64) * (V + H) * 2;
+    const int64_t cpg = static_cast<int64_t>(kFlceGroupBytes) / per_chunk;
+    return cpg < 1 ? 1 : (cpg > nchunks ? nchunks : cpg);
+}
+
+FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t group_chunks) {
     FlceLayout L;
     const int64_t C = chunk < n ? chunk : (n > 0 ? n : 1);
     L.chunk = C;
-    L.splits = kFlceSplitK;
+    const int64_t nchunks = n > 0 ? (n + C - 1) / C : 1;
+    const int64_t cpg = group_chunks < 1 ? 1 : (group_chunks > nchunks ? nchunks : group_chunks);
+    L.group = cpg * C;
+    L.ldg = round_up(L.group, 64);
     size_t off = 0;
     L.off_wt = off;    off += align256(static_cast<size_t>(H) * V * 2);
     L.off_z = off;     off += align256(static_cast<size_t>(C) * V * 2);
-    // the transposed chunk operands use a row stride of C rounded up to 8
-    // elements (16-byte rows for the direct-to-LDS loads)
-    L.off_gt = off;    off += align256(static_cast<size_t>(V) * round8(C) * 2);
-    L.off_ht = off;    off += align256(static_cast<size_t>(H) * round8(C) * 2);
-    L.off_part = off;  off += align256(static_cast<size_t>(L.splits) * C * H * 4);
+    L.off_gt = off;    off += align256(static_cast<size_t>(V) * L.ldg * 2);
+    L.off_ht = off;    off += align256(static_cast<size_t>(H) * L.ldg * 2);
+    L.off_part = off;  off += align256(static_cast<size_t>(kFlceMaxSplitK) * C * H * 4);
     L.off_ce = off;    off += align256(ce_workspace_bytes(C));
     L.bytes = off;
     return L;
@@ -185,7 +224,7 @@ FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk) {
 
 hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     hipError_t e;
-    const FlceLayout L = flce_layout(f.n, f.H, f.V, f.chunk);
+    const FlceLayout L = flce_layout(f.n, f.H, f.V, f.chunk, f.group_chunks);
     char *ws = static_cast<char *>(f.workspace);
     uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
     uint16_t *z = reinterpret_cast<uint16_t *>(ws + L.off_z);
@@ -193,7 +232,7 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.off_ht);
     float *part = reinterpret_cast<float *>(ws + L.off_part);
     void *ce_ws = ws + L.off_ce;
-    const int64_t C = L.chunk, Cp = round8(C), H = f.H, V = f.V;
+    const int64_t C = L.chunk, H = f.H, V = f.V;
 
     // counts (and a zeroed completion counter for the chunk CE calls)
     if ((e = launch_ce_count(f.labels, f.n, V, f.ignore_index, f.counts, static_cast<unsigned *>(ce_ws), f.loss_out,
@@ -208,49 +247,59 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     if ((e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), st)) !=
         hipSuccess)
         return e;
+    const int tiles_dh = static_cast<int>(((C + gemm::BM - 1) / gemm::BM) * ((H + gemm::BN - 1) / gemm::BN));
+    const int splits = choose_splits(tiles_dh, V);
 
-    for (int64_t c0 = 0; c0 < f.n; c0 += C) {
-        const int cn = static_cast<int>(f.n - c0 < C ? f.n - c0 : C);
-        const int cnp = static_cast<int>(round8(cn));   // K of the dW GEMM: zero-padded to whole chunks
-        const uint16_t *hc = static_cast<const uint16_t *>(f.hidden) + c0 * H;
-        // H_c^T [H, cnp] (row stride Cp)
-        if ((e = transpose(hc, H, ht, Cp, cn, cnp, static_cast<int>(H), st)) != hipSuccess) return e;
-        // Z_c = H_c W^T  -> bf16 [cn, V]
-        if ((e = gemm_nt(gemm::OUT_BF16, hc, H, f.weight, H, z, V, cn, static_cast<int>(V), static_cast<int>(H), 1, 0,
-                         st)) != hipSuccess)
-            return e;
-        // G_c = CE(Z_c) in place, mean scale over all n tokens
-        CEArgs a;
-        a.logits = z;
-        a.ld = V;
-        a.n = cn;
-        a.V = V;
-        a.labels = f.labels + c0;
-        a.count_labels = f.labels;
-        a.count_n = f.n;
-        a.ignore_index = f.ignore_index;
-        a.eps = f.eps;
-        a.softcap = f.softcap;
-        a.reduction = f.reduction;
-        a.grad_out = (f.reduction == 0 && f.grad_out) ? f.grad_out + c0 : f.grad_out;
-        a.loss_tok = f.loss_tok + c0;
-        a.loss_out = nullptr;
-        a.argmax_out = nullptr;
-        a.counts = f.counts;
-        a.workspace = ce_ws;
-        if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
-        // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
-        if ((e = gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H), static_cast<int>(V), L.splits,
-                         C * H, st)) != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(splitk_fold_kernel, dim3(1024), dim3(256), 0, st, part, C * H, L.splits,
-                           static_cast<uint16_t *>(f.grad_hidden) + c0 * H, H, cn, static_cast<int>(H));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        // G_c^T [V, cnp] (row stride Cp)
-        if ((e = transpose(z, V, gt, Cp, cn, cnp, static_cast<int>(V), st)) != hipSuccess) return e;
-        // dW (+)= G_c^T H_c
-        if ((e = gemm_nt(c0 == 0 ? gemm::OUT_F32 : gemm::OUT_F32_ACC, gt, Cp, ht, Cp, f.grad_weight, H,
-                         static_cast<int>(V), static_cast<int>(H), cnp, 1, 0, st)) != hipSuccess)
+    for (int64_t g0 = 0; g0 < f.n; g0 += L.group) {
+        const int64_t gn = f.n - g0 < L.group ? f.n - g0 : L.group;
+        for (int64_t c0 = g0; c0 < g0 + gn; c0 += C) {
+            const int cn = static_cast<int>(g0 + gn - c0 < C ? g0 + gn - c0 : C);
+            const bool last_in_group = c0 + cn >= g0 + gn;
+            // the group's K ends on a whole 8-element chunk: pad the last chunk with zeros
+            const int cpad = static_cast<int>(last_in_group ? round8(c0 + cn - g0) - (c0 - g0) : cn);
+            const uint16_t *hc = static_cast<const uint16_t *>(f.hidden) + c0 * H;
+            // H_c^T into columns [c0 - g0, ...) of the group's [H, ldg] buffer
+            if ((e = transpose(hc, H, ht + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(H), st)) != hipSuccess)
+                return e;
+            // Z_c = H_c W^T  -> bf16 [cn, V]
+            if ((e = gemm_nt(gemm::OUT_BF16, hc, H, f.weight, H, z, V, cn, static_cast<int>(V), static_cast<int>(H),
+                             1, 0, st)) != hipSuccess)
+                return e;
+            // G_c = CE(Z_c) in place, mean scale over all n tokens
+            CEArgs a;
+            a.logits = z;
+            a.ld = V;
+            a.n = cn;
+            a.V = V;
+            a.labels = f.labels + c0;
+            a.count_labels = f.labels;
+            a.count_n = f.n;
+            a.ignore_index = f.ignore_index;
+            a.eps = f.eps;
+            a.softcap = f.softcap;
+            a.reduction = f.reduction;
+            a.grad_out = (f.reduction == 0 && f.grad_out) ? f.grad_out + c0 : f.grad_out;
+            a.loss_tok = f.loss_tok + c0;
+            a.loss_out = nullptr;
+            a.argmax_out = nullptr;
+            a.counts = f.counts;
+            a.workspace = ce_ws;
+            if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
+            // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
+            if ((e = gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H), static_cast<int>(V), splits,
+                             C * H, st)) != hipSuccess)
+                return e;
+            hipLaunchKernelGGL(splitk_fold_kernel, dim3(1024), dim3(256), 0, st, part, C * H, splits,
+                               static_cast<uint16_t *>(f.grad_hidden) + c0 * H, H, cn, static_cast<int>(H));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            // G_c^T into columns [c0 - g0, ...) of the group's [V, ldg] buffer
+            if ((e = transpose(z, V, gt + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(V), st)) != hipSuccess)
+                return e;
+        }
+        // dW (+)= G_g^T H_g over the group's tokens (K padded to a whole 8-element chunk)
+        if ((e = gemm_nt(g0 == 0 ? gemm::OUT_F32 : gemm::OUT_F32_ACC, gt, L.ldg, ht, L.ldg, f.grad_weight, H,
+                         static_cast<int>(V), static_cast<int>(H), static_cast<int>(round8(gn)), 1, 0, st)) !=
+            hipSuccess)
             return e;
     }
     if (f.loss_out) {

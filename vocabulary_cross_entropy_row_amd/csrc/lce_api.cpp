@@ -130,7 +130,12 @@ lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const 
 
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens) {
     if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1) return 0;
-    return lce::flce_layout(n, H, V, chunk_tokens).bytes;
+    return lce::flce_layout(n, H, V, chunk_tokens, lce::flce_default_group_chunks(n, H, V, chunk_tokens)).bytes;
+}
+
+size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens, int64_t group_chunks) {
+    if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1 || group_chunks < 1) return 0;
+    return lce::flce_layout(n, H, V, chunk_tokens, group_chunks).bytes;
 }
 
 lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
@@ -153,9 +158,12 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
         return fail(LCE_ERR_INVALID_ARG, "%s: weight, grad_weight, counts and workspace are required", fn);
     if (n > 0 && (!hidden || !labels || !loss_tok || !grad_hidden))
         return fail(LCE_ERR_INVALID_ARG, "%s: hidden, labels, loss_tok and grad_hidden are required", fn);
-    const size_t need = lce_flce_workspace_bytes(n, H, V, chunk_tokens);
+    // the largest grad_weight group (up to the default) whose layout fits the workspace
+    int64_t group = lce::flce_default_group_chunks(n, H, V, chunk_tokens);
+    while (group > 1 && lce::flce_layout(n, H, V, chunk_tokens, group).bytes > workspace_bytes) --group;
+    const size_t need = lce::flce_layout(n, H, V, chunk_tokens, group).bytes;
     if (workspace_bytes < need)
-        return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < required %zu", fn, workspace_bytes, need);
+        return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < minimum %zu", fn, workspace_bytes, need);
     if (!is_aligned(workspace, 256)) return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     if (H % 8 != 0 || V % 8 != 0)
         return fail(LCE_ERR_UNSUPPORTED, "%s: requires H and V to be multiples of 8 (16-byte bf16 rows); got H=%lld V=%lld",
@@ -187,6 +195,7 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
     f.grad_weight = grad_weight;
     f.counts = counts;
     f.workspace = workspace;
+    f.group_chunks = group;
     return hip_status(lce::launch_flce(f, stream), "lce_flce_fwd_bwd launch");
 }
 

@@ -61,8 +61,17 @@ hipError_t launch_ce_count(const int64_t *labels, int64_t n, int64_t V, int64_t 
 
 // ---- fused linear cross-entropy ----------------------------------------------
 
-// K splits of the grad_hidden GEMM (K = V is long and M x N = chunk x H is small).
-constexpr int kFlceSplitK = 8;
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// Most K splits of the grad_hidden GEMM (K = V is long and M x N = chunk x H is
+// small); the count used fills whole rounds of the device's compute units.
+constexpr int kFlceMaxSplitK = 16;
+// Bytes of transposed chunk gradients and hidden states kept for one
+// grad_weight GEMM: the chunks of a group are contracted in one pass, so
+// grad_weight is written once per group instead of read-modify-written once
+// per chunk.
+constexpr size_t kFlceGroupBytes = size_t(2) << 30;
 
 struct FlceArgs {
     const void *hidden;      // bf16 [n, H]
@@ -79,15 +88,19 @@ struct FlceArgs {
     float *grad_weight;      // fp32 [V, H], overwritten
     int64_t *counts;         // [3]
     void *workspace;
+    int64_t group_chunks;    // chunks per grad_weight group (the workspace was sized for it)
 };
 
 // Offsets (bytes) of the fused-linear workspace regions.
 struct FlceLayout {
-    int64_t chunk;
-    int splits;
+    int64_t chunk;        // tokens per logits chunk
+    int64_t group;        // tokens per grad_weight group (a multiple of chunk)
+    int64_t ldg;          // row stride of the transposed group buffers (multiple of 8)
     size_t off_wt, off_z, off_gt, off_ht, off_part, off_ce, bytes;
 };
-FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk);
+FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t group_chunks);
+// Chunks per grad_weight group that kFlceGroupBytes holds (at least 1, at most all chunks).
+int64_t flce_default_group_chunks(int64_t n, int64_t H, int64_t V, int64_t chunk);
 hipError_t launch_flce(const FlceArgs &f, hipStream_t stream);
 
 }  // namespace lce
