@@ -336,8 +336,7 @@ def collect_profiles_flce(workload: str) -> int:
         rows = list(csv.DictReader(open(os.path.join(raw, sub, "run_counter_collection.csv"))))
         rows = [r for r in rows if r["Counter_Name"] == cname]
         k = [float(r["Counter_Value"]) for r in rows if any(o in r["Kernel_Name"] for o in ours)]
-        c = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
-             and int(r["Grid_Size"]) >= (1 << 20)]
+        c = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         # per call: the run makes 2 calls (1 warmup + 1 step); the reference copy is the largest copy
         return sum(k) / 2.0, max(c), len(k)
 

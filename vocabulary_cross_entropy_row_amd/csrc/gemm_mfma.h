@@ -78,15 +78,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
     // XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs;
-    // each XCD walks a contiguous range of the logical tile order (m fastest,
-    // then n, then the K split), so tiles that share a B tile run together on
-    // one L2.
+    // each XCD walks a contiguous range of the logical tile order: the shorter
+    // of the two tile dimensions fastest, then the longer, then the K split.
+    // Consecutive tiles then share their tile of the larger operand, which is
+    // fetched once into that XCD's L2 while the smaller operand is re-read.
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int t = xcd * g.tiles_per_xcd + slot;
     const int total = g.tiles_m * g.tiles_n * g.splits;
     if (slot >= g.tiles_per_xcd || t >= total) return;
-    const int tm = t % g.tiles_m;
-    const int tn = (t / g.tiles_m) % g.tiles_n;
+    const int mn = t % (g.tiles_m * g.tiles_n);
+    const bool m_fast = g.tiles_m <= g.tiles_n;
+    const int tm = m_fast ? mn % g.tiles_m : mn / g.tiles_n;
+    const int tn = m_fast ? mn / g.tiles_m : mn % g.tiles_n;
     const int ks = t / (g.tiles_m * g.tiles_n);
     const int m0 = tm * BM, n0 = tn * BN;
     const int ksteps_total = (g.K + BK - 1) / BK;
