@@ -179,16 +179,21 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *shv, int *
 }
 
 // Valid-label and bad-label counts over the count labels, by one workgroup.
-__device__ __forceinline__ void block_count_labels(const CEArgs &a, long long (*sh)[NWAVE], long long &nv,
-                                                   long long &nb) {
+// n_valid / n_bad over count_labels[0, count_n).  y0 and y1 are this thread's
+// labels at indexes tid and tid + NT (ignore_index past count_n), loaded by the
+// caller ahead of its other memory traffic; the rest are loaded here.
+__device__ __forceinline__ void block_count_labels(const CEArgs &a, long long (*sh)[NWAVE], int64_t y0, int64_t y1,
+                                                   long long &nv, long long &nb) {
     long long v = 0, b = 0;
-    for (int64_t i = threadIdx.x; i < a.count_n; i += NT) {
-        const int64_t y = a.count_labels[i];
+    auto count = [&](int64_t y) {
         if (y != a.ignore_index) {
             if (y >= 0 && y < a.V) ++v;
             else ++b;
         }
-    }
+    };
+    count(y0);
+    count(y1);
+    for (int64_t i = threadIdx.x + 2 * NT; i < a.count_n; i += NT) count(a.count_labels[i]);
     v = wave_sum_ll(v);
     b = wave_sum_ll(b);
     if ((threadIdx.x & 63) == 0) {

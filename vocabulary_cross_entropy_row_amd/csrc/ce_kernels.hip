@@ -286,7 +286,7 @@ hipError_t launch_generic(const CEArgs &a, hipStream_t st) {
 }  // namespace
 
 // Resident-path families compiled from ce_rows_inst.hip: (register rounds, LDS rounds).
-#define LCE_FAMILIES(X) X(1, 0) X(2, 0) X(4, 0) X(8, 0) X(12, 0) X(16, 0) X(16, 3) X(16, 6) X(16, 9)
+#define LCE_FAMILIES(X) X(1, 0) X(2, 0) X(4, 0) X(8, 0) X(4, 8) X(8, 8) X(10, 9) X(13, 9) X(16, 9)
 #define LCE_DECL(kr, kl)                                                         \
     hipError_t launch_rows_0_##kr##_##kl(const CEArgs &, int, hipStream_t);     \
     hipError_t launch_rows_1_##kr##_##kl(const CEArgs &, int, hipStream_t);
@@ -298,7 +298,7 @@ bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, i
     if (V % E != 0 || ld % E != 0) return false;
     if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0) return false;
     const int64_t need = (V / E + NT - 1) / NT;   // rounds of 1024 vectors
-    static const int fam[][2] = {{1, 0}, {2, 0}, {4, 0}, {8, 0}, {12, 0}, {16, 0}, {16, 3}, {16, 6}, {16, 9}};
+    static const int fam[][2] = {{1, 0}, {2, 0}, {4, 0}, {8, 0}, {4, 8}, {8, 8}, {10, 9}, {13, 9}, {16, 9}};
     for (const auto &f : fam)
         if (f[0] + f[1] >= need) {
             *kr = f[0];

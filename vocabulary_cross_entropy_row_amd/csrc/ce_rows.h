@@ -12,17 +12,18 @@
 // Layout of the work: one 1024-thread workgroup per CU walks rows
 // blockIdx.x, blockIdx.x + G, ...  A row is split into K rounds of 1024
 // 16-byte vectors; thread t owns vector (k * 1024 + t) of every round.  The
-// first KR rounds live in VGPRs, the next KL rounds in thread-private LDS
-// slots filled by direct buffer->LDS loads, so the row is read from HBM once.
-// Two passes run over the resident row:
+// first KL rounds live in thread-private LDS slots filled by direct
+// buffer->LDS loads, the remaining KR rounds in VGPRs, so the row is read
+// from HBM once.  Two passes run over the resident row:
 //   pass A, round by round as the data arrives: an online softmax (each
 //           thread keeps a running max m and the sum of exp(z - m) over its
 //           elements, rescaled when m grows), the argmax and sum z when asked;
 //   pass B, once the row's statistics are combined: the gradient.
-// As soon as pass B has stored the gradient, the loads of the workgroup's
-// next row go out into the same registers / LDS slots, and pass A of that row
-// starts on round 0 while later rounds are still on their way, so the HBM
-// traffic of one row overlaps the arithmetic of the next.
+// Pass B handles the LDS rounds first; once they are stored, the LDS rounds of
+// the workgroup's next row are requested, and they stream in while pass B
+// finishes the register rounds.  Then the register rounds of the next row go
+// out, and pass A of that row starts on its (by then resident) LDS rounds.
+// So the HBM traffic of one row overlaps the arithmetic of the previous one.
 //
 // The workgroups count the labels themselves (the mean scale needs n_valid
 // before any gradient is written), keep per-workgroup loss / n_correct
@@ -86,11 +87,6 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     const clabels_t lab = (clabels_t)a.labels;
     const cfloat_t gout = (cfloat_t)a.grad_out;
 
-    long long n_valid, n_bad;
-    block_count_labels(a, sh_c, n_valid, n_bad);
-    const float g_all = (a.reduction != 0 && gout) ? gout[0] : 1.0f;
-    const float red_scale =
-        a.reduction == 1 ? (n_valid > 0 ? g_all / static_cast<float>(n_valid) : 0.0f) : g_all;
 
     auto valid_label = [&](int64_t y) { return y != a.ignore_index && y >= 0 && y < a.V; };
     // the next row >= r of this workgroup's sequence that takes the full path:
@@ -116,29 +112,69 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     };
     const int voff = tid * 16;
 
+    // rounds [0, KL) in LDS, [KL, K) in registers
     u32x4 v[KRV];
     auto issue_round = [&](int k, __amdgpu_buffer_rsrc_t src) {
-        if (k < KR) {
-            v[k < KR ? k : 0] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, k * NT * 16, kNonTemporal);
+        if (k >= KL) {
+            v[k >= KL ? k - KL : 0] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, k * NT * 16, kNonTemporal);
         } else {
             // 16 bytes per lane, written to LDS at (wave-uniform base) + lane * 16
             typedef __attribute__((address_space(3))) void *lptr;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lptr)(&lds_rows[(k - KR) * NT + wave_base]), 16, voff,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lptr)(&lds_rows[k * NT + wave_base]), 16, voff,
                                                      k * NT * 16, 0, kNonTemporal);
         }
     };
+    // stores of a partial last round need no guard: lanes past the row are
+    // outside the descriptor and dropped.  Every wave therefore issues the
+    // same memory operations, which the LDS waits below count on.
     auto store_round = [&](int k, __amdgpu_buffer_rsrc_t dst, u32x4 val) {
         __builtin_amdgcn_raw_buffer_store_b128(val, dst, voff, k * NT * 16, kNonTemporal);
     };
     // a round of the resident row as a 16-byte vector
-    auto round_vec = [&](int k) -> u32x4 { return k < KR ? v[k < KR ? k : 0] : lds_rows[(k - KR) * NT + tid]; };
+    auto round_vec = [&](int k) -> u32x4 { return k >= KL ? v[k >= KL ? k - KL : 0] : lds_rows[k * NT + tid]; };
 
+    // zero gradient and loss for the ignored rows r0, r0 + G, ... before r1 (the
+    // rows next_row stepped over): stores only, issued where they are met so
+    // they overlap the other rows' traffic
+    auto zero_rows = [&](int64_t r0, int64_t r1) {
+        if constexpr (!ARGMAX) {
+            for (int64_t r = r0; r < r1; r += G) {
+                const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
+#pragma unroll
+                for (int k = 0; k < K; ++k) store_round(k, rz, zero4);
+                if (tid == 0) a.loss_tok[r] = 0.0f;
+            }
+        }
+    };
+
+    // The mean scale needs every label counted before any gradient is written.
+    // The first labels are requested ahead of the first row, so counting them
+    // does not wait behind the row's loads.
+    const int64_t yc0 = tid < a.count_n ? a.count_labels[tid] : a.ignore_index;
+    const int64_t yc1 = tid + NT < a.count_n ? a.count_labels[tid + NT] : a.ignore_index;
+    __builtin_amdgcn_sched_barrier(0);
     int64_t row = next_row(blockIdx.x);
     {
         const __amdgpu_buffer_rsrc_t src = row_rsrc(row, row < n);
 #pragma unroll
-        for (int k = 0; k < K; ++k) issue_round(k, src);
+        for (int k = 0; k < K; ++k) {
+            issue_round(k, src);
+            __builtin_amdgcn_sched_barrier(0);   // issue in the order pass A consumes
+        }
+        // KR stores through an empty descriptor (dropped without touching memory):
+        // every row's LDS rounds then have the same 2 KR memory operations issued
+        // behind them, the first row's included, so one wait serves all rows
+        const __amdgpu_buffer_rsrc_t none = row_rsrc(0, false);
+#pragma unroll
+        for (int k = KL; k < K; ++k) store_round(k, none, zero4);
     }
+    zero_rows(blockIdx.x, row < n ? row : n);
+
+    long long n_valid, n_bad;
+    block_count_labels(a, sh_c, yc0, yc1, n_valid, n_bad);
+    const float g_all = (a.reduction != 0 && gout) ? gout[0] : 1.0f;
+    const float red_scale =
+        a.reduction == 1 ? (n_valid > 0 ? g_all / static_cast<float>(n_valid) : 0.0f) : g_all;
 
     double loss_acc = 0.0;
     long long correct = 0;
@@ -167,11 +203,17 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         float zs = 0.0f;         // sum of z (label smoothing)
         float amv = -INFINITY;   // argmax: value and first index over the raw logits
         int am = 0x7fffffff;
+        if constexpr (KL > 0) {
+            // this wave's LDS rounds have landed once at most the 2 KR memory
+            // operations issued after them (KR register-round stores, then the KR
+            // register loads) are outstanding; ignored rows' stores come later still
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KR) : "memory");
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (k == KR && KL > 0) wait_vmem_all();   // LDS rounds have landed
             const int idx = k * NT + tid;
-            if (idx < nvec) {
+            // whole rounds need no per-lane test (uniform check first)
+            if ((k + 1) * NT <= nvec || idx < nvec) {
                 const u32x4 vk = round_vec(k);
                 float x[E], z[E];
 #pragma unroll
@@ -308,82 +350,83 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         float gy = scale * (eps - s / S - (SMOOTH ? eps * invV : 0.0f));   // s_i (p_y - (1 - eps) - eps/V)
         if constexpr (SOFTCAP) gy *= Cap::chain_of_r(cap.r_of(xy));
         opaque_regs(v);
+        auto grad_round = [&](int k) {
+            const u32x4 vk = round_vec(k);
+            float g[E];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int idx = k * NT + tid;
-            if (idx < nvec) {
-                const u32x4 vk = round_vec(k);
-                float g[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float x = EL::get(vk, e);
-                    if constexpr (SOFTCAP) {
-                        const float r = cap.r_of(x);
-                        const float p = exp2_fast(fmaf(r, capk, capb2));        // |s_i| p_j
-                        g[e] = (SMOOTH ? p - epsV : p) * Cap::chain_of_r(r);
-                    } else {
-                        const float p = exp2_fast(fmaf(x, kLog2e, -lseL));      // |s_i| p_j
-                        g[e] = SMOOTH ? p - epsV : p;
-                    }
+            for (int e = 0; e < E; ++e) {
+                const float x = EL::get(vk, e);
+                if constexpr (SOFTCAP) {
+                    const float r = cap.r_of(x);
+                    const float p = exp2_fast(fmaf(r, capk, capb2));        // |s_i| p_j
+                    g[e] = (SMOOTH ? p - epsV : p) * Cap::chain_of_r(r);
+                } else {
+                    const float p = exp2_fast(fmaf(x, kLog2e, -lseL));      // |s_i| p_j
+                    g[e] = SMOOTH ? p - epsV : p;
                 }
-                if (negate) {
-                    asm volatile("");
-#pragma unroll
-                    for (int e = 0; e < E; ++e) g[e] = -g[e];
-                }
-                if (k == ky) {
-                    asm volatile("");
-                    if (owner) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e)
-                            if (e == ey) g[e] = gy;
-                    }
-                }
-                store_round(k, rp, EL::pack(g));
             }
+            if (negate) {
+                asm volatile("");
+#pragma unroll
+                for (int e = 0; e < E; ++e) g[e] = -g[e];
+            }
+            if (k == ky) {
+                asm volatile("");
+                if (owner) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (e == ey) g[e] = gy;
+                }
+            }
+            store_round(k, rp, EL::pack(g));
             // keep the rounds in order: hoisted loads or conversions of later
             // rounds would hold extra row data in registers
             __builtin_amdgcn_sched_barrier(0);
-        }
-        // the next row is requested once this row's stores are all out: HBM
-        // turns between reads and writes less often than with per-round
-        // interleaving, and pass A of the next row consumes round 0 first
+        };
+        // the LDS rounds, then the next row's LDS rounds go out (this wave read
+        // its slots before computing the stores above, and no other wave uses them)
 #pragma unroll
-        for (int k = 0; k < K; ++k) issue_round(k, rn);
+        for (int k = 0; k < KL; ++k) grad_round(k);
+#pragma unroll
+        for (int k = 0; k < KL; ++k) {
+            issue_round(k, rn);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the register rounds, then the next row's register rounds
+#pragma unroll
+        for (int k = KL; k < K; ++k) grad_round(k);
+#pragma unroll
+        for (int k = KL; k < K; ++k) {
+            issue_round(k, rn);   // in the order pass A consumes them
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ignored rows between this row and the next valid one
+        zero_rows(row + G, nxt < n ? nxt : n);
     }
 
-    // ---- ignored tokens (when no argmax is wanted): zero gradient, no read
-    if constexpr (!ARGMAX) {
-        const __amdgpu_buffer_rsrc_t none = row_rsrc(0, false);
-        (void)none;
-        for (int64_t r = blockIdx.x; r < n; r += G) {
-            if (valid_label(lab[r])) continue;
-            const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
-#pragma unroll
-            for (int k = 0; k < K; ++k) store_round(k, rz, zero4);
-            if (tid == 0) a.loss_tok[r] = 0.0f;
-        }
-    }
-
-    // ---- publish this workgroup's partials; the last workgroup folds them
+    // ---- publish this workgroup's partials; the last workgroup folds them.
+    // The partials are written through to memory (system-scope stores) and
+    // acknowledged before the ticket is taken, and the last workgroup reads
+    // them past its own L2: no cache-wide writeback or invalidate is needed.
     if (tid == 0) {
-        ws_loss(a.workspace)[blockIdx.x] = loss_acc;
-        ws_correct(a.workspace, G)[blockIdx.x] = correct;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(reinterpret_cast<unsigned long long *>(ws_loss(a.workspace)) + blockIdx.x,
+                           __builtin_bit_cast(unsigned long long, loss_acc), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(ws_correct(a.workspace, G) + blockIdx.x, correct, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const unsigned t = __hip_atomic_fetch_add(ws_ticket(a.workspace), 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        const int last = t == static_cast<unsigned>(G) - 1u;
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        sh_flag = last;
+                                                  __HIP_MEMORY_SCOPE_SYSTEM);
+        sh_flag = t == static_cast<unsigned>(G) - 1u;
     }
     __syncthreads();
     if (!sh_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     double acc = 0.0;
     long long cor = 0;
     for (int w = tid; w < G; w += NT) {
-        acc += ws_loss(a.workspace)[w];
-        cor += ws_correct(a.workspace, G)[w];
+        acc += __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<unsigned long long *>(ws_loss(a.workspace)) + w,
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+        cor += __hip_atomic_load(ws_correct(a.workspace, G) + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     acc = wave_sum_d(acc);
     cor = wave_sum_ll(cor);
