@@ -52,6 +52,7 @@ template <bool BF16> struct Elt;
 template <> struct Elt<true> {
     static constexpr int E = 8;       // bf16 per 16-byte vector
     static constexpr int bytes = 2;
+    static constexpr uint32_t sign_mask = 0x80008000u;   // the sign bits of a packed word
     __device__ __forceinline__ static uint32_t word(const u32x4 &v, int w) {
         return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
     }
@@ -76,11 +77,18 @@ template <> struct Elt<true> {
     __device__ __forceinline__ static void store_one(void *base, int64_t idx, float g) {
         static_cast<__bf16 *>(base)[idx] = static_cast<__bf16>(g);   // RNE
     }
+    // one element through a buffer descriptor, at element index idx (AUX: cache policy)
+    template <int AUX>
+    __device__ __forceinline__ static void store_one(__amdgpu_buffer_rsrc_t r, int idx, float g) {
+        const __bf16 b = static_cast<__bf16>(g);   // RNE
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, b), r, idx * 2, 0, AUX);
+    }
 };
 
 template <> struct Elt<false> {
     static constexpr int E = 4;       // fp32 per 16-byte vector
     static constexpr int bytes = 4;
+    static constexpr uint32_t sign_mask = 0x80000000u;
     __device__ __forceinline__ static float get(const u32x4 &v, int e) {
         return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
     }
@@ -93,6 +101,10 @@ template <> struct Elt<false> {
     }
     __device__ __forceinline__ static void store_one(void *base, int64_t idx, float g) {
         static_cast<float *>(base)[idx] = g;
+    }
+    template <int AUX>
+    __device__ __forceinline__ static void store_one(__amdgpu_buffer_rsrc_t r, int idx, float g) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), r, idx * 4, 0, AUX);
     }
 };
 
@@ -179,11 +191,14 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *shv, int *
 }
 
 // Valid-label and bad-label counts over the count labels, by one workgroup.
-// n_valid / n_bad over count_labels[0, count_n).  y0 and y1 are this thread's
-// labels at indexes tid and tid + NT (ignore_index past count_n), loaded by the
-// caller ahead of its other memory traffic; the rest are loaded here.
-__device__ __forceinline__ void block_count_labels(const CEArgs &a, long long (*sh)[NWAVE], int64_t y0, int64_t y1,
-                                                   long long &nv, long long &nb) {
+// Label counting for the mean's denominator, in two halves around a barrier
+// of the caller's.  publish: this thread's share of
+// count_labels[0, count_n) -- y0 and y1 are its labels at indexes tid and
+// tid + NT (ignore_index past count_n), loaded by the caller ahead of its
+// other memory traffic, the rest are loaded here -- summed per wave into
+// sh[0][wave] (valid) and sh[1][wave] (bad).  read: the totals, once a barrier
+// has passed since every wave published.
+__device__ __forceinline__ void count_labels_publish(const CEArgs &a, long long (*sh)[NWAVE], int64_t y0, int64_t y1) {
     long long v = 0, b = 0;
     auto count = [&](int64_t y) {
         if (y != a.ignore_index) {
@@ -200,7 +215,8 @@ __device__ __forceinline__ void block_count_labels(const CEArgs &a, long long (*
         sh[0][threadIdx.x >> 6] = v;
         sh[1][threadIdx.x >> 6] = b;
     }
-    __syncthreads();
+}
+__device__ __forceinline__ void count_labels_read(long long (*sh)[NWAVE], long long &nv, long long &nb) {
     nv = 0;
     nb = 0;
 #pragma unroll

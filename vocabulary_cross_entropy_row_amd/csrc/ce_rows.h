@@ -65,7 +65,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // r+1's, never two
     __shared__ float sh_m[2][NWAVE], sh_s[2][NWAVE], sh_z[2][NWAVE], sh_zs[2][NWAVE];
     __shared__ int sh_i[2][NWAVE];
-    __shared__ long long sh_c[2][NWAVE];
+    __shared__ long long sh_c[2][NWAVE];   // label count partials (valid, bad) per wave
+    __shared__ long long sh_k[NWAVE];      // n_correct partials of the final fold
     __shared__ double sh_d[NWAVE];
     __shared__ float sh_xy[2];
     __shared__ int sh_flag;
@@ -170,11 +171,17 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     }
     zero_rows(blockIdx.x, row < n ? row : n);
 
-    long long n_valid, n_bad;
-    block_count_labels(a, sh_c, yc0, yc1, n_valid, n_bad);
+    count_labels_publish(a, sh_c, yc0, yc1);
+    __syncthreads();
     const float g_all = (a.reduction != 0 && gout) ? gout[0] : 1.0f;
-    const float red_scale =
-        a.reduction == 1 ? (n_valid > 0 ? g_all / static_cast<float>(n_valid) : 0.0f) : g_all;
+    float red_scale = g_all;
+    {
+        // only the float scale stays live through the row loop; the fold at the
+        // end reads the counts again
+        long long nv0, nb0;
+        count_labels_read(sh_c, nv0, nb0);
+        if (a.reduction == 1) red_scale = nv0 > 0 ? g_all / static_cast<float>(nv0) : 0.0f;
+    }
 
     double loss_acc = 0.0;
     long long correct = 0;
@@ -370,14 +377,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) g[e] = -g[e];
             }
-            if (k == ky) {
-                asm volatile("");
-                if (owner) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if (e == ey) g[e] = gy;
-                }
-            }
+            // the packed result goes straight to the store: a VALU operation on
+            // the output of v_cvt_pk_bf16_f32 has been seen to read stale data
             store_round(k, rp, EL::pack(g));
             // keep the rounds in order: hoisted loads or conversions of later
             // rounds would hold extra row data in registers
@@ -400,6 +401,9 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             issue_round(k, rn);   // in the order pass A consumes them
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the target element's own gradient replaces what its round stored
+        // (one thread, after that round's store, to the same address)
+        if (owner) EL::template store_one<kNonTemporal>(rp, y, gy);
         // ignored rows between this row and the next valid one
         zero_rows(row + G, nxt < n ? nxt : n);
     }
@@ -421,6 +425,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     }
     __syncthreads();
     if (!sh_flag) return;
+    long long n_valid, n_bad;
+    count_labels_read(sh_c, n_valid, n_bad);
     double acc = 0.0;
     long long cor = 0;
     for (int w = tid; w < G; w += NT) {
@@ -432,7 +438,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     cor = wave_sum_ll(cor);
     if ((tid & 63) == 0) {
         sh_d[tid >> 6] = acc;
-        sh_c[0][tid >> 6] = cor;
+        sh_k[tid >> 6] = cor;
     }
     __syncthreads();
     if (tid == 0) {
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         long long c = 0;
         for (int w = 0; w < NWAVE; ++w) {
             tot += sh_d[w];
-            c += sh_c[0][w];
+            c += sh_k[w];
         }
         if (a.loss_out) {
             float out = 0.0f;
