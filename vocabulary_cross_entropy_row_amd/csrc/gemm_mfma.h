@@ -78,18 +78,22 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
     // XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs;
-    // each XCD walks a contiguous range of the logical tile order: the shorter
-    // of the two tile dimensions fastest, then the longer, then the K split.
-    // Consecutive tiles then share their tile of the larger operand, which is
-    // fetched once into that XCD's L2 while the smaller operand is re-read.
+    // each XCD walks a contiguous range of the logical tile order.  That order
+    // takes row tiles in groups of GROUP_M and, within a group, walks the
+    // column tiles with the group's row tiles fastest (then the K split), so
+    // the ~32 tiles an XCD runs at once form a GROUP_M x 8 block sharing
+    // GROUP_M + 8 operand panels in its L2.
+    constexpr int GROUP_M = 4;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int t = xcd * g.tiles_per_xcd + slot;
     const int total = g.tiles_m * g.tiles_n * g.splits;
     if (slot >= g.tiles_per_xcd || t >= total) return;
     const int mn = t % (g.tiles_m * g.tiles_n);
-    const bool m_fast = g.tiles_m <= g.tiles_n;
-    const int tm = m_fast ? mn % g.tiles_m : mn / g.tiles_n;
-    const int tn = m_fast ? mn / g.tiles_m : mn % g.tiles_n;
+    const int first_m = (mn / (GROUP_M * g.tiles_n)) * GROUP_M;
+    const int gm = min(GROUP_M, g.tiles_m - first_m);
+    const int within = mn - first_m * g.tiles_n;
+    const int tm = first_m + within % gm;
+    const int tn = within / gm;
     const int ks = t / (g.tiles_m * g.tiles_n);
     const int m0 = tm * BM, n0 = tn * BN;
     const int ksteps_total = (g.K + BK - 1) / BK;
