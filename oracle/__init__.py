@@ -178,6 +178,58 @@ class Oracle:
                 "counts": counts}
 
 
+def flce_sampled(orc: "Oracle", hidden: np.ndarray, weight: np.ndarray, labels: np.ndarray, tokens, vocab_rows, *,
+                 ignore_index: int = -100, label_smoothing: float = 0.0, softcap: float = 0.0,
+                 reduction: str = "mean", grad_out: float = 1.0, block: int = 256, nthreads: int = 0) -> dict:
+    """Fused linear cross-entropy at sizes where the plain-loop definition is too slow (Liger-Kernel PR
+    "Add Liger Kernel support for Muse Glimmer", Summary / Memory): the logits Z = H W^T of every token in
+    fp64 by a library matmul (bf16 inputs are exact in fp64), the per-token loss and gradient G by the
+    oracle's own row routine on those fp64 logits, then dH = G W for the sampled tokens and dW = G^T H for
+    the sampled vocabulary rows, both in fp64.  The mean is over every valid label (reduction 'mean' or
+    'sum'; grad_out is the scalar upstream gradient).
+
+    Returns loss_tok [n], loss_out, counts, grad_hidden [len(tokens), H], grad_weight [len(vocab_rows), H]
+    and zmax [n], the largest |z| of each token's (capped) logits.
+    """
+    hidden = np.ascontiguousarray(hidden, dtype=np.uint16)
+    weight = np.ascontiguousarray(weight, dtype=np.uint16)
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    n, H = hidden.shape
+    V = weight.shape[0]
+    tokens = np.asarray(tokens, dtype=np.int64)
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    h64 = (hidden.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w64 = (weight.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    n_valid, n_bad = orc.count(labels, V, ignore_index)
+    if reduction == "mean":
+        scale = grad_out / n_valid if n_valid > 0 else 0.0
+    elif reduction == "sum":
+        scale = grad_out
+    else:
+        raise ValueError("flce_sampled covers the mean and sum reductions")
+    loss = np.zeros(n)
+    zmax = np.zeros(n)
+    gw = np.zeros((vocab_rows.size, H))
+    g_tok = np.zeros((tokens.size, V))
+    for b0 in range(0, n, block):
+        b1 = min(n, b0 + block)
+        z = h64[b0:b1] @ w64.T
+        zmax[b0:b1] = np.abs(softcap * np.tanh(z / softcap) if softcap > 0 else z).max(axis=1)
+        # the row routine with reduction 'sum' and the upstream gradient set to the call's scale gives
+        # the per-token losses and s_i (softmax - target) of these rows
+        o = orc.ce(z, labels[b0:b1], V=V, ignore_index=ignore_index, label_smoothing=label_smoothing,
+                   softcap=softcap, reduction="sum", grad_out=[scale], want_grad=True, nthreads=nthreads)
+        loss[b0:b1] = o["loss_tok"]
+        g = o["grad"]
+        gw += g[:, vocab_rows].T @ h64[b0:b1]
+        sel = np.flatnonzero((tokens >= b0) & (tokens < b1))
+        g_tok[sel] = g[tokens[sel] - b0]
+    gh = g_tok @ w64
+    loss_out = orc.reduce_loss(loss, n_valid, reduction)
+    return {"loss_tok": loss, "loss_out": loss_out, "counts": np.array([n_valid, 0, n_bad]),
+            "grad_hidden": gh, "grad_weight": gw, "zmax": zmax}
+
+
 _default: Oracle | None = None
 
 

@@ -155,3 +155,36 @@ def test_flce_deterministic():
     assert torch.equal(a.grad_weight, b.grad_weight)
     assert torch.equal(a.grad_hidden, b.grad_hidden)
     assert torch.equal(a.loss_tok, b.loss_tok)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_flce_full_size_sampled():
+    """The fused-linear workload at full size (hidden 4096 x 6656, weight 202048 x 6656, T = 30) in the
+    bench's launch configuration (chunks of 1024, default workspace): exact counts, every token's loss
+    within the bf16-logit bound, the mean loss, and sampled grad_hidden rows and grad_weight rows (the
+    sampled tokens' labels included) within 1e-2 relative L2, against the fp64 oracle."""
+    w = synth.C5
+    y = synth.labels(w)
+    hb = synth.flce_hidden_rows(w, np.arange(w.n))
+    wb = synth.flce_weight_rows(w, np.arange(w.V))
+    print(f"\n  inputs ready: hidden {hb.shape}, weight {wb.shape}", flush=True)
+    res = run_flce(hb, wb, y, T=w.softcap, chunk=w.chunk)
+    rng = np.random.default_rng(99)
+    tok = np.sort(rng.choice(w.n, 24, replace=False))
+    lab = y[tok][y[tok] >= 0]
+    voc = np.unique(np.concatenate([rng.choice(w.V, 40, replace=False), lab]))
+    o = oracle.flce_sampled(oracle.default(), hb, wb, y, tok, voc, softcap=w.softcap)
+    print("  oracle done", flush=True)
+    assert res.counts.cpu().tolist() == [int(o["counts"][0]), 0, int(o["counts"][2])]
+    bound = 2.0 * 2.0 ** -9 * o["zmax"] + 1e-4 * np.maximum(1.0, np.abs(o["loss_tok"]))
+    lt = res.loss_tok.cpu().numpy().astype(np.float64)
+    bad = np.abs(lt - o["loss_tok"]) > bound
+    assert not bad.any(), f"loss_tok beyond the bf16-logit bound at {np.flatnonzero(bad)[:5]}"
+    valid = (y != -100)
+    assert abs(float(res.loss_out.cpu()[0]) - o["loss_out"]) <= bound[valid].mean() + 1e-6
+    dh = res.grad_hidden[torch.from_numpy(tok).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
+    e_h = rel_l2(bits_to_f64(dh), o["grad_hidden"])
+    e_w = rel_l2(res.grad_weight[torch.from_numpy(voc).to(DEV)].cpu().numpy().astype(np.float64), o["grad_weight"])
+    print(f"  rel L2 dH {e_h:.2e} dW {e_w:.2e}", flush=True)
+    assert e_h <= REL_L2 and e_w <= REL_L2
