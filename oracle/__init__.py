@@ -80,7 +80,10 @@ class Oracle:
         lib.lce_oracle_flce.restype = ctypes.c_int
         lib.lce_oracle_flce.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_int, p, p, p, p, p, p, ctypes.c_int]
-        if lib.lce_oracle_abi_version() != 1:
+        lib.lce_oracle_row_stats.restype = ctypes.c_int
+        lib.lce_oracle_row_stats.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, ctypes.c_double, p, i64, p, p,
+                                             p, ctypes.c_int]
+        if lib.lce_oracle_abi_version() != 2:
             raise RuntimeError("stale liblce_oracle.so; rebuild it")
         self.lib = lib
 
@@ -137,6 +140,27 @@ class Oracle:
         nb = ctypes.c_int64(0)
         lib.lce_oracle_count(_ptr(lab), lab.size, int(V), int(ignore_index), ctypes.byref(nv), ctypes.byref(nb))
         return nv.value, nb.value
+
+    def row_stats(self, logits: np.ndarray, labels: np.ndarray, *, V: int | None = None, ignore_index: int = -100,
+                  softcap: float = 0.0, rows=None, nthreads: int = 0) -> dict:
+        """Per-row log-sum-exp, target log-probability (0 for ignored rows) and entropy of the softmax over
+        the (capped) logits, in fp64 (labs-molt PR "Enable Liger layers": action log-probabilities and
+        entropy)."""
+        logits = np.ascontiguousarray(logits)
+        n, ld = logits.shape
+        V = ld if V is None else int(V)
+        labels = np.ascontiguousarray(labels, dtype=np.int64)
+        rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = n if rows is None else rows_arr.size
+        lse = np.zeros(nrows)
+        logp = np.zeros(nrows)
+        ent = np.zeros(nrows)
+        rc = self.lib.lce_oracle_row_stats(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V,
+                                           int(ignore_index), float(softcap), _ptr(rows_arr), nrows, _ptr(lse),
+                                           _ptr(logp), _ptr(ent), int(nthreads))
+        if rc != 0:
+            raise ValueError("lce_oracle_row_stats rejected its arguments")
+        return {"lse": lse, "logp": logp, "entropy": ent}
 
     def round_bf16(self, x: np.ndarray) -> np.ndarray:
         """fp64 -> bf16 bit patterns (uint16), round to nearest even, in one step."""

@@ -336,5 +336,60 @@ int lce_oracle_flce(const uint16_t *hidden, const uint16_t *weight, const int64_
     return 0;
 }
 
+/*
+ * Per-row statistics of the softmax over z = T tanh(x/T) (or x when T = 0),
+ * by definition, for the rows listed in `rows` (all n rows when rows == NULL):
+ *   lse_i     = log sum_j exp(z_ij)
+ *   logp_i    = log p_{i,y_i} = z_{i,y_i} - lse_i      (0 for an ignored row)
+ *   entropy_i = -sum_j p_ij log p_ij                   (every row)
+ * The target log-probability and the entropy are the RL-side quantities of
+ * labs-molt PR "Enable Liger layers" (Why attention, RoPE, and RL loss stay in
+ * Molt; Validation / Correctness); lse is what a forward pass keeps for a
+ * deferred backward.  Any of the three outputs may be NULL.
+ */
+int lce_oracle_row_stats(const void *logits, int64_t ld, int dtype, const int64_t *labels, int64_t n,
+                         int64_t V, int64_t ignore_index, double softcap, const int64_t *rows,
+                         int64_t nrows, double *lse_out, double *logp_out, double *entropy_out,
+                         int nthreads)
+{
+    if (n < 0 || V < 1 || ld < V || !logits || !labels || (!rows && nrows != n)) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows && (rows[r] < 0 || rows[r] >= n)) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t row_i = rows ? rows[r] : r;
+            for (int64_t j = 0; j < V; ++j) {
+                double x = load_elem(logits, dtype, row_i * ld + j);
+                z[j] = softcap > 0.0 ? softcap * tanh(x / softcap) : x;
+            }
+            double m = z[0];
+            for (int64_t j = 1; j < V; ++j)
+                if (z[j] > m) m = z[j];
+            double s = 0.0;
+            for (int64_t j = 0; j < V; ++j) s += exp(z[j] - m);
+            const double lse_r = m + log(s);
+            double h = 0.0;   /* -sum p log p with log p_j = z_j - lse */
+            for (int64_t j = 0; j < V; ++j) {
+                double lp = z[j] - lse_r;
+                h -= exp(lp) * lp;
+            }
+            const int64_t y = labels[row_i];
+            if (lse_out) lse_out[r] = lse_r;
+            if (logp_out) logp_out[r] = label_is_valid(y, V, ignore_index) ? z[y] - lse_r : 0.0;
+            if (entropy_out) entropy_out[r] = h;
+        }
+        free(z);
+    }
+    return 0;
+}
+
 /* Version tag so the Python side can check it loaded this file's build. */
-int lce_oracle_abi_version(void) { return 1; }
+int lce_oracle_abi_version(void) { return 2; }

@@ -18,6 +18,8 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
+import synth
 import torch
 import torch.nn.functional as F
 
@@ -426,6 +428,68 @@ def pin_flce_composition(orc):
         _close(o["grad_weight"], c["grad"].T @ Hd, 1e-15, 1e-11, "flce dW = G^T H")
         if not np.array_equal(o["counts"], c["counts"]):
             raise AssertionError("flce counts")
+
+
+# ----------------------------------------------------------------------------- row statistics
+
+def pin_row_stats_closed_forms(orc):
+    """Constant rows: lse = c + ln V, entropy = ln V, log p_y = -ln V.  V = 2: lse = log(e^a + e^b),
+    entropy = the binary entropy of sigmoid(a - b).  Ignored rows give log p = 0 but keep their entropy."""
+    for V in (1, 2, 7, 1000):
+        x = np.full((3, V), 1.75)
+        y = np.array([0, V - 1, -100])
+        o = orc.row_stats(x, y)
+        _close(o["lse"], np.full(3, 1.75 + math.log(V)), 1e-13, 1e-13, f"uniform lse V={V}")
+        _close(o["entropy"], np.full(3, math.log(V)), 1e-12, 1e-13, f"uniform entropy V={V}")
+        _close(o["logp"], np.array([-math.log(V), -math.log(V), 0.0]), 1e-13, 1e-13, f"uniform logp V={V}")
+    a, b = 1.3, -0.4
+    o = orc.row_stats(np.array([[a, b]]), np.array([1]))
+    pa = 1.0 / (1.0 + math.exp(b - a))
+    _close(o["lse"], [math.log(math.exp(a) + math.exp(b))], 1e-14, 0, "V=2 lse")
+    _close(o["logp"], [math.log(1.0 - pa)], 1e-14, 0, "V=2 logp")
+    _close(o["entropy"], [-(pa * math.log(pa) + (1 - pa) * math.log(1 - pa))], 1e-14, 0, "V=2 entropy")
+
+
+def pin_row_stats_torch(orc):
+    """PyTorch fp64 logsumexp, log_softmax at the target and Categorical entropy, with and without the
+    softcap (applied to the logits first), on rows of mixed scale; row subsets and bf16 loading."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(31)
+    x = rng.normal(0, 4, size=(9, 300))
+    x[2] *= 20.0
+    y = rng.integers(0, 300, 9)
+    y[4] = -100
+    for T in (0.0, 30.0, 3.0):
+        t = torch.from_numpy(x)
+        z = T * torch.tanh(t / T) if T > 0 else t
+        lse = torch.logsumexp(z, dim=1).numpy()
+        lsm = torch.log_softmax(z, dim=1).numpy()
+        ent = torch.distributions.Categorical(logits=z).entropy().numpy()
+        o = orc.row_stats(x, y, softcap=T)
+        _close(o["lse"], lse, 1e-13, 1e-12, f"torch lse T={T}")
+        want = np.array([lsm[i, y[i]] if y[i] >= 0 else 0.0 for i in range(9)])
+        _close(o["logp"], want, 1e-13, 1e-12, f"torch logp T={T}")
+        _close(o["entropy"], ent, 1e-12, 1e-12, f"torch entropy T={T}")
+    rows = np.array([8, 0, 4])
+    sub = orc.row_stats(x, y, rows=rows)
+    full = orc.row_stats(x, y)
+    _close(sub["entropy"], full["entropy"][rows], 0, 0, "row subset")
+    xb = synth.f32_to_bf16_bits(x.astype(np.float32))
+    xb64 = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    _close(orc.row_stats(xb, y)["lse"], orc.row_stats(xb64, y)["lse"], 0, 0, "bf16 loading")
+
+
+def pin_row_stats_match_loss(orc):
+    """Without smoothing the per-token loss is -log p_y, and lse - z_y; the entropy of a row equals the
+    label-smoothing loss term (1/V) sum_j (-log p_j) only for the uniform row, where both are ln V."""
+    rng = np.random.default_rng(32)
+    x = rng.normal(0, 2, size=(6, 40))
+    y = rng.integers(0, 40, 6)
+    y[1] = -100
+    for T in (0.0, 7.0):
+        o = orc.row_stats(x, y, softcap=T)
+        c = orc.ce(x, y, softcap=T, want_grad=False)
+        _close(-o["logp"], c["loss_tok"], 1e-13, 1e-13, f"logp vs loss T={T}")
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,12 @@ MUTANTS = [
     ("transposed weight in grad_hidden", "acc += g[i * V + v] * w[v * H + k];", "acc += g[i * V + v] * w[k * H + v % H];"),
     ("grad_weight uses weight instead of hidden", "acc += g[i * V + v] * h[i * H + k];",
      "acc += g[i * V + v] * w[v * H + k];"),
+    ("entropy with the wrong sign", "h -= exp(lp) * lp;", "h += exp(lp) * lp;"),
+    ("entropy weighted by z instead of log p", "h -= exp(lp) * lp;", "h -= exp(lp) * z[j];"),
+    ("target log-probability before the cap", "? z[y] - lse_r : 0.0;",
+     "? load_elem(logits, dtype, row_i * ld + y) - lse_r : 0.0;"),
+    ("row statistics without the max shift", "const double lse_r = m + log(s);", "const double lse_r = log(s);"),
+    ("row statistics ignore the row subset", "const int64_t row_i = rows ? rows[r] : r;", "const int64_t row_i = r;"),
     ("fused-linear scale ignores the reduction",
      "double scale = token_scale(reduction, grad_out, i, n_valid);\n            int64_t am;\n            ce_row(zrow",
      "double scale = token_scale(OR_RED_SUM, grad_out, i, n_valid);\n            int64_t am;\n            ce_row(zrow"),
