@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--workload", default="ce_bf16_2048x131072")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--collect-profiles", action="store_true")
+    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+                    help="split: stats / combine / gradient as separate calls over --tp vocabulary shards")
+    ap.add_argument("--tp", type=int, default=1, help="vocabulary shards of the split path (one GPU)")
     return ap.parse_args()
 
 
@@ -387,6 +390,91 @@ def collect_profiles_flce(workload: str) -> int:
     return 0
 
 
+# ---------------------------------------------------------------- split path
+
+SPLIT_METRIC = "split CE (stats, combine, gradient) ms and HBM GB/s (% peak), bf16 logits 2048×131072, 1 GPU"
+
+
+def bench_split(args, w) -> int:
+    """One step = lce_ce_stats on every shard + lce_ce_combine + lce_ce_grad on every shard, the shards being
+    column slices of one resident matrix (the per-rank work of a vocabulary-parallel layout, or with one shard
+    a forward / deferred-backward pair).  Algorithmic bytes: one read for the statistics and one read + write
+    for the gradient, 3 N V b, plus the records and row outputs."""
+    import numpy as np
+    import torch
+
+    import vocabulary_cross_entropy_row_amd as lce
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    y = synth.labels(w)
+    x = synth.logits(w, y)
+    pristine = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    labels = torch.from_numpy(y).to(dev)
+    nbuf = args.warmup + args.steps
+    bufs = [pristine.clone() for _ in range(nbuf)]
+    tp = args.tp
+    if w.V % (8 * tp):
+        print(f"V = {w.V} does not split into {tp} shards of whole 16-byte vectors", file=sys.stderr)
+        return 2
+    ws = w.V // tp
+    stats = torch.empty((tp, w.n, 8), dtype=torch.float32, device=dev)
+    grad_out = torch.full((1,), w.grad_out, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = {k: [] for k in ("stats", "combine", "grad")}
+
+    def step(buf, timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        for k in range(tp):
+            lce.lce_ce_stats(buf[:, k * ws:(k + 1) * ws], labels, v_offset=k * ws, softcap=w.softcap, stats=stats[k],
+                             stream=stream)
+        e[1].record(stream)
+        rows = lce.lce_ce_combine(stats, labels, w.V, label_smoothing=w.label_smoothing, reduction=w.reduction,
+                                  stream=stream)
+        e[2].record(stream)
+        for k in range(tp):
+            lce.lce_ce_grad(buf[:, k * ws:(k + 1) * ws], labels, w.V, rows, v_offset=k * ws,
+                            label_smoothing=w.label_smoothing, softcap=w.softcap, reduction=w.reduction,
+                            grad_out=grad_out, stream=stream)
+        e[3].record(stream)
+        if timed:
+            ev["stats"].append((e[0], e[1]))
+            ev["combine"].append((e[1], e[2]))
+            ev["grad"].append((e[2], e[3]))
+        return e
+
+    for i in range(args.warmup):
+        step(bufs[i], False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    whole = [step(bufs[args.warmup + i], True) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean([a[0].elapsed_time(a[3]) for a in whole]))
+    phase = {k: round(float(np.mean([a.elapsed_time(b) for a, b in v])), 5) for k, v in ev.items()}
+    nbytes = 3 * w.n * w.V * w.elem_bytes + w.n * (8 + tp * 32 * 2 + 4 * 6)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": SPLIT_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "V": w.V, "shards": tp, "shard_V": ws, "logits_dtype": w.dtype,
+                   "parallelism": f"vocabulary split into {tp} shards on one GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "stats + combine + gradient calls of one step, HIP events", "phase_ms": phase,
+                     "stats_GBps": round(w.n * w.V * w.elem_bytes / (phase["stats"] * 1e-3) / 1e9, 1),
+                     "grad_GBps": round(2 * w.n * w.V * w.elem_bytes / (phase["grad"] * 1e-3) / 1e9, 1),
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------- the bench
 
 def main() -> int:
@@ -404,6 +492,8 @@ def main() -> int:
 
     if args.workload in synth.FLCE_WORKLOADS:
         return bench_flce(args, synth.FLCE_WORKLOADS[args.workload])
+    if args.path == "split":
+        return bench_split(args, synth.WORKLOADS[args.workload])
 
     import numpy as np
     import torch

@@ -114,6 +114,76 @@ lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const 
                          int64_t *counts, hipStream_t stream);
 
 /*
+ * ---- split cross-entropy: shard statistics, combine, gradient -------------
+ *
+ * The same row operation as lce_ce_fwd_bwd in three calls, so that
+ *  - the vocabulary can be split into shards (one per device in a
+ *    vocabulary-parallel layout, Megatron-LM PR "Add opt-in Liger
+ *    vocab-parallel cross entropy", What does this PR do?): every holder of
+ *    a shard runs lce_ce_stats on it, the stats records (32 bytes per row and
+ *    shard) are gathered, lce_ce_combine forms the row results, and every
+ *    holder runs lce_ce_grad on its shard;
+ *  - with one shard, the gradient can be deferred to a backward pass that
+ *    knows the upstream gradient (lce_ce_grad), instead of being written by
+ *    the forward (Liger-Kernel PR "[Megatron] Add SwiGLU integration", Known
+ *    issues: an in-place forward cannot serve a reused graph);
+ *  - the RL-side row outputs -- target log-probability and entropy,
+ *    labs-molt PR "Enable Liger layers", Why attention, RoPE, and RL loss stay
+ *    in Molt -- come out of the same sweep.
+ * A shard holds the global vocabulary columns [v_offset, v_offset + shard_V)
+ * of every row; labels are global.  Shard widths and ld must be multiples of
+ * 8 (bf16) or 4 (fp32) elements and the shard 16-byte aligned
+ * (LCE_ERR_UNSUPPORTED otherwise).  All pointers are device pointers; calls
+ * are stream-ordered and never synchronise the host.
+ */
+
+/* Bytes of one shard's stats records for n rows. */
+size_t lce_ce_stats_bytes(int64_t n);
+
+/*
+ * One read-only sweep of a shard [n, ld] (first shard_V columns used):
+ * writes n stats records (lce_ce_stats_bytes(n) bytes) to stats.  softcap as
+ * for lce_ce_fwd_bwd; the argmax is over the raw logits, first index on ties.
+ */
+lce_status lce_ce_stats(const void *logits, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                        int64_t shard_V, int64_t v_offset, int64_t ignore_index, float softcap, float *stats,
+                        hipStream_t stream);
+
+/*
+ * Row results from the stats of `shards` shards, stored one after another
+ * (shard k's records at stats + k * n * 8 floats) in ascending v_offset
+ * order, the shards covering [0, V) exactly once:
+ *   lse           fp32 [n], required: log sum_j exp(z_j).
+ *   one_minus_py  fp32 [n] or NULL: 1 - p_y for valid rows (0 otherwise),
+ *                 accumulated without the target, as lce_ce_grad needs it.
+ *   loss_tok      fp32 [n] or NULL: lse - (1 - eps) z_y - (eps / V) sum_j z_j
+ *                 (0 for ignored rows).
+ *   loss_out      fp32 scalar or NULL (needs loss_tok): mean over valid
+ *                 labels or sum; 0 for LCE_RED_NONE.
+ *   logprob       fp32 [n] or NULL: log p_y = z_y - lse (0 for ignored rows).
+ *   entropy       fp32 [n] or NULL: -sum_j p_j log p_j (every row).
+ *   argmax_out    int64 [n] or NULL: global first-index argmax.
+ *   counts        int64 [3], required: {n_valid, n_correct, n_bad}.
+ */
+lce_status lce_ce_combine(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
+                          int64_t ignore_index, float label_smoothing, lce_reduction reduction, float *lse,
+                          float *one_minus_py, float *loss_tok, float *loss_out, float *logprob, float *entropy,
+                          int64_t *argmax_out, int64_t *counts, hipStream_t stream);
+
+/*
+ * The gradient of one shard, written in place over it (columns past shard_V
+ * untouched): dx_j = s (p_j - (1 - eps)[j = y] - eps / V) dz_j/dx_j with
+ * p_j = exp(z_j - lse), p_y - 1 = -one_minus_py, and s = grad_out / n_valid
+ * (mean; n_valid = counts[0]), grad_out (sum) or grad_out[i] (none); grad_out
+ * NULL means 1.  Ignored rows are written as zeros.  lse, one_minus_py and
+ * counts come from lce_ce_combine over all shards.
+ */
+lce_status lce_ce_grad(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                       int64_t shard_V, int64_t v_offset, int64_t V, int64_t ignore_index, float label_smoothing,
+                       float softcap, lce_reduction reduction, const float *grad_out, const float *lse,
+                       const float *one_minus_py, const int64_t *counts, hipStream_t stream);
+
+/*
  * Bytes of device workspace lce_flce_fwd_bwd uses by default (0 for invalid
  * sizes).  It holds W^T [H, V], one chunk of logits [C, V], split-K partials
  * [16, C, H] fp32, and the transposed gradients and hidden states of one

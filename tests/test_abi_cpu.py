@@ -154,3 +154,51 @@ def test_flce_workspace_groups():
     # one byte short of the one-chunk layout is rejected before any device work
     st, msg = call_flce(n=n, H=H, V=V, chunk=C, wsb=one - 1)
     assert st == lce.LCE_ERR_INVALID_ARG and "minimum" in msg
+
+
+def call_stats(**over):
+    a = dict(logits=FAKE, ld=64, dtype=lce.LCE_BF16, labels=FAKE, n=4, Vs=64, v0=0, ignore_index=-100, softcap=0.0,
+             stats=FAKE, stream=None)
+    a.update(over)
+    st = lce.lib().lce_ce_stats(a["logits"], a["ld"], a["dtype"], a["labels"], a["n"], a["Vs"], a["v0"],
+                                a["ignore_index"], a["softcap"], a["stats"], a["stream"])
+    return st, lce.lce_last_error()
+
+
+@pytest.mark.parametrize("over,needle,status", [
+    (dict(n=-1), "n must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(Vs=0), "shard width", lce.LCE_ERR_INVALID_ARG),
+    (dict(v0=-8), "v_offset", lce.LCE_ERR_INVALID_ARG),
+    (dict(ld=32), "ld", lce.LCE_ERR_INVALID_ARG),
+    (dict(dtype=3), "dtype", lce.LCE_ERR_INVALID_ARG),
+    (dict(stats=None), "stats", lce.LCE_ERR_INVALID_ARG),
+    (dict(labels=None), "labels", lce.LCE_ERR_INVALID_ARG),
+    (dict(softcap=-2.0), "softcap", lce.LCE_ERR_INVALID_ARG),
+    (dict(Vs=60, ld=64), "16-byte rows", lce.LCE_ERR_UNSUPPORTED),
+    (dict(logits=FAKE + 8), "16-byte rows", lce.LCE_ERR_UNSUPPORTED),
+    (dict(v0=2 ** 31 - 8), "31 bits", lce.LCE_ERR_UNSUPPORTED),
+])
+def test_stats_rejects_bad_arguments(over, needle, status):
+    st, msg = call_stats(**over)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_combine_and_grad_reject_bad_arguments():
+    L = lce.lib()
+    st = L.lce_ce_combine(FAKE, 0, FAKE, 4, 64, -100, 0.0, lce.LCE_RED_MEAN, FAKE, None, FAKE, None, None, None, None,
+                          FAKE, None)
+    assert st == lce.LCE_ERR_INVALID_ARG and "shards" in lce.lce_last_error()
+    st = L.lce_ce_combine(FAKE, 2, FAKE, 4, 64, -100, 0.0, 9, FAKE, None, FAKE, None, None, None, None, FAKE, None)
+    assert st == lce.LCE_ERR_INVALID_ARG and "reduction" in lce.lce_last_error()
+    st = L.lce_ce_combine(FAKE, 2, FAKE, 4, 64, -100, 0.0, lce.LCE_RED_MEAN, None, None, FAKE, None, None, None, None,
+                          FAKE, None)
+    assert st == lce.LCE_ERR_INVALID_ARG and "lse" in lce.lce_last_error()
+    # the shard must lie inside [0, V)
+    st = L.lce_ce_grad(FAKE, 64, lce.LCE_BF16, FAKE, 4, 64, 32, 64, -100, 0.0, 0.0, lce.LCE_RED_MEAN, None, FAKE, FAKE,
+                       FAKE, None)
+    assert st == lce.LCE_ERR_INVALID_ARG and "inside" in lce.lce_last_error()
+    st = L.lce_ce_grad(FAKE, 64, lce.LCE_BF16, FAKE, 4, 64, 0, 64, -100, 0.0, 0.0, lce.LCE_RED_MEAN, None, None, FAKE,
+                       FAKE, None)
+    assert st == lce.LCE_ERR_INVALID_ARG and "lse" in lce.lce_last_error()
+    assert lce.lib().lce_ce_stats_bytes(10) == 320

@@ -1,0 +1,192 @@
+"""GPU parity of the split cross-entropy (lce_ce_stats / lce_ce_combine / lce_ce_grad) against the
+fp64 oracle, through the C ABI.
+
+One shard is the forward / deferred-backward split; several shards of one matrix on this GPU are
+the vocabulary-parallel layout (each shard a column slice; the stats records are what ranks would
+exchange).  Tolerances: integers exact; loss, lse and log p_y within 1e-4 max(1, |o|) (the fp32 loss
+rule); entropy within 1e-4 max(1, |lse|) -- it is lse - E_p[z], a difference of two fp32 terms of
+size |lse|; gradients by the same bf16 2-ulp / fp32 rules as the fused kernel.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import check_bf16_grad, check_f32_grad, check_loss, row_scales, smoothing_allowance
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible to torch", allow_module_level=True)
+
+import vocabulary_cross_entropy_row_amd as lce  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(x: np.ndarray):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def from_dev(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def run_split(x: np.ndarray, y: np.ndarray, V: int, widths, *, eps=0.0, T=0.0, red="mean", grad_out=None):
+    """stats of every shard, one combine, then the gradient of every shard in place."""
+    buf = to_dev(x)
+    lab = torch.from_numpy(y.astype(np.int64)).to(DEV)
+    offs = np.concatenate([[0], np.cumsum(widths)]).astype(int)
+    assert offs[-1] == V
+    stats = torch.stack([lce.lce_ce_stats(buf[:, offs[k]:offs[k + 1]], lab, v_offset=int(offs[k]), softcap=T)
+                         for k in range(len(widths))]).contiguous()
+    rows = lce.lce_ce_combine(stats, lab, V, label_smoothing=eps, reduction=red)
+    g = None
+    if grad_out is not None:
+        g = torch.from_numpy(np.asarray(grad_out, dtype=np.float32).reshape(-1)).to(DEV)
+    for k in range(len(widths)):
+        lce.lce_ce_grad(buf[:, offs[k]:offs[k + 1]], lab, V, rows, v_offset=int(offs[k]), label_smoothing=eps,
+                        softcap=T, reduction=red, grad_out=g)
+    torch.cuda.synchronize()
+    return rows, buf
+
+
+def check_split(x, y, V, widths, *, eps=0.0, T=0.0, red="mean", grad_out=None, rows_sel=None):
+    n = x.shape[0]
+    rows, buf = run_split(x, y, V, widths, eps=eps, T=T, red=red, grad_out=grad_out)
+    orc = oracle.default()
+    o = orc.ce(x, y, V=V, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out, rows=rows_sel)
+    st = orc.row_stats(x, y, V=V, softcap=T, rows=rows_sel)
+    idx = np.arange(n) if rows_sel is None else np.asarray(rows_sel)
+    check_loss(rows.loss_tok.cpu().numpy()[idx], o["loss_tok"], "loss_tok")
+    check_loss(rows.lse.cpu().numpy()[idx], st["lse"], "lse")
+    check_loss(rows.logprob.cpu().numpy()[idx], st["logp"], "logprob")
+    ent = rows.entropy.cpu().numpy()[idx].astype(np.float64)
+    lim = 1e-4 * np.maximum(1.0, np.abs(st["lse"]))
+    assert np.all(np.abs(ent - st["entropy"]) <= lim), f"entropy off by {np.max(np.abs(ent - st['entropy'])):.3e}"
+    assert np.array_equal(rows.argmax.cpu().numpy()[idx], o["argmax"]), "argmax differs"
+    nv, nb = orc.count(y, V)
+    counts = rows.counts.cpu().numpy()
+    assert counts[0] == nv and counts[2] == nb
+    if rows_sel is None:
+        assert counts[1] == o["counts"][1]
+        want = o["loss_out"] if red != "none" else 0.0
+        check_loss(float(rows.loss_out.cpu()[0]), want, "loss_out")
+    out = from_dev(buf)[idx, :V]
+    scales = row_scales(red, grad_out, y, V)[idx]
+    if x.dtype == np.uint16:
+        n_allow = check_bf16_grad(out, o["grad"], orc, allow=smoothing_allowance(scales, eps, V))
+        assert n_allow <= max(4, out.size // 1000)
+    else:
+        check_f32_grad(out, o["grad"], scales)
+    return rows
+
+
+def _labels(rng, n, V, ignore_frac=0.1, bad=0):
+    y = rng.integers(0, V, n).astype(np.int64)
+    y[rng.permutation(n)[: int(round(ignore_frac * n))]] = -100
+    if bad:
+        pos = rng.permutation(n)[:bad]
+        y[pos[::2]] = V + 3
+        y[pos[1::2]] = -7
+    return y
+
+
+CASES = [  # n, V, dtype, shard widths
+    (32, 8488, "bf16", [8488]),
+    (32, 8488, "bf16", [2048, 4096, 2344]),
+    (16, 32768, "bf16", [4096] * 8),
+    (24, 6000, "f32", [2000, 4000]),
+    (8, 131072, "bf16", [16384] * 8),
+    (40, 1000, "bf16", [8, 992]),
+]
+FEATS = {
+    "plain": dict(),
+    "smooth_sum": dict(eps=0.1, red="sum", grad_out=[0.5]),
+    "cap_none": dict(T=5.0, red="none"),
+    "all": dict(eps=0.2, T=30.0, red="mean", grad_out=[-1.5]),
+}
+
+
+@pytest.mark.parametrize("n,V,dt,widths", CASES, ids=[f"{c[0]}x{c[1]}{c[2]}_tp{len(c[3])}" for c in CASES])
+@pytest.mark.parametrize("feat", list(FEATS))
+def test_split_matrix(n, V, dt, widths, feat):
+    rng = np.random.default_rng([n, V, len(widths), len(feat)])
+    x = (rng.standard_normal((n, V)) * (4.0 if "cap" in feat or feat == "all" else 2.0)).astype(np.float32)
+    x = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    y = _labels(rng, n, V, bad=2 if feat == "all" else 0)
+    kw = dict(FEATS[feat])
+    if feat == "cap_none":
+        kw["grad_out"] = rng.normal(size=n)   # per-token, both signs
+    check_split(x, y, V, widths, **kw)
+
+
+def test_split_argmax_tie_across_shards():
+    """Equal maxima in two shards: the smaller global index wins, whichever shard holds it."""
+    rng = np.random.default_rng(5)
+    n, V = 6, 4096
+    x = rng.normal(size=(n, V)).astype(np.float32)
+    for i, (a, b) in enumerate([(10, 3000), (2047, 2048), (0, 4095), (1500, 2600), (100, 101), (4000, 2100)]):
+        x[i, a] = x[i, b] = 9.0
+    xb = synth.f32_to_bf16_bits(x)
+    y = rng.integers(0, V, n)
+    rows = check_split(xb, y, V, [2048, 2048])
+    want = [10, 2047, 0, 1500, 100, 2100]
+    assert rows.argmax.cpu().numpy().tolist() == want
+
+
+def test_split_matches_fused():
+    """One shard, deferred backward: the same loss and gradient as the fused in-place call."""
+    rng = np.random.default_rng(6)
+    n, V = 64, 16384
+    x = synth.f32_to_bf16_bits((rng.standard_normal((n, V)) * 3).astype(np.float32))
+    y = _labels(rng, n, V)
+    rows, buf = run_split(x, y, V, [V], eps=0.1, T=30.0, grad_out=[0.5])
+    fbuf = to_dev(x)
+    res = lce.lce_ce_fwd_bwd(fbuf, torch.from_numpy(y).to(DEV), label_smoothing=0.1, softcap=30.0,
+                             grad_out=torch.tensor([0.5], device=DEV))
+    torch.cuda.synchronize()
+    assert torch.allclose(rows.loss_tok, res.loss_tok, rtol=1e-5, atol=1e-5)
+    diff = (buf.float() - fbuf.float()).abs().max().item()
+    assert diff <= 2.0 ** -7 * fbuf.float().abs().max().item(), diff
+
+
+def test_split_edge_cases():
+    rng = np.random.default_rng(8)
+    V = 64
+    x = synth.f32_to_bf16_bits(rng.normal(size=(5, V)).astype(np.float32))
+    check_split(x, np.full(5, -100), V, [32, 32])                  # all ignored: zeros, loss 0
+    check_split(x, np.array([0, 63, 31, 32, 5]), V, [32, 32])      # targets at shard edges
+    check_split(x[:1], np.array([7]), V, [8] * 8)                   # one row, eight shards
+    # n = 0
+    z = torch.zeros((0, V), dtype=torch.bfloat16, device=DEV)
+    lab = torch.zeros(0, dtype=torch.int64, device=DEV)
+    st = lce.lce_ce_stats(z, lab)
+    rows = lce.lce_ce_combine(st, lab, V)
+    lce.lce_ce_grad(z, lab, V, rows)
+    torch.cuda.synchronize()
+    assert rows.counts.cpu().tolist() == [0, 0, 0] and float(rows.loss_out.cpu()[0]) == 0.0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("tp", [1, 8])
+def test_split_full_size(tp):
+    """bf16 [2048, 131072] as 1 and 8 vocabulary shards: sampled rows element by element, the reduced
+    loss and counts over every row."""
+    w = synth.C2
+    y = synth.labels(w)
+    x = synth.logits(w, y)
+    rng = np.random.default_rng(0)
+    sel = np.unique(np.concatenate([rng.choice(w.n, 16, replace=False), np.flatnonzero(y == -100)[:2], [0, w.n - 1]]))
+    rows = check_split(x, y, w.V, [w.V // tp] * tp, rows_sel=sel)
+    o = oracle.ce(x, y, V=w.V, want_grad=False)
+    check_loss(float(rows.loss_out.cpu()[0]), o["loss_out"], "loss_out")
+    assert int(rows.counts.cpu()[1]) == int(o["counts"][1])

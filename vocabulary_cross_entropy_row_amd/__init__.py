@@ -54,6 +54,15 @@ def lib() -> ctypes.CDLL:
     L.lce_ce_argmax.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, p, p, p]
     L.lce_flce_workspace_bytes.restype = ctypes.c_size_t
     L.lce_flce_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.lce_ce_stats_bytes.restype = ctypes.c_size_t
+    L.lce_ce_stats_bytes.argtypes = [i64]
+    L.lce_ce_stats.restype = ctypes.c_int
+    L.lce_ce_stats.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, i64, f32, p, p]
+    L.lce_ce_combine.restype = ctypes.c_int
+    L.lce_ce_combine.argtypes = [p, i64, p, i64, i64, i64, f32, ctypes.c_int, p, p, p, p, p, p, p, p, p]
+    L.lce_ce_grad.restype = ctypes.c_int
+    L.lce_ce_grad.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, p, p, p,
+                              p]
     L.lce_flce_workspace_bytes_grouped.restype = ctypes.c_size_t
     L.lce_flce_workspace_bytes_grouped.argtypes = [i64, i64, i64, i64, i64]
     L.lce_flce_fwd_bwd.restype = ctypes.c_int
@@ -158,6 +167,80 @@ def lce_ce_argmax(logits, labels=None, *, ignore_index: int = -100, argmax_out=N
                              _ptr(argmax_out), _ptr(counts), _stream(stream))
     _check(st)
     return argmax_out, counts
+
+
+# ---- split cross-entropy: shard statistics, combine, gradient --------------------------------
+
+STATS_FLOATS = 8
+
+
+def _shard_view(shard):
+    if shard.dim() != 2 or (shard.size(1) > 1 and shard.stride(1) != 1):
+        raise ValueError("a shard must be a 2-D view with unit column stride")
+    n, Vs = shard.shape
+    return n, Vs, (shard.stride(0) if n > 1 else Vs)
+
+
+def lce_ce_stats(shard, labels, *, v_offset: int = 0, ignore_index: int = -100, softcap: float = 0.0,
+                 stats=None, stream=None):
+    """One read-only sweep of a vocabulary shard (global columns [v_offset, v_offset + width));
+    returns its stats records, fp32 [n, 8]."""
+    import torch
+    n, Vs, ld = _shard_view(shard)
+    if stats is None:
+        stats = torch.empty((n, STATS_FLOATS), dtype=torch.float32, device=shard.device)
+    _check(lib().lce_ce_stats(_ptr(shard), ld, _dtype_code(shard), _ptr(labels), n, Vs, int(v_offset),
+                              int(ignore_index), float(softcap), _ptr(stats), _stream(stream)))
+    return stats
+
+
+@dataclass
+class SplitRows:
+    lse: object            # fp32 [n]
+    one_minus_py: object   # fp32 [n]
+    loss_tok: object       # fp32 [n]
+    loss_out: object       # fp32 [1]
+    logprob: object        # fp32 [n]
+    entropy: object        # fp32 [n]
+    argmax: object         # int64 [n]
+    counts: object         # int64 [3]
+
+
+def lce_ce_combine(stats, labels, V: int, *, ignore_index: int = -100, label_smoothing: float = 0.0,
+                   reduction: str = "mean", stream=None) -> SplitRows:
+    """Row results from the stats of all shards: ``stats`` is fp32 [shards, n, 8] (or [n, 8] for one),
+    shards in ascending vocabulary order."""
+    import torch
+    if stats.dim() == 2:
+        stats = stats.unsqueeze(0)
+    if not stats.is_contiguous() or stats.size(2) != STATS_FLOATS:
+        raise ValueError("stats must be a contiguous [shards, n, 8] fp32 tensor")
+    shards, n = stats.shape[0], stats.shape[1]
+    dev = stats.device
+    f = lambda: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+    out = SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=dev), f(), f(),
+                    torch.empty(n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
+    _check(lib().lce_ce_combine(_ptr(stats), shards, _ptr(labels), n, int(V), int(ignore_index),
+                                float(label_smoothing), REDUCTIONS[reduction], _ptr(out.lse), _ptr(out.one_minus_py),
+                                _ptr(out.loss_tok), _ptr(out.loss_out), _ptr(out.logprob), _ptr(out.entropy),
+                                _ptr(out.argmax), _ptr(out.counts), _stream(stream)))
+    return out
+
+
+def lce_ce_grad(shard, labels, V: int, rows: SplitRows, *, v_offset: int = 0, ignore_index: int = -100,
+                label_smoothing: float = 0.0, softcap: float = 0.0, reduction: str = "mean", grad_out=None,
+                stream=None) -> None:
+    """Write the gradient of one shard in place, from the combined row results."""
+    import torch
+    n, Vs, ld = _shard_view(shard)
+    if grad_out is not None and not torch.is_tensor(grad_out):
+        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=shard.device)
+    elif grad_out is not None and grad_out.dtype != torch.float32:
+        grad_out = grad_out.float()
+    _check(lib().lce_ce_grad(_ptr(shard), ld, _dtype_code(shard), _ptr(labels), n, Vs, int(v_offset), int(V),
+                             int(ignore_index), float(label_smoothing), float(softcap), REDUCTIONS[reduction],
+                             _ptr(grad_out), _ptr(rows.lse), _ptr(rows.one_minus_py), _ptr(rows.counts),
+                             _stream(stream)))
 
 
 def lce_flce_workspace_bytes(n: int, H: int, V: int, chunk_tokens: int) -> int:

@@ -21,7 +21,7 @@ ARCH = "gfx950"
 # (source, extra flags, object name).  ce_rows_inst.hip is compiled once per
 # (dtype, rounds in VGPRs, rounds in LDS) family of the resident row kernel.
 FAMILIES = [(1, 0), (2, 0), (4, 0), (8, 0), (4, 8), (8, 8), (10, 9), (13, 9), (16, 9)]
-UNITS = [("ce_kernels.hip", [], "ce_kernels"), ("flce.hip", [], "flce"), ("lce_api.cpp", ["-x", "hip"], "lce_api")] + [
+UNITS = [("ce_kernels.hip", [], "ce_kernels"), ("flce.hip", [], "flce"), ("ce_split.hip", [], "ce_split"), ("lce_api.cpp", ["-x", "hip"], "lce_api")] + [
     ("ce_rows_inst.hip", [f"-DLCE_BF16={b}", f"-DLCE_KR={kr}", f"-DLCE_KL={kl}"], f"ce_rows_{b}_{kr}_{kl}")
     for b in (1, 0) for kr, kl in FAMILIES]
 

@@ -1,0 +1,354 @@
+// Cross-entropy split into three phases, for a vocabulary split across
+// devices (Megatron-LM PR "Add opt-in Liger vocab-parallel cross entropy",
+// What does this PR do?: per-token fp32 losses, the supplied TP group, the
+// original global argmax with smallest-index ties) and for a backward pass
+// whose upstream gradient is known only later (the pages' in-place kernels
+// compute the gradient inside the forward; Liger-Kernel PR "[Megatron] Add
+// SwiGLU integration", Known issues, is what that costs a reused graph):
+//
+//   stats    one read of a shard [n, Vs] of the logits (global columns
+//            [v0, v0 + Vs)): per row m = max z, s = sum_{j != y} e^{z - m},
+//            e = sum_j e^{z - m} z, sum z, the target's z when it lies in the
+//            shard, and the shard's first-index argmax of the raw logits.
+//   combine  per row over the shards (in ascending v0): lse, 1 - p_y, the loss,
+//            log p_y and the entropy (labs-molt PR "Enable Liger layers": the
+//            RL side needs action log-probabilities and entropy), the global
+//            argmax, the counts and the reduced loss.
+//   grad     the gradient of a shard in place, from lse and 1 - p_y, with the
+//            reduction and upstream gradient given at this point.
+//
+// With one shard this is a forward / deferred-backward split; with several it
+// is the local half of a vocabulary-parallel loss whose only exchange is the
+// stats records (32 bytes per row and shard).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ce_device.h"
+#include "lce_internal.h"
+
+namespace lce {
+namespace {
+
+using dev::Elt;
+using dev::kLog2e;
+using dev::NT;
+using dev::NWAVE;
+using dev::u32x4;
+
+
+// one thread's running statistics of a stretch of the row
+struct Part {
+    float m = -FLT_MAX;   // running max of z (finite start: no inf - inf)
+    float s = 0.0f;       // sum over j != target of e^{z - m}
+    float e = 0.0f;       // sum over j of e^{z - m} z
+    float zs = 0.0f;      // sum of z
+    float amv = -INFINITY;
+    int am = 0x7fffffff;  // shard-local index of the first maximum of the raw logits
+};
+
+__device__ __forceinline__ void combine(Part &a, float m2, float s2, float e2) {
+    const float M = fmaxf(a.m, m2);
+    const float f1 = dev::exp2_fast((a.m - M) * kLog2e), f2 = dev::exp2_fast((m2 - M) * kLog2e);
+    a.s = a.s * f1 + s2 * f2;
+    a.e = a.e * f1 + e2 * f2;
+    a.m = M;
+}
+
+constexpr int kStatsThreads = 256;                    // four waves per row: several rows per CU
+constexpr int kStatsWaves = kStatsThreads / 64;
+constexpr int kStatsAhead = 8;                        // 16-byte vectors each thread keeps in flight
+
+template <bool BF16, bool SOFTCAP>
+__global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *logits, int64_t ld, int64_t Vs,
+                                                                 int64_t v0, const int64_t *labels,
+                                                                 int64_t ignore_index, float softcap, float *stats) {
+    using EL = Elt<BF16>;
+    constexpr int E = EL::E;
+    constexpr int NTS = kStatsThreads;
+    __shared__ float sh[5][kStatsWaves];
+    __shared__ int sh_i[kStatsWaves];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nvec = static_cast<int>(Vs / E);
+    const int64_t y = labels[row];
+    const int yl = (y != ignore_index && y >= v0 && y < v0 + Vs) ? static_cast<int>(y - v0) : -1;   // in shard
+    const int yv = yl >= 0 ? yl / E : -1, ye = yl >= 0 ? yl % E : 0;
+    const dev::Cap cap{SOFTCAP ? 2.0f * kLog2e / softcap : 0.0f, softcap};
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(logits)) + row * ld * EL::bytes, 0,
+        static_cast<uint32_t>(nvec) * 16u, 0x00020000);
+
+    Part p;
+    float zy = 0.0f;
+    for (int base = 0; base < nvec; base += NTS * kStatsAhead) {
+        u32x4 v[kStatsAhead];
+#pragma unroll
+        for (int u = 0; u < kStatsAhead; ++u)   // past the row: the descriptor returns zeros
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + u * NTS + tid) * 16, 0, 2);
+#pragma unroll
+        for (int u = 0; u < kStatsAhead; ++u) {
+            const int vi = base + u * NTS + tid;
+            if (vi >= nvec) continue;
+            float x[E], z[E];
+            float rmax = -FLT_MAX, xmax = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                x[k] = EL::get(v[u], k);
+                z[k] = SOFTCAP ? cap.z_of_r(cap.r_of(x[k])) : x[k];
+                rmax = fmaxf(rmax, z[k]);
+                xmax = fmaxf(xmax, x[k]);
+            }
+            if (xmax > p.amv) {   // vectors come in index order per thread: keep the first
+                int first = E - 1;
+#pragma unroll
+                for (int k = E - 2; k >= 0; --k)
+                    if (x[k] == xmax) first = k;
+                p.amv = xmax;
+                p.am = vi * E + first;
+            }
+            const float mn = fmaxf(p.m, rmax), mnL = mn * kLog2e;
+            const float f = dev::exp2_fast(fmaf(p.m, kLog2e, -mnL));
+            float ex[E], pe = 0.0f, zsum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                ex[k] = dev::exp2_fast(fmaf(z[k], kLog2e, -mnL));
+                pe = fmaf(ex[k], z[k], pe);
+                zsum += z[k];
+            }
+            if (vi == yv) {   // the target's vector: its element stays out of s
+#pragma unroll
+                for (int k = 0; k < E; ++k)
+                    if (k == ye) {
+                        zy = z[k];
+                        ex[k] = 0.0f;
+                    }
+            }
+            float ps = ex[0];
+#pragma unroll
+            for (int k = 1; k < E; ++k) ps += ex[k];
+            p.zs += zsum;
+            p.s = fmaf(p.s, f, ps);
+            p.e = fmaf(p.e, f, pe);
+            p.m = mn;
+        }
+    }
+    // wave, then workgroup
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        combine(p, __shfl_xor(p.m, o, 64), __shfl_xor(p.s, o, 64), __shfl_xor(p.e, o, 64));
+        p.zs += __shfl_xor(p.zs, o, 64);
+    }
+    dev::wave_argmax(p.amv, p.am);
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) {
+        sh[0][w] = p.m;
+        sh[1][w] = p.s;
+        sh[2][w] = p.e;
+        sh[3][w] = p.zs;
+        sh[4][w] = p.amv;
+        sh_i[w] = p.am;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        Part t;
+        t.m = sh[0][0];
+        t.s = sh[1][0];
+        t.e = sh[2][0];
+        t.zs = sh[3][0];
+        t.amv = sh[4][0];
+        t.am = sh_i[0];
+        for (int k = 1; k < kStatsWaves; ++k) {
+            combine(t, sh[0][k], sh[1][k], sh[2][k]);
+            t.zs += sh[3][k];
+            dev::argmax_combine(t.amv, t.am, sh[4][k], sh_i[k]);
+        }
+        float *o = stats + row * 8;
+        o[0] = t.m;
+        o[1] = t.s;
+        o[2] = t.e;
+        o[3] = t.zs;
+        o[4] = t.amv;
+        o[5] = __int_as_float(static_cast<int>(v0 + t.am));   // global index (V < 2^31)
+        if (yl < 0) {
+            o[6] = 0.0f;
+            o[7] = 0.0f;
+        }
+    }
+    // the target's z, from the thread that read it
+    if (yl >= 0 && tid == yv % NTS) {
+        stats[row * 8 + 6] = zy;
+        stats[row * 8 + 7] = 1.0f;
+    }
+}
+
+// per row over the shards: outputs; n_correct by integer atomics (order-free)
+__global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
+                                                         int64_t ignore_index, float eps, float *lse_out,
+                                                         float *q_out, float *loss_tok, float *logp_out,
+                                                         float *ent_out, int64_t *argmax_out, int64_t *counts) {
+    const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+    if (i >= n) return;
+    Part t;
+    float zy = 0.0f;
+    bool has = false;
+    int64_t am = -1;
+    for (int64_t k = 0; k < shards; ++k) {
+        const float *r = stats + (k * n + i) * 8;
+        combine(t, r[0], r[1], r[2]);
+        t.zs += r[3];
+        if (r[4] > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
+            t.amv = r[4];
+            am = __float_as_int(r[5]);
+        }
+        if (r[7] != 0.0f) {
+            zy = r[6];
+            has = true;
+        }
+    }
+    const int64_t y = labels[i];
+    const bool valid = y != ignore_index && y >= 0 && y < V;
+    const float ey = has ? dev::exp2_fast((zy - t.m) * kLog2e) : 0.0f;
+    const float S = t.s + ey;
+    const float lse = t.m + logf(S);
+    lse_out[i] = lse;
+    if (q_out) q_out[i] = valid ? t.s / S : 0.0f;
+    if (loss_tok) loss_tok[i] = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
+    if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
+    if (ent_out) ent_out[i] = lse - t.e / S;   // -sum p log p = lse - sum p z
+    if (argmax_out) argmax_out[i] = am;
+    if (valid && am == y) __hip_atomic_fetch_add(reinterpret_cast<unsigned long long *>(counts + 1), 1ull,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool BF16, bool SOFTCAP, bool SMOOTH>
+__global__ __launch_bounds__(256) void ce_grad_kernel(void *logits, int64_t ld, int64_t Vs, int64_t v0, int64_t V,
+                                                      const int64_t *labels, int64_t ignore_index, float eps,
+                                                      float softcap, int reduction, const float *grad_out,
+                                                      const float *lse, const float *q, const int64_t *counts,
+                                                      int blocks_per_row) {
+    using EL = Elt<BF16>;
+    constexpr int E = EL::E;
+    constexpr int PER = 4;   // vectors per thread
+    const int64_t row = blockIdx.x / blocks_per_row;
+    const int part = blockIdx.x % blocks_per_row;
+    const int nvec = static_cast<int>(Vs / E);
+    const int64_t y = labels[row];
+    const bool valid = y != ignore_index && y >= 0 && y < V;
+    const int64_t nv = counts[0];
+    const float g = reduction == 0 ? (grad_out ? grad_out[row] : 1.0f) : (grad_out ? grad_out[0] : 1.0f);
+    const float scale = !valid ? 0.0f : (reduction == 1 ? (nv > 0 ? g / static_cast<float>(nv) : 0.0f) : g);
+    const int64_t yl = (valid && y >= v0 && y < v0 + Vs) ? y - v0 : -1;
+    const dev::Cap cap{SOFTCAP ? 2.0f * kLog2e / softcap : 0.0f, softcap};
+    char *rowp = static_cast<char *>(logits) + row * ld * EL::bytes;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rowp, 0, static_cast<uint32_t>(nvec) * 16u,
+                                                                        0x00020000);
+    const int v_first = part * 256 * PER + threadIdx.x;
+    if (scale == 0.0f) {
+        // ignored rows (and a zero upstream gradient): zeros, nothing to read
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){0u, 0u, 0u, 0u}, rs, (v_first + u * 256) * 16, 0, 2);
+        return;
+    }
+    const float ascale = fabsf(scale);
+    const bool negate = scale < 0.0f;
+    const float lseL = lse[row] * kLog2e - log2f(ascale);
+    const float epsV = SMOOTH ? eps / static_cast<float>(V) * ascale : 0.0f;
+    const float capk = -2.0f * softcap * kLog2e, capb2 = (softcap - lse[row]) * kLog2e + log2f(ascale);
+    u32x4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (v_first + u * 256) * 16, 0, 2);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int vi = v_first + u * 256;
+        float gv[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const float x = EL::get(v[u], k);
+            if constexpr (SOFTCAP) {
+                const float r = cap.r_of(x);
+                const float pp = dev::exp2_fast(fmaf(r, capk, capb2));   // |s| p_j
+                gv[k] = (SMOOTH ? pp - epsV : pp) * dev::Cap::chain_of_r(r);
+            } else {
+                const float pp = dev::exp2_fast(fmaf(x, kLog2e, -lseL));
+                gv[k] = SMOOTH ? pp - epsV : pp;
+            }
+        }
+        if (yl >= 0 && yl / E == vi) {
+            // the target: s (p_y - (1 - eps) - eps / V) with p_y - 1 = -(1 - p_y)
+            const int k = static_cast<int>(yl % E);
+            float gy = ascale * (eps - q[row] - (SMOOTH ? eps / static_cast<float>(V) : 0.0f));
+            if constexpr (SOFTCAP) gy *= dev::Cap::chain_of_r(cap.r_of(EL::get(v[u], k)));
+#pragma unroll
+            for (int kk = 0; kk < E; ++kk)
+                if (kk == k) gv[kk] = gy;
+        }
+        if (negate) {
+#pragma unroll
+            for (int k = 0; k < E; ++k) gv[k] = -gv[k];
+        }
+        // lanes past the row are outside the descriptor: dropped
+        __builtin_amdgcn_raw_buffer_store_b128(EL::pack(gv), rs, vi * 16, 0, 2);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ce_stats(const void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n,
+                           int64_t Vs, int64_t v0, int64_t ignore_index, float softcap, float *stats,
+                           hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(n)), block(kStatsThreads);
+    const bool sc = softcap > 0.0f;
+    if (is_bf16) {
+        if (sc) hipLaunchKernelGGL((ce_stats_kernel<true, true>), grid, block, 0, st, logits, ld, Vs, v0, labels, ignore_index, softcap, stats);
+        else hipLaunchKernelGGL((ce_stats_kernel<true, false>), grid, block, 0, st, logits, ld, Vs, v0, labels, ignore_index, softcap, stats);
+    } else {
+        if (sc) hipLaunchKernelGGL((ce_stats_kernel<false, true>), grid, block, 0, st, logits, ld, Vs, v0, labels, ignore_index, softcap, stats);
+        else hipLaunchKernelGGL((ce_stats_kernel<false, false>), grid, block, 0, st, logits, ld, Vs, v0, labels, ignore_index, softcap, stats);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ce_combine(const float *stats, int64_t shards, const int64_t *labels,
+                             int64_t n, int64_t V, int64_t ignore_index, float eps, int reduction, float *lse,
+                             float *q, float *loss_tok, float *loss_out, float *logp, float *ent,
+                             int64_t *argmax_out, int64_t *counts, hipStream_t st) {
+    hipError_t e;
+    // counts {n_valid, 0, n_bad}; n_correct is added below
+    if ((e = launch_ce_count(labels, n, V, ignore_index, counts, nullptr, loss_out, st)) != hipSuccess) return e;
+    if (n > 0) {
+        const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
+        hipLaunchKernelGGL(ce_combine_kernel, grid, block, 0, st, stats, shards, labels, n, V, ignore_index, eps,
+                           lse, q, loss_tok, logp, ent, argmax_out, counts);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (loss_out) return launch_loss_fold(loss_tok, n, counts, reduction, loss_out, st);
+    return hipSuccess;
+}
+
+hipError_t launch_ce_grad(void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n, int64_t Vs,
+                          int64_t v0, int64_t V, int64_t ignore_index, float eps, float softcap, int reduction,
+                          const float *grad_out, const float *lse, const float *q, const int64_t *counts,
+                          hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int E = is_bf16 ? 8 : 4;
+    const int64_t nvec = Vs / E;
+    const int bpr = static_cast<int>((nvec + 256 * 4 - 1) / (256 * 4));
+    const dim3 grid(static_cast<unsigned>(n * bpr)), block(256);
+    const bool sc = softcap > 0.0f, sm = eps != 0.0f;
+#define LCE_GRAD(B, S, M)                                                                                        \
+    hipLaunchKernelGGL((ce_grad_kernel<B, S, M>), grid, block, 0, st, logits, ld, Vs, v0, V, labels, ignore_index, \
+                       eps, softcap, reduction, grad_out, lse, q, counts, bpr)
+    if (is_bf16) {
+        if (sc) { if (sm) LCE_GRAD(true, true, true); else LCE_GRAD(true, true, false); }
+        else { if (sm) LCE_GRAD(true, false, true); else LCE_GRAD(true, false, false); }
+    } else {
+        if (sc) { if (sm) LCE_GRAD(false, true, true); else LCE_GRAD(false, true, false); }
+        else { if (sm) LCE_GRAD(false, false, true); else LCE_GRAD(false, false, false); }
+    }
+#undef LCE_GRAD
+    return hipGetLastError();
+}
+
+}  // namespace lce

@@ -195,6 +195,12 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
+hipError_t launch_loss_fold(const float *loss_tok, int64_t n, const int64_t *counts, int reduction, float *loss_out,
+                            hipStream_t st) {
+    hipLaunchKernelGGL(loss_fold_kernel, dim3(1), dim3(1024), 0, st, loss_tok, n, counts, reduction, loss_out);
+    return hipGetLastError();
+}
+
 int64_t flce_default_group_chunks(int64_t n, int64_t H, int64_t V, int64_t chunk) {
     const int64_t C = chunk < n ? chunk : (n > 0 ? n : 1);
     const int64_t nchunks = n > 0 ? (n + C - 1) / C : 1;
@@ -302,11 +308,7 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             hipSuccess)
             return e;
     }
-    if (f.loss_out) {
-        hipLaunchKernelGGL(loss_fold_kernel, dim3(1), dim3(1024), 0, st, f.loss_tok, f.n, f.counts, f.reduction,
-                           f.loss_out);
-        return hipGetLastError();
-    }
+    if (f.loss_out) return launch_loss_fold(f.loss_tok, f.n, f.counts, f.reduction, f.loss_out, st);
     return hipSuccess;
 }
 

@@ -128,6 +128,90 @@ lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const 
                       "lce_ce_argmax launch");
 }
 
+// shared checks of a logits shard [n, Vs] with row stride ld
+static lce_status check_shard(const char *fn, const void *logits, int64_t ld, lce_dtype dtype, const int64_t *labels,
+                              int64_t n, int64_t Vs, int64_t v0) {
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "%s: n must be >= 0 (got %lld)", fn, (long long)n);
+    if (Vs < 1) return fail(LCE_ERR_INVALID_ARG, "%s: the shard width must be >= 1 (got %lld)", fn, (long long)Vs);
+    if (v0 < 0) return fail(LCE_ERR_INVALID_ARG, "%s: v_offset must be >= 0 (got %lld)", fn, (long long)v0);
+    if (ld < Vs) return fail(LCE_ERR_INVALID_ARG, "%s: ld (%lld) must be >= the shard width (%lld)", fn,
+                             (long long)ld, (long long)Vs);
+    if (dtype != LCE_F32 && dtype != LCE_BF16) return fail(LCE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    if (n > 0 && (!logits || !labels)) return fail(LCE_ERR_INVALID_ARG, "%s: logits and labels are required", fn);
+    const int64_t E = dtype == LCE_BF16 ? 8 : 4;
+    if (Vs % E != 0 || ld % E != 0 || (logits && !is_aligned(logits, 16)))
+        return fail(LCE_ERR_UNSUPPORTED,
+                    "%s: requires 16-byte rows (shard width and ld multiples of %lld elements, 16-byte aligned logits)",
+                    fn, (long long)E);
+    if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "%s: n > 2^31-1 rows is not supported", fn);
+    if (v0 + Vs > 0x7fffffffLL || Vs * (dtype == LCE_BF16 ? 2 : 4) >= (1ll << 32))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: vocabulary indexes must fit 31 bits and a shard row 4 GiB", fn);
+    return LCE_OK;
+}
+
+size_t lce_ce_stats_bytes(int64_t n) { return n < 0 ? 0 : static_cast<size_t>(n) * lce::kStatsFloats * sizeof(float); }
+
+lce_status lce_ce_stats(const void *logits, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                        int64_t shard_V, int64_t v_offset, int64_t ignore_index, float softcap, float *stats,
+                        hipStream_t stream) {
+    const char *fn = "lce_ce_stats";
+    lce_status st = check_shard(fn, logits, ld, dtype, labels, n, shard_V, v_offset);
+    if (st != LCE_OK) return st;
+    if (!(softcap >= 0.0f) || isinf(softcap))
+        return fail(LCE_ERR_INVALID_ARG, "%s: softcap must be finite and >= 0 (got %g)", fn, (double)softcap);
+    if (n > 0 && !stats) return fail(LCE_ERR_INVALID_ARG, "%s: stats is required", fn);
+    return hip_status(lce::launch_ce_stats(logits, ld, dtype == LCE_BF16, labels, n, shard_V, v_offset, ignore_index,
+                                           softcap, stats, stream),
+                      "lce_ce_stats launch");
+}
+
+lce_status lce_ce_combine(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
+                          int64_t ignore_index, float label_smoothing, lce_reduction reduction, float *lse,
+                          float *one_minus_py, float *loss_tok, float *loss_out, float *logprob, float *entropy,
+                          int64_t *argmax_out, int64_t *counts, hipStream_t stream) {
+    const char *fn = "lce_ce_combine";
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "%s: n must be >= 0 (got %lld)", fn, (long long)n);
+    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "%s: V must be >= 1 (got %lld)", fn, (long long)V);
+    if (shards < 1) return fail(LCE_ERR_INVALID_ARG, "%s: shards must be >= 1 (got %lld)", fn, (long long)shards);
+    if (reduction != LCE_RED_NONE && reduction != LCE_RED_MEAN && reduction != LCE_RED_SUM)
+        return fail(LCE_ERR_INVALID_ARG, "%s: unknown reduction %d", fn, (int)reduction);
+    if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
+        return fail(LCE_ERR_INVALID_ARG, "%s: label_smoothing must be in [0, 1] (got %g)", fn, (double)label_smoothing);
+    if (!counts) return fail(LCE_ERR_INVALID_ARG, "%s: counts is required", fn);
+    if (n > 0 && (!stats || !labels || !lse))
+        return fail(LCE_ERR_INVALID_ARG, "%s: stats, labels and lse are required", fn);
+    if (n > 0 && loss_out && !loss_tok) return fail(LCE_ERR_INVALID_ARG, "%s: loss_out needs loss_tok", fn);
+    if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "%s: n > 2^31-1 rows is not supported", fn);
+    return hip_status(lce::launch_ce_combine(stats, shards, labels, n, V, ignore_index, label_smoothing,
+                                             static_cast<int>(reduction), lse, one_minus_py, loss_tok, loss_out,
+                                             logprob, entropy, argmax_out, counts, stream),
+                      "lce_ce_combine launch");
+}
+
+lce_status lce_ce_grad(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                       int64_t shard_V, int64_t v_offset, int64_t V, int64_t ignore_index, float label_smoothing,
+                       float softcap, lce_reduction reduction, const float *grad_out, const float *lse,
+                       const float *one_minus_py, const int64_t *counts, hipStream_t stream) {
+    const char *fn = "lce_ce_grad";
+    lce_status st = check_shard(fn, logits_inout, ld, dtype, labels, n, shard_V, v_offset);
+    if (st != LCE_OK) return st;
+    if (V < 1 || v_offset + shard_V > V)
+        return fail(LCE_ERR_INVALID_ARG, "%s: the shard [%lld, %lld) must lie inside [0, V = %lld)", fn,
+                    (long long)v_offset, (long long)(v_offset + shard_V), (long long)V);
+    if (reduction != LCE_RED_NONE && reduction != LCE_RED_MEAN && reduction != LCE_RED_SUM)
+        return fail(LCE_ERR_INVALID_ARG, "%s: unknown reduction %d", fn, (int)reduction);
+    if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
+        return fail(LCE_ERR_INVALID_ARG, "%s: label_smoothing must be in [0, 1] (got %g)", fn, (double)label_smoothing);
+    if (!(softcap >= 0.0f) || isinf(softcap))
+        return fail(LCE_ERR_INVALID_ARG, "%s: softcap must be finite and >= 0 (got %g)", fn, (double)softcap);
+    if (n > 0 && (!lse || !one_minus_py || !counts))
+        return fail(LCE_ERR_INVALID_ARG, "%s: lse, one_minus_py and counts are required", fn);
+    return hip_status(lce::launch_ce_grad(logits_inout, ld, dtype == LCE_BF16, labels, n, shard_V, v_offset, V,
+                                          ignore_index, label_smoothing, softcap, static_cast<int>(reduction),
+                                          grad_out, lse, one_minus_py, counts, stream),
+                      "lce_ce_grad launch");
+}
+
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens) {
     if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1) return 0;
     return lce::flce_layout(n, H, V, chunk_tokens, lce::flce_default_group_chunks(n, H, V, chunk_tokens)).bytes;

@@ -59,6 +59,29 @@ bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, i
 hipError_t launch_ce_count(const int64_t *labels, int64_t n, int64_t V, int64_t ignore_index, int64_t *counts,
                            unsigned *ticket, float *loss_out, hipStream_t stream);
 
+// loss_out = mean (over counts[0]) or sum of loss_tok[0, n), 0 for 'none'; one
+// workgroup, fixed-order fp64 sum.
+hipError_t launch_loss_fold(const float *loss_tok, int64_t n, const int64_t *counts, int reduction, float *loss_out,
+                            hipStream_t stream);
+
+// ---- split cross-entropy: shard statistics, combine, gradient ----------------
+
+// One stats record per row and shard: 8 floats (max z, sum of e^{z-max} without
+// the target, sum of e^{z-max} z, sum z, argmax value, global argmax index as
+// int bits, target z, target-present flag).
+constexpr int kStatsFloats = 8;
+hipError_t launch_ce_stats(const void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n,
+                           int64_t Vs, int64_t v0, int64_t ignore_index, float softcap, float *stats,
+                           hipStream_t stream);
+hipError_t launch_ce_combine(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
+                             int64_t ignore_index, float eps, int reduction, float *lse, float *q, float *loss_tok,
+                             float *loss_out, float *logp, float *ent, int64_t *argmax_out, int64_t *counts,
+                             hipStream_t stream);
+hipError_t launch_ce_grad(void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n, int64_t Vs,
+                          int64_t v0, int64_t V, int64_t ignore_index, float eps, float softcap, int reduction,
+                          const float *grad_out, const float *lse, const float *q, const int64_t *counts,
+                          hipStream_t stream);
+
 // ---- fused linear cross-entropy ----------------------------------------------
 
 // Compute units of the current device (cached per device).
