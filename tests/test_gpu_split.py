@@ -190,3 +190,38 @@ def test_split_full_size(tp):
     o = oracle.ce(x, y, V=w.V, want_grad=False)
     check_loss(float(rows.loss_out.cpu()[0]), o["loss_out"], "loss_out")
     assert int(rows.counts.cpu()[1]) == int(o["counts"][1])
+
+
+@pytest.mark.parametrize("red", ["mean", "sum", "none"])
+def test_deferred_autograd(red):
+    """The autograd form: forward is a read-only sweep, backward writes the gradient in place with the
+    upstream gradient it receives; a second backward through the same graph is refused."""
+    rng = np.random.default_rng([9, len(red)])
+    n, V, eps, T = 48, 8192, 0.1, 30.0
+    xb = synth.f32_to_bf16_bits((rng.standard_normal((n, V)) * 4).astype(np.float32))
+    y = _labels(rng, n, V)
+    x = to_dev(xb).clone().requires_grad_()
+    lab = torch.from_numpy(y).to(DEV)
+    loss, logp, ent, am, counts = lce.cross_entropy(x, lab, label_smoothing=eps, softcap=T, reduction=red)
+    before = from_dev(x.detach())
+    assert np.array_equal(before, xb), "the forward must not write the logits"
+    if red == "none":
+        w = rng.normal(size=n)
+        (loss * torch.from_numpy(w).to(DEV, torch.float32)).sum().backward(retain_graph=True)
+        grad_out = w
+    else:
+        (loss * 0.5).backward(retain_graph=True)
+        grad_out = [0.5]
+    assert x.grad is not None and x.grad.dtype == torch.bfloat16
+    orc = oracle.default()
+    o = orc.ce(xb, y, V=V, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out)
+    got = loss.detach().cpu().numpy()
+    check_loss(got if red == "none" else float(got), o["loss_tok"] if red == "none" else o["loss_out"], "loss")
+    st = orc.row_stats(xb, y, V=V, softcap=T)
+    check_loss(logp.cpu().numpy(), st["logp"], "logprob")
+    assert np.array_equal(am.cpu().numpy(), o["argmax"])
+    scales = row_scales(red, grad_out, y, V)
+    n_allow = check_bf16_grad(from_dev(x.grad), o["grad"], orc, allow=smoothing_allowance(scales, eps, V))
+    assert n_allow <= max(4, n * V // 1000)
+    with pytest.raises(RuntimeError, match="second time"):
+        (loss.sum() if red == "none" else loss).backward()

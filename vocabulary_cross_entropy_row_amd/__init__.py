@@ -243,6 +243,73 @@ def lce_ce_grad(shard, labels, V: int, rows: SplitRows, *, v_offset: int = 0, ig
                              _stream(stream)))
 
 
+def cross_entropy(logits, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0, softcap: float = 0.0,
+                  reduction: str = "mean"):
+    """Autograd form of the split path with the gradient deferred to backward.
+
+    The forward is one read-only sweep (lce_ce_stats, lce_ce_combine); backward
+    writes the gradient over ``logits`` in place with the upstream gradient it
+    receives (lce_ce_grad) and returns that buffer, so the gradient has the
+    logits' dtype and ``logits`` must not be used after backward.  A second
+    backward through the same graph raises, since the logits are gone.
+    Returns (loss, logprob, entropy, argmax, counts): loss is the reduced fp32
+    scalar, or fp32 [n] for reduction "none"; the rest carry no gradient.
+    """
+    return _DeferredCE.apply(logits, labels, int(ignore_index), float(label_smoothing), float(softcap),
+                             reduction)
+
+
+def _deferred_ce_class():
+    import torch
+
+    class DeferredCE(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, logits, labels, ignore_index, eps, softcap, reduction):
+            if reduction not in REDUCTIONS:
+                raise ValueError(f"unknown reduction {reduction!r}")
+            V = logits.shape[-1]
+            stats = lce_ce_stats(logits, labels, ignore_index=ignore_index, softcap=softcap)
+            rows = lce_ce_combine(stats, labels, V, ignore_index=ignore_index, label_smoothing=eps,
+                                  reduction=reduction)
+            ctx.save_for_backward(logits, labels)
+            ctx.rows = rows
+            ctx.args = (V, ignore_index, eps, softcap, reduction)
+            ctx.consumed = False
+            loss = rows.loss_tok if reduction == "none" else rows.loss_out.view(())
+            ctx.mark_non_differentiable(rows.logprob, rows.entropy, rows.argmax, rows.counts)
+            return loss, rows.logprob, rows.entropy, rows.argmax, rows.counts
+
+        @staticmethod
+        def backward(ctx, g, *_unused):
+            if ctx.consumed:
+                raise RuntimeError("cross_entropy: the logits buffer already holds its gradient; "
+                                   "backward through this graph a second time is not supported")
+            logits, labels = ctx.saved_tensors
+            V, ignore_index, eps, softcap, reduction = ctx.args
+            grad_out = g.detach().to(torch.float32).reshape(-1).contiguous()
+            lce_ce_grad(logits, labels, V, ctx.rows, ignore_index=ignore_index, label_smoothing=eps,
+                        softcap=softcap, reduction=reduction, grad_out=grad_out)
+            ctx.consumed = True
+            return logits, None, None, None, None, None
+
+    return DeferredCE
+
+
+class _LazyFunction:
+    """Builds the autograd class on first use, so importing this module does not import torch."""
+
+    def __init__(self, make):
+        self._make, self._cls = make, None
+
+    def apply(self, *args):
+        if self._cls is None:
+            self._cls = self._make()
+        return self._cls.apply(*args)
+
+
+_DeferredCE = _LazyFunction(_deferred_ce_class)
+
+
 def lce_flce_workspace_bytes(n: int, H: int, V: int, chunk_tokens: int) -> int:
     return int(lib().lce_flce_workspace_bytes(int(n), int(H), int(V), int(chunk_tokens)))
 
