@@ -38,6 +38,8 @@ METRIC = "CE fwd+bwd ms and HBM GB/s (% peak), bf16 logits 2048×131072, 1 GPU"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 FLCE_METRIC = "FLCE fwd+bwd ms and bf16 MFMA TFLOP/s (% peak), hidden 4096×6656, weight 202048×6656, 1 GPU"
+RESIDENT_METRIC = ("tile-resident FLCE (logits never stored) fwd+bwd ms and bf16 MFMA TFLOP/s at 6·N·H·V "
+                   "(% peak), hidden 4096×6656, weight 202048×6656, 1 GPU")
 CSRC = os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -55,8 +57,9 @@ def parse():
     ap.add_argument("--workload", default="ce_bf16_2048x131072")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--collect-profiles", action="store_true")
-    ap.add_argument("--path", choices=["fused", "split"], default="fused",
-                    help="split: stats / combine / gradient as separate calls over --tp vocabulary shards")
+    ap.add_argument("--path", choices=["fused", "split", "resident"], default="fused",
+                    help="split: stats / combine / gradient as separate calls over --tp vocabulary shards; "
+                         "resident: the tile-resident fused linear forward + backward (fused-linear workloads)")
     ap.add_argument("--tp", type=int, default=1, help="vocabulary shards of the split path (one GPU)")
     return ap.parse_args()
 
@@ -258,12 +261,28 @@ def bench_flce(args, w) -> int:
     wsb = lce.lce_flce_workspace_bytes(w.n, w.H, w.V, w.chunk)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    resident = args.path == "resident"
+    if resident:
+        f = lambda: torch.empty(w.n, dtype=torch.float32, device=dev)  # noqa: E731
+        rows = lce.SplitRows(f(), f(), loss_tok, loss_out, f(), f(), torch.empty(w.n, dtype=torch.int64, device=dev),
+                             counts)
+        stats_ws = torch.empty(lce.lce_flce_stats_bytes(w.n, w.V), dtype=torch.uint8, device=dev)
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    def step():
-        lce.lce_flce_fwd_bwd(hidden, weight, labels, label_smoothing=w.label_smoothing, softcap=w.softcap,
-                             reduction=w.reduction, grad_out=grad_out, chunk_tokens=w.chunk, loss_tok=loss_tok,
-                             loss_out=loss_out, grad_hidden=grad_hidden, grad_weight=grad_weight, counts=counts,
-                             workspace=ws, stream=stream)
+    def step(i=None):
+        if not resident:
+            lce.lce_flce_fwd_bwd(hidden, weight, labels, label_smoothing=w.label_smoothing, softcap=w.softcap,
+                                 reduction=w.reduction, grad_out=grad_out, chunk_tokens=w.chunk, loss_tok=loss_tok,
+                                 loss_out=loss_out, grad_hidden=grad_hidden, grad_weight=grad_weight, counts=counts,
+                                 workspace=ws, stream=stream)
+            return
+        lce.lce_flce_forward(hidden, weight, labels, label_smoothing=w.label_smoothing, softcap=w.softcap,
+                             reduction=w.reduction, workspace=stats_ws, out=rows, stream=stream)
+        if i is not None:
+            mid[i].record(stream)
+        lce.lce_flce_backward(hidden, weight, labels, rows, label_smoothing=w.label_smoothing, softcap=w.softcap,
+                              reduction=w.reduction, grad_out=grad_out, chunk_tokens=w.chunk, grad_hidden=grad_hidden,
+                              grad_weight=grad_weight, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -272,7 +291,7 @@ def bench_flce(args, w) -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        step()
+        step(i)
         ev[i][1].record(stream)
         print(f"# step {i} issued", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -285,10 +304,10 @@ def bench_flce(args, w) -> int:
     achieved = flops / (call_ms * 1e-3) / 1e12
     prof = read_profile(w.name)
     traffic = None
-    if prof and prof.get("kernel_source_sha256_16") == kernel_source_hash(w.name):
+    if not resident and prof and prof.get("kernel_source_sha256_16") == kernel_source_hash(w.name):
         traffic = int(prof["traffic_bytes_per_dispatch"])
     out = {
-        "metric": FLCE_METRIC,
+        "metric": RESIDENT_METRIC if resident else FLCE_METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -306,11 +325,17 @@ def bench_flce(args, w) -> int:
                    "workspace_bytes": wsb, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "lce_flce_fwd_bwd call (all its GEMM, CE and transpose launches), HIP events per call",
+                     "kernel": ("lce_flce_forward + lce_flce_backward" if resident else "lce_flce_fwd_bwd call") +
+                               " (all GEMM, CE and transpose launches), HIP events per step",
                      "call_ms_mean": round(call_ms, 4), "call_ms_min": round(min(per_call_ms), 4),
                      "call_ms_max": round(max(per_call_ms), 4), "algorithmic_flops": flops},
         "cpu_baseline": None,
     }
+    if resident:
+        fwd_ms = float(np.mean([a.elapsed_time(m) for (a, _), m in zip(ev, mid)]))
+        out["phase_ms"] = {"forward": round(fwd_ms, 4), "backward": round(call_ms - fwd_ms, 4)}
+        out["executed_flops"] = 8 * w.n * w.H * w.V   # the backward forms the logits again
+        out["executed_tflops"] = round(8 * w.n * w.H * w.V / (call_ms * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         nthr = len(os.sched_getaffinity(0))
         if os.environ.get("OMP_NUM_THREADS"):

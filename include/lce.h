@@ -235,6 +235,57 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Tile-resident fused linear cross-entropy [P5 Summary; Details/Softcap;
+ * Memory]: the logits Z = hidden * weight^T are formed tile by tile (256 x 256,
+ * fp32 from bf16 MFMA) and never stored.  The forward reduces every tile to
+ * per-row statistics; the backward forms the same tiles again and keeps only
+ * the gradient, so the upstream gradient can arrive after the forward.  The
+ * row operation is that of lce_ce_fwd_bwd applied to the fp32 logits (not the
+ * bf16-rounded logits of lce_flce_fwd_bwd); the mean's denominator counts every
+ * token's label.  H and V must be multiples of 8, hidden and weight 16-byte
+ * aligned (LCE_ERR_UNSUPPORTED otherwise).
+ */
+
+/* Bytes of workspace lce_flce_forward needs: n * ceil(V / 256) records of 32 bytes. */
+size_t lce_flce_stats_bytes(int64_t n, int64_t V);
+
+/*
+ * Forward [P5 Summary: loss and token accuracy without the logits]:
+ *   hidden, weight, labels  as for lce_flce_fwd_bwd.
+ *   loss_tok      fp32 [n], required; loss_out fp32 scalar or NULL (mean over
+ *                 valid labels or sum; 0 for LCE_RED_NONE).
+ *   lse           fp32 [n], required: log sum_j exp(z_j).
+ *   one_minus_py  fp32 [n], required: 1 - p_y (0 for ignored rows), kept for
+ *                 the backward.
+ *   logprob, entropy  fp32 [n] or NULL: log p_y (0 for ignored rows) and
+ *                 -sum_j p_j log p_j of every row.
+ *   argmax_out    int64 [n] or NULL: first argmax of the raw fp32 logits.
+ *   counts        int64 [3], required: {n_valid, n_correct, n_bad}; token
+ *                 accuracy = n_correct / n_valid.
+ *   workspace     device, 256-byte aligned, at least lce_flce_stats_bytes(n, V)
+ *                 bytes (LCE_ERR_INVALID_ARG otherwise); clobbered.
+ */
+lce_status lce_flce_forward(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
+                            int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                            lce_reduction reduction, float *loss_tok, float *loss_out, float *lse, float *one_minus_py,
+                            float *logprob, float *entropy, int64_t *argmax_out, int64_t *counts, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward: grad_hidden bf16 [n, H] and grad_weight fp32 [V, H] (overwritten)
+ * from lse, one_minus_py and counts of lce_flce_forward on the same inputs and
+ * options, with the upstream gradient grad_out (as for lce_ce_fwd_bwd).  Tokens
+ * go in chunks of chunk_tokens; the workspace is that of lce_flce_fwd_bwd
+ * (lce_flce_workspace_bytes[_grouped], the same group rule).  Nothing of the
+ * forward's outputs is modified.
+ */
+lce_status lce_flce_backward(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
+                             int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                             lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, const float *lse,
+                             const float *one_minus_py, const int64_t *counts, void *grad_hidden, float *grad_weight,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Text of the most recent error on the calling thread ("" if none).  Valid
  * until the next lce_* call on the same thread.
  */

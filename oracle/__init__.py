@@ -254,6 +254,53 @@ def flce_sampled(orc: "Oracle", hidden: np.ndarray, weight: np.ndarray, labels: 
             "grad_hidden": gh, "grad_weight": gw, "zmax": zmax}
 
 
+def flce_rows(orc: "Oracle", hidden: np.ndarray, weight: np.ndarray, labels: np.ndarray, *, tokens=None,
+              ignore_index: int = -100, label_smoothing: float = 0.0, softcap: float = 0.0,
+              grad_scale: float | None = None, block: int = 256, nthreads: int = 0) -> dict:
+    """Per-token row outputs of the fused linear cross-entropy (Liger-Kernel PR "Add Liger Kernel
+    support for Muse Glimmer", Summary: loss and token accuracy without the logits; labs-molt PR
+    "Enable Liger layers": log-probabilities and entropy): the logits Z = H W^T of the chosen tokens
+    in fp64 by a library matmul (bf16 inputs are exact in fp64), then the oracle's row routines on them.
+
+    Returns, per token: loss_tok (reduction 'none', with the given smoothing), argmax (first index of
+    the raw logits), lse, logp, entropy, and gap = the largest raw logit minus the largest at any other
+    index; with grad_scale s, also grad_hidden = G W for these tokens, G = s (p - t) dz/dx being the
+    row routine's gradient (s = the upstream gradient over the mean's denominator, or as given).
+    """
+    hidden = np.ascontiguousarray(hidden, dtype=np.uint16)
+    weight = np.ascontiguousarray(weight, dtype=np.uint16)
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    n = hidden.shape[0]
+    V = weight.shape[0]
+    tokens = np.arange(n) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    h64 = (hidden.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w64 = (weight.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = {k: np.zeros(tokens.size) for k in ("loss_tok", "lse", "logp", "entropy", "gap")}
+    out["argmax"] = np.zeros(tokens.size, dtype=np.int64)
+    if grad_scale is not None:
+        out["grad_hidden"] = np.zeros((tokens.size, hidden.shape[1]))
+    for b0 in range(0, tokens.size, block):
+        sel = tokens[b0:b0 + block]
+        z = h64[sel] @ w64.T
+        y = labels[sel]
+        # reduction 'sum' with the upstream gradient set to the scale: per-token losses and s (p - t)
+        o = orc.ce(z, y, V=V, ignore_index=ignore_index, label_smoothing=label_smoothing, softcap=softcap,
+                   reduction="sum", grad_out=[1.0 if grad_scale is None else grad_scale],
+                   want_grad=grad_scale is not None, nthreads=nthreads)
+        if grad_scale is not None:
+            out["grad_hidden"][b0:b0 + block] = o["grad"] @ w64
+        st = orc.row_stats(z, y, V=V, ignore_index=ignore_index, softcap=softcap, nthreads=nthreads)
+        out["loss_tok"][b0:b0 + block] = o["loss_tok"]
+        out["argmax"][b0:b0 + block] = o["argmax"]
+        for k in ("lse", "logp", "entropy"):
+            out[k][b0:b0 + block] = st[k]
+        top = z[np.arange(sel.size), o["argmax"]]
+        rest = z.copy()
+        rest[np.arange(sel.size), o["argmax"]] = -np.inf
+        out["gap"][b0:b0 + block] = top - rest.max(axis=1) if V > 1 else np.inf
+    return out
+
+
 _default: Oracle | None = None
 
 

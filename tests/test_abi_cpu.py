@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_workspace():
-    assert lce.lib().lce_abi_version() == 1
+    assert lce.lib().lce_abi_version() == lce.ABI_VERSION == 2
     assert lce.lce_ce_workspace_bytes(2048, 131072) > 0
 
 
@@ -202,3 +202,66 @@ def test_combine_and_grad_reject_bad_arguments():
                        FAKE, None)
     assert st == lce.LCE_ERR_INVALID_ARG and "lse" in lce.lce_last_error()
     assert lce.lib().lce_ce_stats_bytes(10) == 320
+
+
+def call_flce_forward(**over):
+    a = dict(hidden=FAKE, weight=FAKE, labels=FAKE, n=4, H=8, V=16, ignore_index=-100, eps=0.0, softcap=0.0,
+             red=lce.LCE_RED_MEAN, loss_tok=FAKE, loss_out=None, lse=FAKE, q=FAKE, logp=None, ent=None, argmax=None,
+             counts=FAKE, ws=ALIGNED_WS, wsb=1 << 20, stream=None)
+    a.update(over)
+    st = lce.lib().lce_flce_forward(a["hidden"], a["weight"], a["labels"], a["n"], a["H"], a["V"], a["ignore_index"],
+                                    a["eps"], a["softcap"], a["red"], a["loss_tok"], a["loss_out"], a["lse"], a["q"],
+                                    a["logp"], a["ent"], a["argmax"], a["counts"], a["ws"], a["wsb"], a["stream"])
+    return st, lce.lce_last_error()
+
+
+def call_flce_backward(**over):
+    a = dict(hidden=FAKE, weight=FAKE, labels=FAKE, n=4, H=8, V=16, ignore_index=-100, eps=0.0, softcap=0.0,
+             red=lce.LCE_RED_MEAN, grad_out=None, chunk=4, lse=FAKE, q=FAKE, counts=FAKE, gh=FAKE, gw=FAKE,
+             ws=ALIGNED_WS, wsb=1 << 30, stream=None)
+    a.update(over)
+    st = lce.lib().lce_flce_backward(a["hidden"], a["weight"], a["labels"], a["n"], a["H"], a["V"],
+                                     a["ignore_index"], a["eps"], a["softcap"], a["red"], a["grad_out"], a["chunk"],
+                                     a["lse"], a["q"], a["counts"], a["gh"], a["gw"], a["ws"], a["wsb"], a["stream"])
+    return st, lce.lce_last_error()
+
+
+@pytest.mark.parametrize("over,needle,status", [
+    (dict(n=-1), "n must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(H=0), "H must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(V=0), "V must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(red=5), "reduction", lce.LCE_ERR_INVALID_ARG),
+    (dict(eps=1.5), "label_smoothing", lce.LCE_ERR_INVALID_ARG),
+    (dict(softcap=-1.0), "softcap", lce.LCE_ERR_INVALID_ARG),
+    (dict(weight=None), "weight", lce.LCE_ERR_INVALID_ARG),
+    (dict(hidden=None), "hidden", lce.LCE_ERR_INVALID_ARG),
+    (dict(counts=None), "counts", lce.LCE_ERR_INVALID_ARG),
+    (dict(lse=None), "lse", lce.LCE_ERR_INVALID_ARG),
+    (dict(wsb=100), "workspace_bytes", lce.LCE_ERR_INVALID_ARG),
+    (dict(ws=ALIGNED_WS + 16), "256-byte", lce.LCE_ERR_INVALID_ARG),
+    (dict(H=12), "multiples of 8", lce.LCE_ERR_UNSUPPORTED),
+    (dict(hidden=FAKE + 8), "16-byte", lce.LCE_ERR_UNSUPPORTED),
+])
+def test_flce_forward_rejects_bad_arguments(over, needle, status):
+    st, msg = call_flce_forward(**over)
+    assert st == status and needle in msg and "lce_flce_forward" in msg
+
+
+@pytest.mark.parametrize("over,needle,status", [
+    (dict(n=-1), "n must be", lce.LCE_ERR_INVALID_ARG),
+    (dict(chunk=0), "chunk_tokens", lce.LCE_ERR_INVALID_ARG),
+    (dict(gw=None), "grad_weight", lce.LCE_ERR_INVALID_ARG),
+    (dict(q=None), "one_minus_py", lce.LCE_ERR_INVALID_ARG),
+    (dict(wsb=100), "workspace_bytes", lce.LCE_ERR_INVALID_ARG),
+    (dict(V=20), "multiples of 8", lce.LCE_ERR_UNSUPPORTED),
+    (dict(gh=FAKE + 2), "16-byte", lce.LCE_ERR_UNSUPPORTED),
+])
+def test_flce_backward_rejects_bad_arguments(over, needle, status):
+    st, msg = call_flce_backward(**over)
+    assert st == status and needle in msg and "lce_flce_backward" in msg
+
+
+def test_flce_stats_bytes():
+    assert lce.lce_flce_stats_bytes(4096, 202048) == 4096 * 790 * 32
+    assert lce.lce_flce_stats_bytes(3, 8) == 3 * 32
+    assert lce.lce_flce_stats_bytes(-1, 8) == 0

@@ -19,6 +19,7 @@ LCE_OK, LCE_ERR_INVALID_ARG, LCE_ERR_UNSUPPORTED, LCE_ERR_HIP = 0, 1, 2, 3
 LCE_F32, LCE_BF16 = 0, 1
 LCE_RED_NONE, LCE_RED_MEAN, LCE_RED_SUM = 0, 1, 2
 REDUCTIONS = {"none": LCE_RED_NONE, "mean": LCE_RED_MEAN, "sum": LCE_RED_SUM}
+ABI_VERSION = 2
 
 _lib = None
 
@@ -68,7 +69,15 @@ def lib() -> ctypes.CDLL:
     L.lce_flce_fwd_bwd.restype = ctypes.c_int
     L.lce_flce_fwd_bwd.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, i64, p, p, p, p, p, p,
                                    ctypes.c_size_t, p]
-    if L.lce_abi_version() != 1:
+    L.lce_flce_stats_bytes.restype = ctypes.c_size_t
+    L.lce_flce_stats_bytes.argtypes = [i64, i64]
+    L.lce_flce_forward.restype = ctypes.c_int
+    L.lce_flce_forward.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, p, p, p, p, p, p, p, p,
+                                   ctypes.c_size_t, p]
+    L.lce_flce_backward.restype = ctypes.c_int
+    L.lce_flce_backward.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, i64, p, p, p, p, p, p,
+                                    ctypes.c_size_t, p]
+    if L.lce_abi_version() != ABI_VERSION:
         raise ImportError("liblce.so ABI version mismatch; rebuild it")
     _lib = L
     return L
@@ -364,3 +373,113 @@ def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st)
     return FLCEResult(loss_tok, loss_out, grad_hidden, grad_weight, counts)
+
+
+# ---- tile-resident fused linear cross-entropy: forward stats, deferred backward ---------------
+
+def lce_flce_stats_bytes(n: int, V: int) -> int:
+    return int(lib().lce_flce_stats_bytes(int(n), int(V)))
+
+
+def _check_flce_operands(hidden, weight):
+    import torch
+    for t, nm in ((hidden, "hidden"), (weight, "weight")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous 2-D bfloat16 tensor")
+
+
+def lce_flce_forward(hidden, weight, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
+                     softcap: float = 0.0, reduction: str = "mean", workspace=None, out: SplitRows | None = None,
+                     stream=None) -> SplitRows:
+    """Loss, log-sum-exp, 1 - p_y, log p_y, entropy, argmax and counts of the logits hidden weight^T,
+    formed tile by tile and never stored.  ``out`` (optional) supplies the output tensors."""
+    import torch
+    _check_flce_operands(hidden, weight)
+    n, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if out is None:
+        f = lambda: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+        out = SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=dev), f(), f(),
+                        torch.empty(n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
+    if workspace is None:
+        workspace = torch.empty(max(lce_flce_stats_bytes(n, V), 1), dtype=torch.uint8, device=dev)
+    _check(lib().lce_flce_forward(_ptr(hidden), _ptr(weight), _ptr(labels), n, H, V, int(ignore_index),
+                                  float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(out.loss_tok),
+                                  _ptr(out.loss_out), _ptr(out.lse), _ptr(out.one_minus_py), _ptr(out.logprob),
+                                  _ptr(out.entropy), _ptr(out.argmax), _ptr(out.counts), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def lce_flce_backward(hidden, weight, labels, rows: SplitRows, *, ignore_index: int = -100,
+                      label_smoothing: float = 0.0, softcap: float = 0.0, reduction: str = "mean", grad_out=None,
+                      chunk_tokens: int = 1024, grad_hidden=None, grad_weight=None, workspace=None, stream=None):
+    """grad_hidden (bf16 [n, H]) and grad_weight (fp32 [V, H]) from the forward's rows."""
+    import torch
+    _check_flce_operands(hidden, weight)
+    n, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if grad_out is not None and not torch.is_tensor(grad_out):
+        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=dev)
+    elif grad_out is not None and grad_out.dtype != torch.float32:
+        grad_out = grad_out.float()
+    if grad_hidden is None:
+        grad_hidden = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    if grad_weight is None:
+        grad_weight = torch.empty((V, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(lce_flce_workspace_bytes(n, H, V, chunk_tokens), dtype=torch.uint8, device=dev)
+    _check(lib().lce_flce_backward(_ptr(hidden), _ptr(weight), _ptr(labels), n, H, V, int(ignore_index),
+                                   float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
+                                   int(chunk_tokens), _ptr(rows.lse), _ptr(rows.one_minus_py), _ptr(rows.counts),
+                                   _ptr(grad_hidden), _ptr(grad_weight), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return grad_hidden, grad_weight
+
+
+def linear_cross_entropy(hidden, weight, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
+                         softcap: float = 0.0, reduction: str = "mean", chunk_tokens: int = 1024):
+    """Autograd form of the tile-resident fused linear cross-entropy.
+
+    Forward: lce_flce_forward (no logits stored).  Backward: lce_flce_backward with the upstream
+    gradient it receives; grad_weight is accumulated in fp32 and handed to autograd, which casts it
+    to the weight's dtype.  Returns (loss, logprob, entropy, argmax, counts); loss is the reduced fp32
+    scalar, or fp32 [n] for reduction "none"; the rest carry no gradient.
+    """
+    return _DeferredFLCE.apply(hidden, weight, labels, int(ignore_index), float(label_smoothing), float(softcap),
+                               reduction, int(chunk_tokens))
+
+
+def _deferred_flce_class():
+    import torch
+
+    class DeferredFLCE(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, hidden, weight, labels, ignore_index, eps, softcap, reduction, chunk_tokens):
+            if reduction not in REDUCTIONS:
+                raise ValueError(f"unknown reduction {reduction!r}")
+            rows = lce_flce_forward(hidden, weight, labels, ignore_index=ignore_index, label_smoothing=eps,
+                                    softcap=softcap, reduction=reduction)
+            ctx.save_for_backward(hidden, weight, labels)
+            ctx.rows = rows
+            ctx.args = (ignore_index, eps, softcap, reduction, chunk_tokens)
+            loss = rows.loss_tok if reduction == "none" else rows.loss_out.view(())
+            ctx.mark_non_differentiable(rows.logprob, rows.entropy, rows.argmax, rows.counts)
+            return loss, rows.logprob, rows.entropy, rows.argmax, rows.counts
+
+        @staticmethod
+        def backward(ctx, g, *_unused):
+            hidden, weight, labels = ctx.saved_tensors
+            ignore_index, eps, softcap, reduction, chunk_tokens = ctx.args
+            grad_out = g.detach().to(torch.float32).reshape(-1).contiguous()
+            gh, gw = lce_flce_backward(hidden, weight, labels, ctx.rows, ignore_index=ignore_index,
+                                       label_smoothing=eps, softcap=softcap, reduction=reduction, grad_out=grad_out,
+                                       chunk_tokens=chunk_tokens)
+            return gh, gw, None, None, None, None, None, None
+
+    return DeferredFLCE
+
+
+_DeferredFLCE = _LazyFunction(_deferred_flce_class)

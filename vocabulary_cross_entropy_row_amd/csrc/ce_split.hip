@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
 }
 
 // per row over the shards: outputs; n_correct by integer atomics (order-free)
-__global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
+__global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int64_t shards, int64_t shard_stride,
+                                                         int64_t row_stride, const int64_t *labels, int64_t n, int64_t V,
                                                          int64_t ignore_index, float eps, float *lse_out,
                                                          float *q_out, float *loss_tok, float *logp_out,
                                                          float *ent_out, int64_t *argmax_out, int64_t *counts) {
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int
     bool has = false;
     int64_t am = -1;
     for (int64_t k = 0; k < shards; ++k) {
-        const float *r = stats + (k * n + i) * 8;
+        const float *r = stats + (k * shard_stride + i * row_stride) * 8;
         combine(t, r[0], r[1], r[2]);
         t.zs += r[3];
         if (r[4] > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
@@ -215,6 +216,59 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int
     if (loss_tok) loss_tok[i] = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
     if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
     if (ent_out) ent_out[i] = lse - t.e / S;   // -sum p log p = lse - sum p z
+    if (argmax_out) argmax_out[i] = am;
+    if (valid && am == y) __hip_atomic_fetch_add(reinterpret_cast<unsigned long long *>(counts + 1), 1ull,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Many shards per row (one per 256 columns in the tile-resident fused linear
+// path): one wave per row, each lane merges every 64th shard in ascending
+// order, then a butterfly merges the lanes (argmax ties to the smaller index).
+__global__ __launch_bounds__(256) void ce_combine_wide_kernel(const float *stats, int64_t shards,
+                                                              int64_t shard_stride, int64_t row_stride,
+                                                              const int64_t *labels, int64_t n, int64_t V,
+                                                              int64_t ignore_index, float eps, float *lse_out,
+                                                              float *q_out, float *loss_tok, float *logp_out,
+                                                              float *ent_out, int64_t *argmax_out, int64_t *counts) {
+    const int64_t i = blockIdx.x * 4ll + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= n) return;   // uniform over the wave
+    Part t;
+    float zy = 0.0f, has = 0.0f;
+    for (int64_t k = lane; k < shards; k += 64) {
+        const float4 *r = reinterpret_cast<const float4 *>(stats + (k * shard_stride + i * row_stride) * 8);
+        const float4 a = r[0], b = r[1];
+        combine(t, a.x, a.y, a.z);
+        t.zs += a.w;
+        if (b.x > t.amv) {   // this lane's shards ascend: ties keep the earlier
+            t.amv = b.x;
+            t.am = __float_as_int(b.y);
+        }
+        if (b.w != 0.0f) {
+            zy = b.z;
+            has = 1.0f;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        combine(t, __shfl_xor(t.m, o, 64), __shfl_xor(t.s, o, 64), __shfl_xor(t.e, o, 64));
+        t.zs += __shfl_xor(t.zs, o, 64);
+        dev::argmax_combine(t.amv, t.am, __shfl_xor(t.amv, o, 64), __shfl_xor(t.am, o, 64));
+        zy += __shfl_xor(zy, o, 64);   // at most one lane holds the target
+        has += __shfl_xor(has, o, 64);
+    }
+    if (lane != 0) return;
+    const int64_t y = labels[i];
+    const bool valid = y != ignore_index && y >= 0 && y < V;
+    const float ey = has != 0.0f ? dev::exp2_fast((zy - t.m) * kLog2e) : 0.0f;
+    const float S = t.s + ey;
+    const float lse = t.m + logf(S);
+    const int64_t am = t.am;
+    lse_out[i] = lse;
+    if (q_out) q_out[i] = valid ? t.s / S : 0.0f;
+    if (loss_tok) loss_tok[i] = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
+    if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
+    if (ent_out) ent_out[i] = lse - t.e / S;
     if (argmax_out) argmax_out[i] = am;
     if (valid && am == y) __hip_atomic_fetch_add(reinterpret_cast<unsigned long long *>(counts + 1), 1ull,
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -310,17 +364,22 @@ hipError_t launch_ce_stats(const void *logits, int64_t ld, bool is_bf16, const i
     return hipGetLastError();
 }
 
-hipError_t launch_ce_combine(const float *stats, int64_t shards, const int64_t *labels,
-                             int64_t n, int64_t V, int64_t ignore_index, float eps, int reduction, float *lse,
+hipError_t launch_ce_combine(const float *stats, int64_t shards, int64_t shard_stride, int64_t row_stride,
+                             const int64_t *labels, int64_t n, int64_t V, int64_t ignore_index, float eps, int reduction, float *lse,
                              float *q, float *loss_tok, float *loss_out, float *logp, float *ent,
                              int64_t *argmax_out, int64_t *counts, hipStream_t st) {
     hipError_t e;
     // counts {n_valid, 0, n_bad}; n_correct is added below
     if ((e = launch_ce_count(labels, n, V, ignore_index, counts, nullptr, loss_out, st)) != hipSuccess) return e;
-    if (n > 0) {
+    if (n > 0 && shards > 16) {
+        const dim3 grid(static_cast<unsigned>((n + 3) / 4)), block(256);
+        hipLaunchKernelGGL(ce_combine_wide_kernel, grid, block, 0, st, stats, shards, shard_stride, row_stride, labels,
+                           n, V, ignore_index, eps, lse, q, loss_tok, logp, ent, argmax_out, counts);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (n > 0) {
         const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
-        hipLaunchKernelGGL(ce_combine_kernel, grid, block, 0, st, stats, shards, labels, n, V, ignore_index, eps,
-                           lse, q, loss_tok, logp, ent, argmax_out, counts);
+        hipLaunchKernelGGL(ce_combine_kernel, grid, block, 0, st, stats, shards, shard_stride, row_stride, labels, n,
+                           V, ignore_index, eps, lse, q, loss_tok, logp, ent, argmax_out, counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (loss_out) return launch_loss_fold(loss_tok, n, counts, reduction, loss_out, st);

@@ -130,16 +130,18 @@ hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, i
     return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool SOFTCAP = false>
 void launch_gemm(const GemmArgs &g, bool ktail, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u), block(gemm::NTHR);
-    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true>), grid, block, 0, st, g);
-    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false>), grid, block, 0, st, g);
+    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true, SOFTCAP>), grid, block, 0, st, g);
+    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false, SOFTCAP>), grid, block, 0, st, g);
 }
 
-// C (+)= A B^T over [M, N] with K split into `splits` ranges
+// C (+)= A B^T over [M, N] with K split into `splits` ranges; the cross-entropy
+// modes (OUT_STATS, OUT_GRAD) take their inputs from *ce and run unsplit.
 hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, int M,
-                   int N, int K, int splits, int64_t c_split_stride, hipStream_t st) {
+                   int N, int K, int splits, int64_t c_split_stride, hipStream_t st,
+                   const gemm::CeEpi *ce = nullptr) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if ((K & 7) || (lda & 7) || (ldb & 7) || (reinterpret_cast<uintptr_t>(A) & 15) ||
         (reinterpret_cast<uintptr_t>(B) & 15))
@@ -163,8 +165,19 @@ hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t 
     g.tiles_n = ceil_div(N, gemm::BN);
     const int64_t total = static_cast<int64_t>(g.tiles_m) * g.tiles_n * splits;
     g.tiles_per_xcd = ceil_div(total, 8);
+    g.ce = ce ? *ce : gemm::CeEpi{};
     const bool ktail = (K % gemm::BK) != 0;
-    if (mode == gemm::OUT_BF16) launch_gemm<gemm::OUT_BF16>(g, ktail, st);
+    if (mode == gemm::OUT_STATS || mode == gemm::OUT_GRAD) {
+        if (!ce || splits != 1) return hipErrorInvalidValue;
+        const bool sc = ce->softcap > 0.0f;
+        if (mode == gemm::OUT_STATS) {
+            if (sc) launch_gemm<gemm::OUT_STATS, true>(g, ktail, st);
+            else launch_gemm<gemm::OUT_STATS, false>(g, ktail, st);
+        } else {
+            if (sc) launch_gemm<gemm::OUT_GRAD, true>(g, ktail, st);
+            else launch_gemm<gemm::OUT_GRAD, false>(g, ktail, st);
+        }
+    } else if (mode == gemm::OUT_BF16) launch_gemm<gemm::OUT_BF16>(g, ktail, st);
     else if (mode == gemm::OUT_F32) launch_gemm<gemm::OUT_F32>(g, ktail, st);
     else launch_gemm<gemm::OUT_F32_ACC>(g, ktail, st);
     return hipGetLastError();
@@ -240,9 +253,11 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     void *ce_ws = ws + L.off_ce;
     const int64_t C = L.chunk, H = f.H, V = f.V;
 
-    // counts (and a zeroed completion counter for the chunk CE calls)
-    if ((e = launch_ce_count(f.labels, f.n, V, f.ignore_index, f.counts, static_cast<unsigned *>(ce_ws), f.loss_out,
-                             st)) != hipSuccess)
+    const bool resident = f.lse != nullptr;
+    // counts (and a zeroed completion counter for the chunk CE calls); the
+    // resident backward takes them from its stats pass
+    if (!resident && (e = launch_ce_count(f.labels, f.n, V, f.ignore_index, f.counts, static_cast<unsigned *>(ce_ws),
+                                          f.loss_out, st)) != hipSuccess)
         return e;
     if (f.n == 0) {
         const int64_t tot = V * H;
@@ -267,30 +282,47 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             // H_c^T into columns [c0 - g0, ...) of the group's [H, ldg] buffer
             if ((e = transpose(hc, H, ht + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(H), st)) != hipSuccess)
                 return e;
-            // Z_c = H_c W^T  -> bf16 [cn, V]
-            if ((e = gemm_nt(gemm::OUT_BF16, hc, H, f.weight, H, z, V, cn, static_cast<int>(V), static_cast<int>(H),
-                             1, 0, st)) != hipSuccess)
-                return e;
-            // G_c = CE(Z_c) in place, mean scale over all n tokens
-            CEArgs a;
-            a.logits = z;
-            a.ld = V;
-            a.n = cn;
-            a.V = V;
-            a.labels = f.labels + c0;
-            a.count_labels = f.labels;
-            a.count_n = f.n;
-            a.ignore_index = f.ignore_index;
-            a.eps = f.eps;
-            a.softcap = f.softcap;
-            a.reduction = f.reduction;
-            a.grad_out = (f.reduction == 0 && f.grad_out) ? f.grad_out + c0 : f.grad_out;
-            a.loss_tok = f.loss_tok + c0;
-            a.loss_out = nullptr;
-            a.argmax_out = nullptr;
-            a.counts = f.counts;
-            a.workspace = ce_ws;
-            if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
+            if (resident) {
+                // G_c straight from the GEMM's epilogue: Z_c stays in registers
+                gemm::CeEpi ce{};
+                ce.labels = f.labels + c0;
+                ce.ignore_index = f.ignore_index;
+                ce.softcap = f.softcap;
+                ce.eps = f.eps;
+                ce.lse = f.lse + c0;
+                ce.q = f.q + c0;
+                ce.grad_out = (f.reduction == 0 && f.grad_out) ? f.grad_out + c0 : f.grad_out;
+                ce.counts = f.counts;
+                ce.reduction = f.reduction;
+                if ((e = gemm_nt(gemm::OUT_GRAD, hc, H, f.weight, H, z, V, cn, static_cast<int>(V),
+                                 static_cast<int>(H), 1, 0, st, &ce)) != hipSuccess)
+                    return e;
+            } else {
+                // Z_c = H_c W^T  -> bf16 [cn, V]
+                if ((e = gemm_nt(gemm::OUT_BF16, hc, H, f.weight, H, z, V, cn, static_cast<int>(V), static_cast<int>(H),
+                                 1, 0, st)) != hipSuccess)
+                    return e;
+                // G_c = CE(Z_c) in place, mean scale over all n tokens
+                CEArgs a;
+                a.logits = z;
+                a.ld = V;
+                a.n = cn;
+                a.V = V;
+                a.labels = f.labels + c0;
+                a.count_labels = f.labels;
+                a.count_n = f.n;
+                a.ignore_index = f.ignore_index;
+                a.eps = f.eps;
+                a.softcap = f.softcap;
+                a.reduction = f.reduction;
+                a.grad_out = (f.reduction == 0 && f.grad_out) ? f.grad_out + c0 : f.grad_out;
+                a.loss_tok = f.loss_tok + c0;
+                a.loss_out = nullptr;
+                a.argmax_out = nullptr;
+                a.counts = f.counts;
+                a.workspace = ce_ws;
+                if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
+            }
             // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
             if ((e = gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H), static_cast<int>(V), splits,
                              C * H, st)) != hipSuccess)
@@ -308,8 +340,33 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             hipSuccess)
             return e;
     }
-    if (f.loss_out) return launch_loss_fold(f.loss_tok, f.n, f.counts, f.reduction, f.loss_out, st);
+    if (!resident && f.loss_out) return launch_loss_fold(f.loss_tok, f.n, f.counts, f.reduction, f.loss_out, st);
     return hipSuccess;
+}
+
+size_t flce_stats_bytes(int64_t n, int64_t V) {
+    return static_cast<size_t>(n) * static_cast<size_t>(ceil_div(V, gemm::BN)) * kStatsFloats * sizeof(float);
+}
+
+hipError_t launch_flce_forward(const FlceFwdArgs &f, hipStream_t st) {
+    hipError_t e;
+    const int64_t tiles_n = ceil_div(f.V, gemm::BN);
+    float *rec = static_cast<float *>(f.workspace);   // [n][tiles_n] records
+    if (f.n > 0) {
+        gemm::CeEpi ce{};
+        ce.labels = f.labels;
+        ce.ignore_index = f.ignore_index;
+        ce.softcap = f.softcap;
+        ce.eps = f.eps;
+        ce.stats = rec;
+        ce.rec_row_stride = tiles_n;
+        ce.rec_tile_stride = 1;
+        if ((e = gemm_nt(gemm::OUT_STATS, f.hidden, f.H, f.weight, f.H, nullptr, 0, static_cast<int>(f.n),
+                         static_cast<int>(f.V), static_cast<int>(f.H), 1, 0, st, &ce)) != hipSuccess)
+            return e;
+    }
+    return launch_ce_combine(rec, tiles_n, 1, tiles_n, f.labels, f.n, f.V, f.ignore_index, f.eps, f.reduction, f.lse,
+                             f.q, f.loss_tok, f.loss_out, f.logp, f.ent, f.argmax_out, f.counts, st);
 }
 
 }  // namespace lce

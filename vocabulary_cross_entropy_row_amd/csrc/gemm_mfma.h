@@ -24,10 +24,23 @@
 // MFMA operand layout (v_mfma_f32_32x32x16_bf16, checked on the device):
 // lane l supplies A[l % 32][(l / 32) * 8 + j] and B^T[(l / 32) * 8 + j][l % 32]
 // (j = 0..7); result register r of lane l is C[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32].
+//
+// Two epilogues treat C as logits and never store it (the tile-resident form of
+// the fused linear cross-entropy; the Muse Glimmer page's Summary asks for the
+// loss without the [tokens, V] logits):
+//   OUT_STATS  reduces each row of the fp32 tile to one stats record (running
+//              max, sum of exponentials without the target, sum of e^{z-m} z,
+//              sum of z, first argmax of the raw logits, the target's z);
+//   OUT_GRAD   recomputes the same tile and stores the bf16 gradient
+//              s (p - (1 - eps)[j = y] - eps / V) dz/dx from the row's
+//              log-sum-exp and 1 - p_y.
+// Both passes run the identical main loop, so they see bitwise the same logits.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "ce_device.h"
 
 namespace lce {
 namespace gemm {
@@ -42,11 +55,27 @@ constexpr int LOADS = NBLK / NWAVES;                 // per wave per operand per
 constexpr int KK = BK / 16;                          // MFMA K sub-steps per step
 constexpr int kBufWord3 = 0x00020000;                // gfx9-family buffer descriptor word 3
 
-enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_ACC = 2 };
+enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_ACC = 2, OUT_STATS = 3, OUT_GRAD = 4 };
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// Inputs of the cross-entropy epilogues; GEMM row m is token m of the call.
+struct CeEpi {
+    const int64_t *labels;   // label of row m at labels[m]
+    int64_t ignore_index;
+    float softcap;           // > 0: z = T tanh(x / T); 0: z = x
+    float eps;               // label smoothing (OUT_GRAD)
+    float *stats;            // OUT_STATS: record of row m, column tile t at
+    int64_t rec_row_stride;  //   stats + (m * rec_row_stride + t * rec_tile_stride) * 8
+    int64_t rec_tile_stride;
+    const float *lse;        // OUT_GRAD: log-sum-exp of row m at lse[m]
+    const float *q;          // OUT_GRAD: 1 - p_y of row m at q[m]
+    const float *grad_out;   // OUT_GRAD: NULL = 1; reduction none: grad_out[m]; else grad_out[0]
+    const int64_t *counts;   // OUT_GRAD: counts[0] = valid labels, the mean's denominator
+    int reduction;           // 0 none, 1 mean, 2 sum
+};
 
 struct GemmArgs {
     const uint16_t *A;   // [M, K] bf16, row stride lda
@@ -58,6 +87,7 @@ struct GemmArgs {
     int64_t c_split_stride;
     int tiles_m, tiles_n;
     int tiles_per_xcd;   // ceil(total tiles / 8)
+    CeEpi ce;            // OUT_STATS / OUT_GRAD only
 };
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
@@ -71,9 +101,212 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, ui
                                              __builtin_amdgcn_readfirstlane(nrec), kBufWord3);
 }
 
+// Epilogue layout: lane l of wave (wm, wn) holds tile column wn * 128 + j * 32 + l % 32
+// of tile rows wm * 64 + i * 32 + (r / 4) * 8 + (l / 32) * 4 + r % 4.
+__device__ __forceinline__ int epi_row(int wm, int i, int r, int lane) {
+    return wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+
+// One stats record per row of the tile (columns [n0, n0 + 256) of the vocabulary).
+template <bool SOFTCAP>
+__device__ __forceinline__ void stats_epilogue(const GemmArgs &g, f16v (&acc)[WI][4], unsigned char *lds, int m0,
+                                               int n0, int tn, int wm, int wn, int lane) {
+    constexpr float kL2e = dev::kLog2e;
+    int *sh_y = reinterpret_cast<int *>(lds);                 // [BM] target column in the tile, or -1
+    float *sh_rec = reinterpret_cast<float *>(lds + BM * 4);  // [2 column halves][BM][8] partial records
+    const int tid = threadIdx.x;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave is done with the operand stages
+    if (tid < BM) {
+        int yr = -1;
+        if (m0 + tid < g.M) {
+            const int64_t y = g.ce.labels[m0 + tid];
+            if (y != g.ce.ignore_index && y >= n0 && y < n0 + BN && y < g.N) yr = static_cast<int>(y - n0);
+        }
+        sh_y[tid] = yr;
+    }
+    __syncthreads();
+    const dev::Cap cap{SOFTCAP ? 2.0f * kL2e / g.ce.softcap : 0.0f, g.ce.softcap};
+    const int cbase = wn * 128 + (lane & 31);   // tile column of j = 0
+    bool cv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cv[j] = n0 + cbase + j * 32 < g.N;
+    float *rec_w = sh_rec + wn * BM * 8;
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+#pragma unroll
+        for (int rb = 0; rb < 16; rb += 8) {
+            float lm[8], lx[8];
+            int li[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                lm[u] = -FLT_MAX;
+                lx[u] = -INFINITY;
+                li[u] = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (!cv[j]) continue;
+                    const float x = acc[i][j][rb + u];
+                    const float z = SOFTCAP ? cap.z_of_r(cap.r_of(x)) : x;
+                    acc[i][j][rb + u] = z;
+                    lm[u] = fmaxf(lm[u], z);
+                    if (x > lx[u]) {   // columns ascend with j: the first maximum stays
+                        lx[u] = x;
+                        li[u] = cbase + j * 32;
+                    }
+                }
+            }
+            // over the 32 lanes that share each row
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    lm[u] = fmaxf(lm[u], __shfl_xor(lm[u], o, 64));
+                    const float v2 = __shfl_xor(lx[u], o, 64);
+                    const int i2 = __shfl_xor(li[u], o, 64);
+                    dev::argmax_combine(lx[u], li[u], v2, i2);
+                }
+            float sx[8], se[8], sz[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int rl = epi_row(wm, i, rb + u, lane);
+                const int yr = sh_y[rl];
+                const float mL = lm[u] * kL2e;
+                sx[u] = 0.0f;
+                se[u] = 0.0f;
+                sz[u] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (!cv[j]) continue;
+                    const float z = acc[i][j][rb + u];
+                    float ex = dev::exp2_fast(fmaf(z, kL2e, -mL));
+                    se[u] = fmaf(ex, z, se[u]);
+                    sz[u] += z;
+                    if (cbase + j * 32 == yr) {   // the target: its z, and out of the sum
+                        rec_w[rl * 8 + 6] = z;
+                        rec_w[rl * 8 + 7] = 1.0f;
+                        ex = 0.0f;
+                    }
+                    sx[u] += ex;
+                }
+            }
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    sx[u] += __shfl_xor(sx[u], o, 64);
+                    se[u] += __shfl_xor(se[u], o, 64);
+                    sz[u] += __shfl_xor(sz[u], o, 64);
+                }
+            if ((lane & 31) == 0) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int rl = epi_row(wm, i, rb + u, lane);
+                    float *o = rec_w + rl * 8;
+                    o[0] = lm[u];
+                    o[1] = sx[u];
+                    o[2] = se[u];
+                    o[3] = sz[u];
+                    o[4] = lx[u];
+                    o[5] = __int_as_float(li[u]);
+                    const int yr = sh_y[rl] - wn * 128;
+                    if (yr < 0 || yr >= 128) {   // no target in this half
+                        o[6] = 0.0f;
+                        o[7] = 0.0f;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // the two column halves of each row, in column order
+    if (tid < BM && m0 + tid < g.M) {
+        const float *a = sh_rec + tid * 8, *b = sh_rec + (BM + tid) * 8;
+        const float M = fmaxf(a[0], b[0]);
+        const float fa = dev::exp2_fast((a[0] - M) * kL2e), fb = dev::exp2_fast((b[0] - M) * kL2e);
+        float amv = a[4];
+        int am = __float_as_int(a[5]);
+        if (b[4] > amv) {
+            amv = b[4];
+            am = __float_as_int(b[5]);
+        }
+        const bool ha = a[7] != 0.0f;
+        float4 *o = reinterpret_cast<float4 *>(
+            g.ce.stats + (static_cast<int64_t>(m0 + tid) * g.ce.rec_row_stride + tn * g.ce.rec_tile_stride) * 8);
+        o[0] = make_float4(M, a[1] * fa + b[1] * fb, a[2] * fa + b[2] * fb, a[3] + b[3]);
+        o[1] = make_float4(amv, __int_as_float(n0 + am), ha ? a[6] : b[6], ha ? 1.0f : b[7]);
+    }
+}
+
+// The bf16 gradient of every element of the tile, stored at C[row, col].
+template <bool SOFTCAP>
+__device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI][4], unsigned char *lds, int m0,
+                                              int n0, int wm, int wn, int lane) {
+    constexpr float kL2e = dev::kLog2e;
+    float4 *sh_p = reinterpret_cast<float4 *>(lds);    // [BM] {lse log2e - log2|s|, |s| eps / V, target value, sign}
+    int *sh_y = reinterpret_cast<int *>(lds + BM * 16);  // [BM] target column in the tile, or -1
+    const int tid = threadIdx.x;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid < BM) {
+        float4 p = make_float4(INFINITY, 0.0f, 0.0f, 1.0f);   // a zero scale: every element 0
+        int yr = -1;
+        const int m = m0 + tid;
+        if (m < g.M) {
+            const int64_t y = g.ce.labels[m];
+            const bool valid = y != g.ce.ignore_index && y >= 0 && y < g.N;
+            const float *go = g.ce.grad_out;
+            const float gv = g.ce.reduction == 0 ? (go ? go[m] : 1.0f) : (go ? go[0] : 1.0f);
+            const int64_t nv = g.ce.counts[0];
+            const float scale =
+                !valid ? 0.0f : (g.ce.reduction == 1 ? (nv > 0 ? gv / static_cast<float>(nv) : 0.0f) : gv);
+            if (scale != 0.0f) {
+                const float as = fabsf(scale);
+                p.x = g.ce.lse[m] * kL2e - log2f(as);
+                p.y = g.ce.eps / static_cast<float>(g.N) * as;
+                p.z = as * (g.ce.eps - g.ce.q[m]) - p.y;   // p_y - 1 = -q, kept exact
+                p.w = scale < 0.0f ? -1.0f : 1.0f;
+                if (y >= n0 && y < n0 + BN) yr = static_cast<int>(y - n0);
+            }
+        }
+        sh_p[tid] = p;
+        sh_y[tid] = yr;
+    }
+    __syncthreads();
+    const dev::Cap cap{SOFTCAP ? 2.0f * kL2e / g.ce.softcap : 0.0f, g.ce.softcap};
+    const int cbase = wn * 128 + (lane & 31);
+    __bf16 *C = static_cast<__bf16 *>(g.C);
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rl = epi_row(wm, i, r, lane);
+            if (m0 + rl >= g.M) continue;
+            const float4 P = sh_p[rl];
+            const int yr = sh_y[rl];
+            __bf16 *crow = C + static_cast<int64_t>(m0 + rl) * g.ldc + n0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = cbase + j * 32;
+                if (n0 + c >= g.N) continue;
+                const float x = acc[i][j][r];
+                float z = x, ch = P.w;
+                if constexpr (SOFTCAP) {
+                    const float rr = cap.r_of(x);
+                    z = cap.z_of_r(rr);
+                    ch *= dev::Cap::chain_of_r(rr);
+                }
+                const float pe = dev::exp2_fast(fmaf(z, kL2e, -P.x));
+                const float gval = c == yr ? P.z : pe - P.y;
+                crow[c] = static_cast<__bf16>(gval * ch);   // RNE
+            }
+        }
+    }
+}
+
 // KTAIL: K is not a multiple of BK, so each load checks its K column; otherwise
 // the K position rides in the scalar offset and the per-lane offsets are fixed.
-template <int MODE, bool KTAIL>
+template <int MODE, bool KTAIL, bool SOFTCAP = false>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_nt_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
@@ -216,6 +449,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         }
     }
 
+    if constexpr (MODE == OUT_STATS) {
+        stats_epilogue<SOFTCAP>(g, acc, lds, m0, n0, tn, wm, wn, lane);
+        return;
+    } else if constexpr (MODE == OUT_GRAD) {
+        grad_epilogue<SOFTCAP>(g, acc, lds, m0, n0, wm, wn, lane);
+        return;
+    }
     // epilogue: lane holds column n0 + wn*128 + j*32 + lane%32 of rows
     // m0 + wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4
     const int col_base = n0 + wn * 128 + (lane & 31);

@@ -34,11 +34,37 @@ lce_status hip_status(hipError_t e, const char *what) {
 
 bool is_aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Checks shared by the tile-resident fused linear entry points.
+lce_status check_flce_resident(const char *fn, const void *hidden, const void *weight, const int64_t *labels,
+                               int64_t n, int64_t H, int64_t V, float label_smoothing, float softcap,
+                               lce_reduction reduction) {
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "%s: n must be >= 0 (got %lld)", fn, (long long)n);
+    if (H < 1) return fail(LCE_ERR_INVALID_ARG, "%s: H must be >= 1 (got %lld)", fn, (long long)H);
+    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "%s: V must be >= 1 (got %lld)", fn, (long long)V);
+    if (reduction != LCE_RED_NONE && reduction != LCE_RED_MEAN && reduction != LCE_RED_SUM)
+        return fail(LCE_ERR_INVALID_ARG, "%s: unknown reduction %d", fn, (int)reduction);
+    if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
+        return fail(LCE_ERR_INVALID_ARG, "%s: label_smoothing must be in [0, 1] (got %g)", fn, (double)label_smoothing);
+    if (!(softcap >= 0.0f) || isinf(softcap))
+        return fail(LCE_ERR_INVALID_ARG, "%s: softcap must be finite and >= 0 (got %g)", fn, (double)softcap);
+    if (!weight) return fail(LCE_ERR_INVALID_ARG, "%s: weight is required", fn);
+    if (n > 0 && (!hidden || !labels)) return fail(LCE_ERR_INVALID_ARG, "%s: hidden and labels are required", fn);
+    if (H % 8 != 0 || V % 8 != 0)
+        return fail(LCE_ERR_UNSUPPORTED, "%s: requires H and V to be multiples of 8 (16-byte bf16 rows); got H=%lld V=%lld",
+                    fn, (long long)H, (long long)V);
+    if ((hidden && !is_aligned(hidden, 16)) || !is_aligned(weight, 16))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: hidden and weight must be 16-byte aligned", fn);
+    if (n > 0x7fffffffLL || V > 0x7fffffffLL / 16 || H > 0x7fffffffLL / 16 || 256ull * V * 2 >= (1ull << 32) ||
+        256ull * H * 2 >= (1ull << 32))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: n >= 2^31 or a 256-row operand tile exceeds 4 GiB", fn);
+    return LCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int lce_abi_version(void) { return 1; }
+int lce_abi_version(void) { return 2; }
 
 const char *lce_last_error(void) { return g_err; }
 
@@ -182,7 +208,7 @@ lce_status lce_ce_combine(const float *stats, int64_t shards, const int64_t *lab
         return fail(LCE_ERR_INVALID_ARG, "%s: stats, labels and lse are required", fn);
     if (n > 0 && loss_out && !loss_tok) return fail(LCE_ERR_INVALID_ARG, "%s: loss_out needs loss_tok", fn);
     if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "%s: n > 2^31-1 rows is not supported", fn);
-    return hip_status(lce::launch_ce_combine(stats, shards, labels, n, V, ignore_index, label_smoothing,
+    return hip_status(lce::launch_ce_combine(stats, shards, n, 1, labels, n, V, ignore_index, label_smoothing,
                                              static_cast<int>(reduction), lse, one_minus_py, loss_tok, loss_out,
                                              logprob, entropy, argmax_out, counts, stream),
                       "lce_ce_combine launch");
@@ -281,6 +307,99 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
     f.workspace = workspace;
     f.group_chunks = group;
     return hip_status(lce::launch_flce(f, stream), "lce_flce_fwd_bwd launch");
+}
+
+size_t lce_flce_stats_bytes(int64_t n, int64_t V) {
+    if (n < 0 || V < 1) return 0;
+    return lce::flce_stats_bytes(n, V);
+}
+
+lce_status lce_flce_forward(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
+                            int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                            lce_reduction reduction, float *loss_tok, float *loss_out, float *lse, float *one_minus_py,
+                            float *logprob, float *entropy, int64_t *argmax_out, int64_t *counts, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "lce_flce_forward";
+    lce_status st = check_flce_resident(fn, hidden, weight, labels, n, H, V, label_smoothing, softcap, reduction);
+    if (st != LCE_OK) return st;
+    if (!counts) return fail(LCE_ERR_INVALID_ARG, "%s: counts is required", fn);
+    if (n > 0 && (!loss_tok || !lse || !one_minus_py))
+        return fail(LCE_ERR_INVALID_ARG, "%s: loss_tok, lse and one_minus_py are required", fn);
+    const size_t need = lce::flce_stats_bytes(n, V);
+    if (n > 0 && (!workspace || workspace_bytes < need))
+        return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < minimum %zu", fn, workspace_bytes, need);
+    if (n > 0 && !is_aligned(workspace, 256))
+        return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    lce::FlceFwdArgs f;
+    f.hidden = hidden;
+    f.weight = weight;
+    f.labels = labels;
+    f.n = n;
+    f.H = H;
+    f.V = V;
+    f.ignore_index = ignore_index;
+    f.eps = label_smoothing;
+    f.softcap = softcap;
+    f.reduction = static_cast<int>(reduction);
+    f.lse = lse;
+    f.q = one_minus_py;
+    f.loss_tok = loss_tok;
+    f.loss_out = loss_out;
+    f.logp = logprob;
+    f.ent = entropy;
+    f.argmax_out = argmax_out;
+    f.counts = counts;
+    f.workspace = workspace;
+    return hip_status(lce::launch_flce_forward(f, stream), "lce_flce_forward launch");
+}
+
+lce_status lce_flce_backward(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
+                             int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                             lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, const float *lse,
+                             const float *one_minus_py, const int64_t *counts, void *grad_hidden, float *grad_weight,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "lce_flce_backward";
+    lce_status st = check_flce_resident(fn, hidden, weight, labels, n, H, V, label_smoothing, softcap, reduction);
+    if (st != LCE_OK) return st;
+    if (chunk_tokens < 1) return fail(LCE_ERR_INVALID_ARG, "%s: chunk_tokens must be >= 1", fn);
+    if (!grad_weight || !counts || !workspace)
+        return fail(LCE_ERR_INVALID_ARG, "%s: grad_weight, counts and workspace are required", fn);
+    if (n > 0 && (!grad_hidden || !lse || !one_minus_py))
+        return fail(LCE_ERR_INVALID_ARG, "%s: grad_hidden, lse and one_minus_py are required", fn);
+    if ((grad_hidden && !is_aligned(grad_hidden, 16)) || !is_aligned(grad_weight, 16))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: grad_hidden and grad_weight must be 16-byte aligned", fn);
+    int64_t group = lce::flce_default_group_chunks(n, H, V, chunk_tokens);
+    while (group > 1 && lce::flce_layout(n, H, V, chunk_tokens, group).bytes > workspace_bytes) --group;
+    const size_t need = lce::flce_layout(n, H, V, chunk_tokens, group).bytes;
+    if (workspace_bytes < need)
+        return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < minimum %zu", fn, workspace_bytes, need);
+    if (!is_aligned(workspace, 256)) return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    const int64_t C = chunk_tokens < n ? chunk_tokens : n;
+    if (C > 0x7fffffffLL / 16 || static_cast<unsigned long long>(C) * V * 2 >= (1ull << 32))
+        return fail(LCE_ERR_UNSUPPORTED, "%s: a chunk of gradients exceeds 4 GiB", fn);
+    lce::FlceArgs f;
+    f.hidden = hidden;
+    f.weight = weight;
+    f.labels = labels;
+    f.n = n;
+    f.H = H;
+    f.V = V;
+    f.chunk = chunk_tokens;
+    f.ignore_index = ignore_index;
+    f.eps = label_smoothing;
+    f.softcap = softcap;
+    f.reduction = static_cast<int>(reduction);
+    f.grad_out = grad_out;
+    f.loss_tok = nullptr;
+    f.loss_out = nullptr;
+    f.grad_hidden = grad_hidden;
+    f.grad_weight = grad_weight;
+    f.counts = const_cast<int64_t *>(counts);   // read only on this path
+    f.workspace = workspace;
+    f.group_chunks = group;
+    f.lse = lse;
+    f.q = one_minus_py;
+    return hip_status(lce::launch_flce(f, stream), "lce_flce_backward launch");
 }
 
 }  // extern "C"

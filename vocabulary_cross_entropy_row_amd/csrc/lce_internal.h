@@ -73,7 +73,9 @@ constexpr int kStatsFloats = 8;
 hipError_t launch_ce_stats(const void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n,
                            int64_t Vs, int64_t v0, int64_t ignore_index, float softcap, float *stats,
                            hipStream_t stream);
-hipError_t launch_ce_combine(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
+// Record of row i, shard k at stats + (k * shard_stride + i * row_stride) * 8.
+hipError_t launch_ce_combine(const float *stats, int64_t shards, int64_t shard_stride, int64_t row_stride,
+                             const int64_t *labels, int64_t n, int64_t V,
                              int64_t ignore_index, float eps, int reduction, float *lse, float *q, float *loss_tok,
                              float *loss_out, float *logp, float *ent, int64_t *argmax_out, int64_t *counts,
                              hipStream_t stream);
@@ -112,7 +114,33 @@ struct FlceArgs {
     int64_t *counts;         // [3]
     void *workspace;
     int64_t group_chunks;    // chunks per grad_weight group (the workspace was sized for it)
+    // Tile-resident backward: with lse and q (1 - p_y) of every token from the
+    // stats pass, each chunk's gradient is formed in the logits GEMM's epilogue
+    // (no logits stored, no losses written, counts read as given).
+    const float *lse = nullptr;
+    const float *q = nullptr;
 };
+
+// Stats pass of the tile-resident fused linear cross-entropy: one record per
+// token and 256-column tile of Z = hidden weight^T, merged into the row outputs.
+struct FlceFwdArgs {
+    const void *hidden;      // bf16 [n, H]
+    const void *weight;      // bf16 [V, H]
+    const int64_t *labels;   // [n]
+    int64_t n, H, V;
+    int64_t ignore_index;
+    float eps, softcap;
+    int reduction;
+    float *lse, *q;          // [n], required
+    float *loss_tok;         // [n], required
+    float *loss_out;         // scalar or NULL
+    float *logp, *ent;       // [n] or NULL
+    int64_t *argmax_out;     // [n] or NULL
+    int64_t *counts;         // [3]
+    void *workspace;         // flce_stats_bytes(n, V)
+};
+size_t flce_stats_bytes(int64_t n, int64_t V);
+hipError_t launch_flce_forward(const FlceFwdArgs &f, hipStream_t stream);
 
 // Offsets (bytes) of the fused-linear workspace regions.
 struct FlceLayout {
