@@ -208,7 +208,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         float m = -FLT_MAX;      // running max of z (finite start: no inf - inf)
         float s = 0.0f;          // sum over this thread's elements j != y of exp(z_j - m)
         float zs = 0.0f;         // sum of z (label smoothing)
-        float amv = -INFINITY;   // argmax: value and first index over the raw logits
+        float amv = -INFINITY;   // argmax: value and first index over the raw logits, kept
+        int am_k = -1, am_e = 0; // as (round, element): no per-round index lives across rows
         int am = 0x7fffffff;
         if constexpr (KL > 0) {
             // this wave's LDS rounds have landed once at most the 2 KR memory
@@ -239,13 +240,16 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                     } else {
                         xmax = rmax;
                     }
-                    int first = E - 1;
-#pragma unroll
-                    for (int e = E - 2; e >= 0; --e)
-                        if (x[e] == xmax) first = e;
                     if (xmax > amv) {                 // rounds come in index order: keep the first
+                        // (rare once the running maximum has settled: the search
+                        // for the element runs only then)
+                        int first = E - 1;
+#pragma unroll
+                        for (int e = E - 2; e >= 0; --e)
+                            if (x[e] == xmax) first = e;
                         amv = xmax;
-                        am = idx * E + first;
+                        am_k = k;
+                        am_e = first;
                     }
                 }
                 if constexpr (SMOOTH) {
@@ -295,6 +299,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 sh_s[pb][tid >> 6] = sw;
             }
             if constexpr (ARGMAX) {
+                am = am_k < 0 ? 0x7fffffff : (am_k * NT + tid) * E + am_e;
                 wave_argmax(amv, am);
                 if ((tid & 63) == 0) {
                     sh_z[pb][tid >> 6] = amv;

@@ -45,15 +45,25 @@
 namespace lce {
 namespace gemm {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+#ifndef LCE_GEMM_BK
+#define LCE_GEMM_BK 64
+#endif
+#ifndef LCE_GEMM_NSTAGE
+#define LCE_GEMM_NSTAGE 2
+#endif
+constexpr int BM = 256, BN = 256, BK = LCE_GEMM_BK;
+constexpr int NSTAGE = LCE_GEMM_NSTAGE;              // LDS stages; NSTAGE - 1 steps of loads in flight
 constexpr int NWAVES = 8, NTHR = 64 * NWAVES;
 constexpr int WI = 2;                                // A fragments (32 rows each) per wave
-constexpr int TILE_BYTES = BM * BK * 2;              // one operand tile of one stage: 32 KB
-constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;        // two stages of A | B: 128 KB
+constexpr int CPR = BK / 8;                          // 16-byte K chunks per tile row
+constexpr int TILE_BYTES = BM * BK * 2;              // one operand tile of one stage
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;          // A | B
+constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
 constexpr int NBLK = TILE_BYTES / 1024;              // one-KB load blocks per operand tile
 constexpr int LOADS = NBLK / NWAVES;                 // per wave per operand per step
 constexpr int KK = BK / 16;                          // MFMA K sub-steps per step
 constexpr int kBufWord3 = 0x00020000;                // gfx9-family buffer descriptor word 3
+static_assert(LDS_BYTES <= 160 * 1024 && LOADS >= 1 && (CPR == 4 || CPR == 8), "unsupported GEMM staging");
 
 enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_ACC = 2, OUT_STATS = 3, OUT_GRAD = 4 };
 
@@ -90,7 +100,10 @@ struct GemmArgs {
     CeEpi ce;            // OUT_STATS / OUT_GRAD only
 };
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// LDS position of K chunk c of row r is c ^ swz(r): the 16 rows that one LDS
+// cycle serves for a fragment read (lanes 0-15, consecutive rows, one chunk)
+// land on 16 distinct 16-byte bank groups of the 256-byte bank window.
+__device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
 
 // A buffer descriptor built from wave-uniform values, so it lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, uint32_t nrec) {
@@ -348,18 +361,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     int kcol[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-        const int r = (j * NWAVES + wave) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
+        const int r = (j * NWAVES + wave) * (64 / CPR) + lane / CPR;
+        const int c = (lane % CPR) ^ swz(r);
         kcol[j] = c * 8;
         voffA[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(g.lda) * 2u + c * 16u;
         voffB[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(g.ldb) * 2u + c * 16u;
     }
 
-    // load j of one operand of step `step` into stage `st`.  A step past the end
-    // of K (issued ahead of need, never used) stays inside the descriptor or
-    // reads zeros.
+    // load j of one operand of step `step` into stage `st`
     auto issue = [&](int step, int st, int j, bool isB) {
-        unsigned char *dst = lds + st * 2 * TILE_BYTES + (isB ? TILE_BYTES : 0) + (j * NWAVES + wave) * 1024;
+        unsigned char *dst = lds + st * STAGE_BYTES + (isB ? TILE_BYTES : 0) + (j * NWAVES + wave) * 1024;
         const int k0 = step * BK;
         if constexpr (KTAIL) {
             uint32_t v = (isB ? voffB[j] : voffA[j]) + static_cast<uint32_t>(k0) * 2u;
@@ -371,19 +382,28 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         }
     };
     auto read_frags = [&](int st, int kk, bf8 *af, bf8 *bfr) {
-        const unsigned char *At = lds + st * 2 * TILE_BYTES;
+        const unsigned char *At = lds + st * STAGE_BYTES;
         const unsigned char *Bt = At + TILE_BYTES;
         const int c = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
             const int r = wm * 64 + i * 32 + (lane & 31);
-            af[i] = *reinterpret_cast<const bf8 *>(At + (r * 8 + (c ^ swz(r))) * 16);
+            af[i] = *reinterpret_cast<const bf8 *>(At + (r * CPR + (c ^ swz(r))) * 16);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = wn * 128 + j * 32 + (lane & 31);
-            bfr[j] = *reinterpret_cast<const bf8 *>(Bt + (r * 8 + (c ^ swz(r))) * 16);
+            bfr[j] = *reinterpret_cast<const bf8 *>(Bt + (r * CPR + (c ^ swz(r))) * 16);
         }
+    };
+    // wait until at most `steps` steps of this wave's loads are outstanding
+    // (loads complete in issue order; the count must be an immediate)
+    auto wait_steps = [&](int steps) {
+        constexpr int L = 2 * LOADS;
+        if (steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (steps == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+        else if (steps == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L) : "memory");
     };
 
     f16v acc[WI][4];
@@ -393,35 +413,41 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         for (int j = 0; j < 4; ++j) acc[i][j] = (f16v){};
 
     const int nsteps = kend - kbeg;
+    constexpr int D = NSTAGE - 1;   // steps of loads in flight ahead of the one being consumed
+    static_assert(D >= 1 && D <= 4, "wait_steps covers up to three outstanding steps");
     bf8 af0[WI], bf0[4], af1[WI], bf1[4];
     if (nsteps > 0) {
+        for (int p = 0; p < D && p < nsteps; ++p) {
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            issue(kbeg, 0, j, false);
-            issue(kbeg, 0, j, true);
+            for (int j = 0; j < LOADS; ++j) {
+                issue(kbeg + p, p, j, false);
+                issue(kbeg + p, p, j, true);
+            }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of the first step
-        asm volatile("s_barrier" ::: "memory");            // ... and every wave's
+        wait_steps(min(D, nsteps) - 1);                // this wave's loads of the first step
+        asm volatile("s_barrier" ::: "memory");       // ... and every wave's
         read_frags(0, 0, af0, bf0);
     }
     // settle the scalar loads so the LDS waits inside the loop count precisely
     // (s_waitcnt lgkmcnt(0), vmcnt and expcnt left open)
     __builtin_amdgcn_s_waitcnt(0xC07F);
 
+    int st = 0;   // stage of step s
     for (int s = 0; s < nsteps; ++s) {
-        const int st = s & 1;
+        const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             bf8 *ac = (kk & 1) ? af1 : af0, *bc = (kk & 1) ? bf1 : bf0;
             bf8 *an = (kk & 1) ? af0 : af1, *bn = (kk & 1) ? bf0 : bf1;
             __builtin_amdgcn_sched_barrier(0);
-            if (kk == 0) {
-                // stage st^1 was last read in step s-1, which every wave finished
-                // before the barrier that ended it
+            if (kk == 0 && s + D < nsteps) {
+                // the stage of step s+D was last read in step s-1, which every wave
+                // finished before the barrier that ended it
+                const int st_issue = st == 0 ? NSTAGE - 1 : st - 1;
 #pragma unroll
                 for (int j = 0; j < LOADS; ++j) {
-                    issue(kbeg + s + 1, st ^ 1, j, false);
-                    issue(kbeg + s + 1, st ^ 1, j, true);
+                    issue(kbeg + s + D, st_issue, j, false);
+                    issue(kbeg + s + D, st_issue, j, true);
                 }
             }
             if (kk + 1 < KK) {
@@ -430,9 +456,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                 // this wave's fragments of stage st are in registers and its loads
                 // of step s+1 have landed; after the barrier so are everyone's
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                wait_steps(min(s + D, nsteps - 1) - (s + 1));
                 asm volatile("s_barrier" ::: "memory");
-                read_frags(st ^ 1, 0, an, bn);
+                read_frags(st_next, 0, an, bn);
             }
 #pragma unroll
             for (int i = 0; i < WI; ++i)
@@ -447,6 +473,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                 if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
             }
         }
+        st = st_next;
     }
 
     if constexpr (MODE == OUT_STATS) {
