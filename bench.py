@@ -97,7 +97,7 @@ def cpu_baseline(w, x, y, nthreads: int, min_seconds: float = 10.0) -> dict:
 # the sources each measured kernel is compiled from: the persistent row kernel, and for the
 # fused variant also its GEMM, transposes and driver
 CE_SOURCES = ("ce_device.h", "ce_rows.h", "ce_rows_inst.hip")
-FLCE_SOURCES = CE_SOURCES + ("lce_internal.h", "ce_kernels.hip", "gemm_mfma.h", "flce.hip")
+FLCE_SOURCES = CE_SOURCES + ("lce_internal.h", "ce_kernels.hip", "gemm_mfma.h", "flce.hip", "ce_split.hip")
 
 
 def kernel_source_hash(workload: str = "") -> str:
@@ -109,14 +109,14 @@ def kernel_source_hash(workload: str = "") -> str:
     return h.hexdigest()[:16]
 
 
-def profile_path(workload: str) -> str:
-    kind = "flce_gemm" if workload.startswith("flce") else "ce_rows_kernel"
+def profile_path(workload: str, resident: bool = False) -> str:
+    kind = ("flce_resident_gemm" if resident else "flce_gemm") if workload.startswith("flce") else "ce_rows_kernel"
     return os.path.join(PROFILES, f"{kind}__{workload}.txt")
 
 
-def read_profile(workload: str) -> dict | None:
+def read_profile(workload: str, resident: bool = False) -> dict | None:
     try:
-        with open(profile_path(workload)) as f:
+        with open(profile_path(workload, resident)) as f:
             lines = f.read().splitlines()
     except OSError:
         return None
@@ -302,9 +302,9 @@ def bench_flce(args, w) -> int:
     flops = flce_flops(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (call_ms * 1e-3) / 1e12
-    prof = read_profile(w.name)
+    prof = read_profile(w.name, resident)
     traffic = None
-    if not resident and prof and prof.get("kernel_source_sha256_16") == kernel_source_hash(w.name):
+    if prof and prof.get("kernel_source_sha256_16") == kernel_source_hash(w.name):
         traffic = int(prof["traffic_bytes_per_dispatch"])
     out = {
         "metric": RESIDENT_METRIC if resident else FLCE_METRIC,
@@ -345,12 +345,12 @@ def bench_flce(args, w) -> int:
     return 0
 
 
-def collect_profiles_flce(workload: str) -> int:
+def collect_profiles_flce(workload: str, resident: bool = False) -> int:
     import synth
     w = synth.FLCE_WORKLOADS[workload]
-    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", workload)
+    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", workload + ("_resident" if resident else ""))
     os.makedirs(raw, exist_ok=True)
-    base = ["--workload", workload, "--no-cpu-baseline"]
+    base = ["--workload", workload, "--no-cpu-baseline"] + (["--path", "resident"] if resident else [])
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "3", "--warmup", "1"], 600)
     _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "1", "--warmup", "1"], 600)
     _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "1", "--warmup", "1"], 600)
@@ -358,7 +358,7 @@ def collect_profiles_flce(workload: str) -> int:
     calls = 4   # warmup + steps of the trace run
     ref_kib = (256 << 20) * 4 / 1024.0
     ours = ("gemm_nt_kernel", "transpose_bf16_kernel", "splitk_fold_kernel", "ce_rows_kernel", "ce_count_kernel",
-            "loss_fold_kernel", "fill_zero_f32_kernel", "ce_row_generic")
+            "loss_fold_kernel", "fill_zero_f32_kernel", "ce_row_generic", "ce_combine")
 
     def counter(sub: str, cname: str):
         rows = list(csv.DictReader(open(os.path.join(raw, sub, "run_counter_collection.csv"))))
@@ -374,17 +374,19 @@ def collect_profiles_flce(workload: str) -> int:
     traffic = (fk * fscale + wk * wscale) * 1024.0
     b = " ".join(base)
     total_ns = sum(float(r["TotalDurationNs"]) for r in stats if any(o in r["Name"] for o in ours)) / calls
+    what = ("tile-resident fused linear cross-entropy (lce_flce_forward + lce_flce_backward)" if resident
+            else "fused linear cross-entropy (lce_flce_fwd_bwd)")
     lines = [
-        f"# rocprofv3 summary: fused linear cross-entropy, workload {workload}",
+        f"# rocprofv3 summary: {what}, workload {workload}",
         f"# (hidden {w.n} x {w.H}, weight {w.V} x {w.H} bf16, chunk {w.chunk}, softcap {w.softcap})",
-        f"# made by: python bench.py --collect-profiles --workload {workload}",
+        f"# made by: python bench.py --collect-profiles --workload {workload}" + (" --path resident" if resident else ""),
         "# which runs, from /tmp with TMPDIR=/tmp:",
         f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 3 --warmup 1",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <raw>/fetch -o run -- python bench.py {b} --steps 1 --warmup 1",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <raw>/write -o run -- python bench.py {b} --steps 1 --warmup 1",
         "# Counter scale: what each counter reads for a plain 1 GiB device copy (__amd_rocclr_copyBuffer)",
-        "# made once before timing, divided into its known size.  Traffic is per lce_flce_fwd_bwd call,",
-        "# summed over all of its kernels.",
+        "# made once before timing, divided into its known size.  Traffic is per step (one call, or",
+        "# forward + backward), summed over all of its kernels.",
         "#",
         "# kernel trace (--stats), nanoseconds (per-call share = total / calls):",
     ]
@@ -393,6 +395,14 @@ def collect_profiles_flce(workload: str) -> int:
                      f"per-call-share {float(r['TotalDurationNs']) / calls / 1e6:>8.3f} ms")
     gemm = [r for r in stats if "gemm_nt_kernel" in r["Name"]]
     gemm_ns = sum(float(r["TotalDurationNs"]) for r in gemm) / calls
+    if resident:
+        # the stats GEMM (epilogue mode 3) is one launch per forward: 2 n H V flops
+        st = [r for r in gemm if "gemm_nt_kernel<3" in r["Name"]]
+        if st:
+            st_ns = float(st[0]["AverageNs"])
+            lines += [f"stats_gemm_kernel: {st[0]['Name']}", f"stats_gemm_avg_ns: {st_ns:.1f}",
+                      f"stats_gemm_tflops: {2 * w.n * w.H * w.V / (st_ns * 1e-9) / 1e12:.1f}"]
+        lines.append("gemm_flops_executed_per_step: " + str(8 * w.n * w.H * w.V) + "   (the backward forms the logits again)")
     lines += [
         f"call_kernel_ns: {total_ns:.0f}",
         f"gemm_kernel_ns_per_call: {gemm_ns:.0f}",
@@ -409,9 +419,9 @@ def collect_profiles_flce(workload: str) -> int:
         f"kernel_source_sha256_16: {kernel_source_hash(workload)}",
     ]
     os.makedirs(PROFILES, exist_ok=True)
-    with open(profile_path(workload), "w") as f:
+    with open(profile_path(workload, resident), "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(open(profile_path(workload)).read(), flush=True)
+    print(open(profile_path(workload, resident)).read(), flush=True)
     return 0
 
 
@@ -507,7 +517,7 @@ def main() -> int:
     import synth
     if args.collect_profiles:
         if args.workload in synth.FLCE_WORKLOADS:
-            return collect_profiles_flce(args.workload)
+            return collect_profiles_flce(args.workload, args.path == "resident")
         return collect_profiles(args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (token rows would shard "
