@@ -79,6 +79,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     const float eps = a.eps;
     const float invV = 1.0f / static_cast<float>(a.V);
     const Cap cap{SOFTCAP ? 2.0f * kLog2e / a.softcap : 0.0f, a.softcap};
+    const float capk = -2.0f * a.softcap * kLog2e;   // d(z log2 e)/dr under the softcap
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     // Labels and the upstream gradient are read-only for the kernel's lifetime:
     // read them through the constant address space, i.e. with scalar loads,
@@ -223,15 +224,19 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             // whole rounds need no per-lane test (uniform check first)
             if ((k + 1) * NT <= nvec || idx < nvec) {
                 const u32x4 vk = round_vec(k);
+                // z = x, or with the softcap z = T - 2 T r (r = 1 / (1 + e^{2x/T})):
+                // then the exponent of z is one fma on r and max z = z(min r)
+                // (the fma is monotone in r), so z itself is never formed
                 float x[E], z[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     x[e] = EL::get(vk, e);
-                    z[e] = SOFTCAP ? cap.z_of_r(cap.r_of(x[e])) : x[e];
+                    z[e] = SOFTCAP ? cap.r_of(x[e]) : x[e];
                 }
                 float rmax = z[0];
 #pragma unroll
-                for (int e = 1; e < E; ++e) rmax = fmaxf(rmax, z[e]);
+                for (int e = 1; e < E; ++e) rmax = SOFTCAP ? fminf(rmax, z[e]) : fmaxf(rmax, z[e]);
+                if constexpr (SOFTCAP) rmax = cap.z_of_r(rmax);
                 if constexpr (ARGMAX) {
                     float xmax = x[0];
                     if constexpr (SOFTCAP) {
@@ -253,15 +258,23 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                     }
                 }
                 if constexpr (SMOOTH) {
+                    float t = z[0];
 #pragma unroll
-                    for (int e = 0; e < E; ++e) zs += z[e];
+                    for (int e = 1; e < E; ++e) t += z[e];
+                    zs += SOFTCAP ? fmaf(-2.0f * a.softcap, t, E * a.softcap) : t;
                 }
                 const float mn = fmaxf(m, rmax);
                 const float mnL = mn * kLog2e;
                 float part = 0.0f;
                 float ex[E];
+                if constexpr (SOFTCAP) {
+                    const float b = fmaf(a.softcap, kLog2e, -mnL);
 #pragma unroll
-                for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], kLog2e, -mnL));
+                    for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], capk, b));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], kLog2e, -mnL));
+                }
                 if (k == ky) {
                     // the target's round (uniform branch, taken once per row); the
                     // asm keeps it a branch instead of per-element selects everywhere
@@ -357,7 +370,6 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const float l2s = log2f(ascale);                  // -inf when the scale is 0
         const float epsV = SMOOTH ? eps * invV * ascale : 0.0f;
         const float lseL = lse * kLog2e - l2s;
-        const float capk = -2.0f * a.softcap * kLog2e;   // d(z log2 e)/dr
         const float capb2 = (a.softcap - lse) * kLog2e + l2s;
         float gy = scale * (eps - s / S - (SMOOTH ? eps * invV : 0.0f));   // s_i (p_y - (1 - eps) - eps/V)
         if constexpr (SOFTCAP) gy *= Cap::chain_of_r(cap.r_of(xy));
@@ -369,9 +381,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             for (int e = 0; e < E; ++e) {
                 const float x = EL::get(vk, e);
                 if constexpr (SOFTCAP) {
+                    // chain 4 r (1 - r): the 4 rides in the exponent (capb2 + 2)
                     const float r = cap.r_of(x);
-                    const float p = exp2_fast(fmaf(r, capk, capb2));        // |s_i| p_j
-                    g[e] = (SMOOTH ? p - epsV : p) * Cap::chain_of_r(r);
+                    const float p4 = exp2_fast(fmaf(r, capk, capb2 + 2.0f));   // 4 |s_i| p_j
+                    g[e] = (SMOOTH ? p4 - 4.0f * epsV : p4) * fmaf(-r, r, r);
                 } else {
                     const float p = exp2_fast(fmaf(x, kLog2e, -lseL));      // |s_i| p_j
                     g[e] = SMOOTH ? p - epsV : p;
