@@ -40,6 +40,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 FLCE_METRIC = "FLCE fwd+bwd ms and bf16 MFMA TFLOP/s (% peak), hidden 4096×6656, weight 202048×6656, 1 GPU"
 RESIDENT_METRIC = ("tile-resident FLCE (logits never stored) fwd+bwd ms and bf16 MFMA TFLOP/s at 6·N·H·V "
                    "(% peak), hidden 4096×6656, weight 202048×6656, 1 GPU")
+# The pages' CE fwd+bwd latencies for this shape (Megatron-LM PR "Add opt-in Liger vocab-parallel cross
+# entropy", Performance (Liger v0.8.5), TP=1 row): another machine, context only, never the target.
+H100_CONTEXT = {"hardware": "H100 80GB, BF16, [2048, 131072], TP=1", "liger_ms": 2.041,
+                "megatron_native_fused_ms": 3.646, "transformer_engine_ms": 0.711}
 CSRC = os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -610,6 +614,8 @@ def main() -> int:
                      "call_ms_max": round(max(per_call_ms), 5), "algorithmic_bytes": nbytes},
         "cpu_baseline": None,
     }
+    if w.n == 2048 and w.V == 131072 and w.dtype == "bf16":
+        out["context_other_hardware"] = H100_CONTEXT
     if not args.no_cpu_baseline:
         nthr = len(os.sched_getaffinity(0))
         if os.environ.get("OMP_NUM_THREADS"):
