@@ -96,6 +96,35 @@ def cpu_baseline(w, x, y, nthreads: int, min_seconds: float = 10.0) -> dict:
                       f"gradient of every row, OpenMP over rows"}
 
 
+def split_cpu_baseline(w, x, y, nbytes: int, nthreads: int, min_seconds: float = 10.0) -> dict:
+    """The oracle as it stands on the split path's outputs: per 256-row chunk the fp64 loss and gradient
+    (row routine) and log-sum-exp, log p_y and entropy (row statistics), repeated over the workload's rows
+    until ``min_seconds`` have elapsed; the rate is scaled to the step's algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.default()
+    chunk = 256
+    rows_done = 0
+    t0 = time.perf_counter()
+    while True:
+        for r0 in range(0, w.n, chunk):
+            rows = np.arange(r0, min(w.n, r0 + chunk))
+            orc.ce(x, y, V=w.V, label_smoothing=w.label_smoothing, softcap=w.softcap, reduction=w.reduction,
+                   grad_out=[w.grad_out], rows=rows, want_grad=True, nthreads=nthreads)
+            orc.row_stats(x, y, V=w.V, softcap=w.softcap, rows=rows, nthreads=nthreads)
+            rows_done += rows.size
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(rows_done / w.n * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{rows_done} rows of the workload ({w.n} x {w.V}) in 256-row chunks: fp64 loss, gradient, "
+                      f"log-sum-exp, log p_y and entropy, scaled to the step's algorithmic bytes"}
+
+
 # ---------------------------------------------------------------- counter summaries
 
 # the sources each measured kernel is compiled from: the persistent row kernel, and for the
@@ -510,7 +539,81 @@ def bench_split(args, w) -> int:
                      "algorithmic_bytes": nbytes},
         "cpu_baseline": None,
     }
+    prof = read_split_profile(w.name, tp)
+    if prof:
+        out["roofline"]["rocprof_kernel_ns"] = {k: float(v) for k, v in prof.items() if k.endswith("_avg_ns")}
+    if not args.no_cpu_baseline:
+        nthr = len(os.sched_getaffinity(0))
+        if os.environ.get("OMP_NUM_THREADS"):
+            nthr = min(nthr, int(os.environ["OMP_NUM_THREADS"]))
+        out["cpu_baseline"] = split_cpu_baseline(w, x, y, nbytes, nthr)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+SPLIT_SOURCES = ("ce_device.h", "lce_internal.h", "ce_split.hip", "ce_kernels.hip")
+
+
+def split_profile_path(workload: str, tp: int) -> str:
+    return os.path.join(PROFILES, f"ce_split__{workload}_tp{tp}.txt")
+
+
+def split_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SPLIT_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_split_profile(workload: str, tp: int) -> dict | None:
+    try:
+        lines = open(split_profile_path(workload, tp)).read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for line in lines:
+        if ": " in line and not line.startswith("#"):
+            k, v = line.split(": ", 1)
+            kv[k.strip()] = v.split()[0] if v.split() else ""
+    if kv.get("kernel_source_sha256_16") != split_source_hash():
+        return None
+    return kv
+
+
+def collect_profiles_split(workload: str, tp: int) -> int:
+    """Kernel trace of the split path's three kernels (stats per shard, combine, gradient per shard)."""
+    import synth
+    w = synth.WORKLOADS[workload]
+    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", f"{workload}_split_tp{tp}")
+    os.makedirs(raw, exist_ok=True)
+    base = ["--workload", workload, "--no-cpu-baseline", "--path", "split", "--tp", str(tp)]
+    _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
+    stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
+    b = " ".join(base)
+    lines = [
+        f"# rocprofv3 summary: split cross-entropy (lce_ce_stats per shard, lce_ce_combine, lce_ce_grad per shard),",
+        f"# workload {workload} ({w.n} x {w.V} {w.dtype}) as {tp} vocabulary shards of {w.V // tp} columns",
+        f"# made by: python bench.py --collect-profiles --workload {workload} --path split --tp {tp}",
+        "# which runs, from /tmp with TMPDIR=/tmp:",
+        f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 10 --warmup 3",
+        "# kernel trace (--stats), nanoseconds per launch (13 steps; stats and grad launch once per shard):",
+    ]
+    for r in stats:
+        lines.append(f"#   {r['Name'][:92]:<92} calls {r['Calls']:>4} avg {float(r['AverageNs']):>11.1f} "
+                     f"min {r['MinNs']:>9} max {r['MaxNs']:>9}")
+    for key, sub in (("stats", "ce_stats_kernel"), ("combine", "ce_combine"), ("grad", "ce_grad_kernel")):
+        rs = [r for r in stats if sub in r["Name"]]
+        if rs:
+            ns = sum(float(r["TotalDurationNs"]) for r in rs) / sum(int(r["Calls"]) for r in rs)
+            lines.append(f"{key}_avg_ns: {ns:.1f}")
+    shard_bytes = w.n * (w.V // tp) * w.elem_bytes
+    lines += [f"stats_bytes_per_launch: {shard_bytes}", f"grad_bytes_per_launch: {2 * shard_bytes}",
+              f"kernel_source_sha256_16: {split_source_hash()}"]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(split_profile_path(workload, tp), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(split_profile_path(workload, tp)).read(), flush=True)
     return 0
 
 
@@ -520,6 +623,8 @@ def main() -> int:
     args = parse()
     import synth
     if args.collect_profiles:
+        if args.path == "split":
+            return collect_profiles_split(args.workload, args.tp)
         if args.workload in synth.FLCE_WORKLOADS:
             return collect_profiles_flce(args.workload, args.path == "resident")
         return collect_profiles(args.workload)
