@@ -687,6 +687,15 @@ def main() -> int:
     per_call_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = wall * 1e3 / args.steps
     call_ms = float(np.mean(per_call_ms))
+    # context, after the timed region: a plain device copy of the same logits (one read + one write of
+    # N V b bytes, the same traffic as one call), HIP events around each copy
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a_, b_ in cev:
+        a_.record(stream)
+        bufs[0].copy_(pristine)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in cev]))
 
     nbytes = algorithmic_bytes(w)
     prof = read_profile(w.name)
@@ -716,7 +725,9 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "lce_ce_fwd_bwd call = one persistent row-kernel launch, HIP events per call",
                      "call_ms_mean": round(call_ms, 5), "call_ms_min": round(min(per_call_ms), 5),
-                     "call_ms_max": round(max(per_call_ms), 5), "algorithmic_bytes": nbytes},
+                     "call_ms_max": round(max(per_call_ms), 5), "algorithmic_bytes": nbytes,
+                     "copy_GBps_same_bytes": round(2 * w.n * w.V * w.elem_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                     "workspace_bytes": int(ws.numel())},
         "cpu_baseline": None,
     }
     if w.n == 2048 and w.V == 131072 and w.dtype == "bf16":
