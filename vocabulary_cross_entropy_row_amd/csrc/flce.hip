@@ -17,6 +17,7 @@
 // (once per call), H_c^T and G_c^T are produced by a bandwidth-bound
 // transpose first.  Only one chunk of logits exists at a time.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "ce_device.h"
@@ -86,12 +87,33 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *in,
 // out[m][n] = bf16(sum_s part[s][m][n])   (part rows of stride N, splits of stride split_stride)
 __global__ __launch_bounds__(256) void splitk_fold_kernel(const float *part, int64_t split_stride, int splits,
                                                           uint16_t *out, int64_t ld_out, int M, int N) {
-    const int64_t total = static_cast<int64_t>(M) * N;
-    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += static_cast<int64_t>(gridDim.x) * 256) {
-        float s = 0.0f;
-        for (int k = 0; k < splits; ++k) s += part[k * split_stride + i];
+    // four consecutive columns per thread (N is a multiple of 8); the splits are
+    // added in index order, two loads in flight
+    typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+    const int64_t total4 = static_cast<int64_t>(M) * N / 4;
+    for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < total4; q += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i = q * 4;
+        float4 s = *reinterpret_cast<const float4 *>(part + i);
+        int k = 1;
+        for (; k + 1 < splits; k += 2) {
+            const float4 a = *reinterpret_cast<const float4 *>(part + k * split_stride + i);
+            const float4 b = *reinterpret_cast<const float4 *>(part + (k + 1) * split_stride + i);
+            s.x = (s.x + a.x) + b.x;
+            s.y = (s.y + a.y) + b.y;
+            s.z = (s.z + a.z) + b.z;
+            s.w = (s.w + a.w) + b.w;
+        }
+        if (k < splits) {
+            const float4 a = *reinterpret_cast<const float4 *>(part + k * split_stride + i);
+            s.x += a.x;
+            s.y += a.y;
+            s.z += a.z;
+            s.w += a.w;
+        }
         const int64_t m = i / N, n = i - m * N;
-        reinterpret_cast<__bf16 *>(out)[m * ld_out + n] = static_cast<__bf16>(s);
+        // converted straight into the store (RNE)
+        *reinterpret_cast<bf4 *>(reinterpret_cast<__bf16 *>(out) + m * ld_out + n) =
+            (bf4){static_cast<__bf16>(s.x), static_cast<__bf16>(s.y), static_cast<__bf16>(s.z), static_cast<__bf16>(s.w)};
     }
 }
 
@@ -327,8 +349,12 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             if ((e = gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H), static_cast<int>(V), splits,
                              C * H, st)) != hipSuccess)
                 return e;
-            hipLaunchKernelGGL(splitk_fold_kernel, dim3(1024), dim3(256), 0, st, part, C * H, splits,
-                               static_cast<uint16_t *>(f.grad_hidden) + c0 * H, H, cn, static_cast<int>(H));
+            {
+                const int64_t quads = static_cast<int64_t>(cn) * H / 4;
+                const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((quads + 255) / 256, 8192));
+                hipLaunchKernelGGL(splitk_fold_kernel, dim3(blocks), dim3(256), 0, st, part, C * H, splits,
+                                   static_cast<uint16_t *>(f.grad_hidden) + c0 * H, H, cn, static_cast<int>(H));
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
             // G_c^T into columns [c0 - g0, ...) of the group's [V, ldg] buffer
             if ((e = transpose(z, V, gt + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(V), st)) != hipSuccess)
