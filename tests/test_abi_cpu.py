@@ -265,3 +265,13 @@ def test_flce_stats_bytes():
     assert lce.lce_flce_stats_bytes(4096, 202048) == 4096 * 790 * 32
     assert lce.lce_flce_stats_bytes(3, 8) == 3 * 32
     assert lce.lce_flce_stats_bytes(-1, 8) == 0
+
+
+def test_build_families_match_the_kernel_table():
+    """The (register rounds, LDS rounds) families the build instantiates are the ones the launcher picks from."""
+    from vocabulary_cross_entropy_row_amd import build
+    src = open(os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc", "ce_kernels.hip")).read()
+    line = re.search(r"#define LCE_FAMILIES\(X\)(.*)", src).group(1)
+    fams = [tuple(int(v) for v in m) for m in re.findall(r"X\((\d+),\s*(\d+)\)", line)]
+    assert fams == [tuple(f) for f in build.FAMILIES]
+    assert [a + b for a, b in fams] == sorted(a + b for a, b in fams)

@@ -120,6 +120,10 @@ SHAPES = [  # (n, V, ld, dtype): register path with full / partial last round, K
     (16, 1000, 1000, "f32"),
     (8, 60000, 60000, "f32"),                                       # f32 K=15
     (4, 120000, 120000, "f32"),                                     # f32 too wide -> generic
+    (2, 204800, 204800, "bf16"),                                    # widest resident bf16 row (K=25)
+    (2, 204808, 204808, "bf16"),                                    # one vector more -> generic
+    (2, 102400, 102400, "f32"),                                     # widest resident f32 row
+    (2, 102404, 102404, "f32"),                                     # one vector more -> generic
 ]
 
 

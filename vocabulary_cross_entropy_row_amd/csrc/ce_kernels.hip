@@ -298,7 +298,9 @@ bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, i
     if (V % E != 0 || ld % E != 0) return false;
     if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0) return false;
     const int64_t need = (V / E + NT - 1) / NT;   // rounds of 1024 vectors
-    static const int fam[][2] = {{1, 0}, {2, 0}, {4, 0}, {8, 0}, {4, 8}, {8, 8}, {10, 9}, {13, 9}, {16, 9}};
+#define LCE_FAM_ENTRY(r, l) {r, l},
+    static const int fam[][2] = {LCE_FAMILIES(LCE_FAM_ENTRY)};   // in increasing K = KR + KL
+#undef LCE_FAM_ENTRY
     for (const auto &f : fam)
         if (f[0] + f[1] >= need) {
             *kr = f[0];
