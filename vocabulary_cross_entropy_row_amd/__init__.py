@@ -116,6 +116,58 @@ def _dtype_code(t) -> int:
     raise TypeError(f"logits must be bfloat16 or float32, not {t.dtype}")
 
 
+# Every tensor reaches the library as a raw device pointer, so its device, dtype, layout and size are
+# checked here: a host tensor or a short buffer would otherwise be read by a kernel.
+
+def _on_gpu(t, name: str):
+    import torch
+    if not torch.is_tensor(t):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}): the library takes device pointers")
+    return t.device
+
+
+def _buf(t, name: str, dtype, numel: int, device, required: bool = False) -> None:
+    import torch
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not torch.is_tensor(t):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements (got {t.numel()})")
+
+
+def _grad_out(grad_out, reduction: str, n: int, device):
+    """The upstream gradient as the library reads it: fp32, contiguous, one value per token for
+    reduction 'none' (a Python number is broadcast), else one value."""
+    import torch
+    if grad_out is None:
+        return None
+    need = n if reduction == "none" else 1
+    if not torch.is_tensor(grad_out):
+        return torch.full((max(need, 1),), float(grad_out), dtype=torch.float32, device=device)
+    if grad_out.device != device:
+        raise ValueError(f"grad_out must be on {device} (got {grad_out.device})")
+    g = grad_out.to(torch.float32).reshape(-1).contiguous()
+    if g.numel() < need:
+        raise ValueError(f"grad_out needs {need} value(s) for reduction {reduction!r} (got {g.numel()})")
+    return g
+
+
+def _ws(workspace, need: int, device) -> None:
+    import torch
+    _buf(workspace, "workspace", torch.uint8, need, device, required=True)
+
+
 @dataclass
 class CEResult:
     loss_tok: object      # fp32 [n]
@@ -135,11 +187,9 @@ def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing:
         raise ValueError("logits must be a 2-D view with unit column stride")
     n, V = logits.shape
     ld = logits.stride(0) if n > 1 else V
-    dev = logits.device
-    if grad_out is not None and not torch.is_tensor(grad_out):
-        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=dev)
-    elif grad_out is not None and grad_out.dtype != torch.float32:
-        grad_out = grad_out.float()
+    dev = _on_gpu(logits, "logits")
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
+    grad_out = _grad_out(grad_out, reduction, n, dev)
     if loss_tok is None:
         loss_tok = torch.empty(n, dtype=torch.float32, device=dev)
     if loss_out is None:
@@ -151,6 +201,11 @@ def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing:
     wsb = lce_ce_workspace_bytes(n, V)
     if workspace is None:
         workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    _buf(loss_tok, "loss_tok", torch.float32, n, dev)
+    _buf(loss_out, "loss_out", torch.float32, 1, dev)
+    _buf(argmax_out, "argmax_out", torch.int64, n, dev)
+    _buf(counts, "counts", torch.int64, 3, dev)
+    _ws(workspace, wsb, dev)
     st = lib().lce_ce_fwd_bwd(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V, int(ignore_index),
                               float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                               _ptr(loss_tok), _ptr(loss_out), _ptr(argmax_out), _ptr(counts), _ptr(workspace),
@@ -167,11 +222,14 @@ def lce_ce_argmax(logits, labels=None, *, ignore_index: int = -100, argmax_out=N
         raise ValueError("logits must be a 2-D view with unit column stride")
     n, V = logits.shape
     ld = logits.stride(0) if n > 1 else V
-    dev = logits.device
+    dev = _on_gpu(logits, "logits")
+    _buf(labels, "labels", torch.int64, n, dev)
     if argmax_out is None:
         argmax_out = torch.empty(n, dtype=torch.int64, device=dev)
     if counts is None:
         counts = torch.empty(3, dtype=torch.int64, device=dev)
+    _buf(argmax_out, "argmax_out", torch.int64, n, dev)
+    _buf(counts, "counts", torch.int64, 3, dev)
     st = lib().lce_ce_argmax(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V, int(ignore_index),
                              _ptr(argmax_out), _ptr(counts), _stream(stream))
     _check(st)
@@ -196,8 +254,11 @@ def lce_ce_stats(shard, labels, *, v_offset: int = 0, ignore_index: int = -100, 
     returns its stats records, fp32 [n, 8]."""
     import torch
     n, Vs, ld = _shard_view(shard)
+    dev = _on_gpu(shard, "shard")
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
     if stats is None:
-        stats = torch.empty((n, STATS_FLOATS), dtype=torch.float32, device=shard.device)
+        stats = torch.empty((n, STATS_FLOATS), dtype=torch.float32, device=dev)
+    _buf(stats, "stats", torch.float32, n * STATS_FLOATS, dev)
     _check(lib().lce_ce_stats(_ptr(shard), ld, _dtype_code(shard), _ptr(labels), n, Vs, int(v_offset),
                               int(ignore_index), float(softcap), _ptr(stats), _stream(stream)))
     return stats
@@ -222,10 +283,11 @@ def lce_ce_combine(stats, labels, V: int, *, ignore_index: int = -100, label_smo
     import torch
     if stats.dim() == 2:
         stats = stats.unsqueeze(0)
-    if not stats.is_contiguous() or stats.size(2) != STATS_FLOATS:
+    if not stats.is_contiguous() or stats.dim() != 3 or stats.size(2) != STATS_FLOATS or stats.dtype != torch.float32:
         raise ValueError("stats must be a contiguous [shards, n, 8] fp32 tensor")
     shards, n = stats.shape[0], stats.shape[1]
-    dev = stats.device
+    dev = _on_gpu(stats, "stats")
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
     f = lambda: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
     out = SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=dev), f(), f(),
                     torch.empty(n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
@@ -242,10 +304,12 @@ def lce_ce_grad(shard, labels, V: int, rows: SplitRows, *, v_offset: int = 0, ig
     """Write the gradient of one shard in place, from the combined row results."""
     import torch
     n, Vs, ld = _shard_view(shard)
-    if grad_out is not None and not torch.is_tensor(grad_out):
-        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=shard.device)
-    elif grad_out is not None and grad_out.dtype != torch.float32:
-        grad_out = grad_out.float()
+    dev = _on_gpu(shard, "shard")
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
+    grad_out = _grad_out(grad_out, reduction, n, dev)
+    _buf(rows.lse, "rows.lse", torch.float32, n, dev, required=True)
+    _buf(rows.one_minus_py, "rows.one_minus_py", torch.float32, n, dev, required=True)
+    _buf(rows.counts, "rows.counts", torch.int64, 3, dev, required=True)
     _check(lib().lce_ce_grad(_ptr(shard), ld, _dtype_code(shard), _ptr(labels), n, Vs, int(v_offset), int(V),
                              int(ignore_index), float(label_smoothing), float(softcap), REDUCTIONS[reduction],
                              _ptr(grad_out), _ptr(rows.lse), _ptr(rows.one_minus_py), _ptr(rows.counts),
@@ -343,16 +407,11 @@ def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_
     """Fused linear cross-entropy of hidden [n, H] (bf16) and weight [V, H] (bf16), chunked over
     tokens.  Outputs not passed in are allocated."""
     import torch
-    for t, nm in ((hidden, "hidden"), (weight, "weight")):
-        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous 2-D bfloat16 tensor")
+    dev = _check_flce_operands(hidden, weight)
     n, H = hidden.shape
     V = weight.shape[0]
-    dev = hidden.device
-    if grad_out is not None and not torch.is_tensor(grad_out):
-        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=dev)
-    elif grad_out is not None and grad_out.dtype != torch.float32:
-        grad_out = grad_out.float()
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
+    grad_out = _grad_out(grad_out, reduction, n, dev)
     if loss_tok is None:
         loss_tok = torch.empty(n, dtype=torch.float32, device=dev)
     if loss_out is None:
@@ -366,6 +425,12 @@ def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_
     wsb = lce_flce_workspace_bytes(n, H, V, chunk_tokens)
     if workspace is None:
         workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    _buf(loss_tok, "loss_tok", torch.float32, n, dev)
+    _buf(loss_out, "loss_out", torch.float32, 1, dev)
+    _buf(grad_hidden, "grad_hidden", torch.bfloat16, n * H, dev)
+    _buf(grad_weight, "grad_weight", torch.float32, V * H, dev)
+    _buf(counts, "counts", torch.int64, 3, dev)
+    _ws(workspace, 1, dev)   # the library checks the size against the layout it needs
     st = lib().lce_flce_fwd_bwd(_ptr(hidden), _ptr(weight), _ptr(labels), n, H, V, int(ignore_index),
                                 float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                                 int(chunk_tokens), _ptr(loss_tok), _ptr(loss_out), _ptr(grad_hidden),
@@ -382,10 +447,17 @@ def lce_flce_stats_bytes(n: int, V: int) -> int:
 
 
 def _check_flce_operands(hidden, weight):
+    """Both operands contiguous 2-D bf16 on one GPU, sharing H; returns that device."""
     import torch
     for t, nm in ((hidden, "hidden"), (weight, "weight")):
-        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+        if not torch.is_tensor(t) or t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous 2-D bfloat16 tensor")
+    dev = _on_gpu(hidden, "hidden")
+    if weight.device != dev:
+        raise ValueError(f"weight must be on {dev} (got {weight.device})")
+    if weight.shape[1] != hidden.shape[1]:
+        raise ValueError(f"hidden [n, {hidden.shape[1]}] and weight [V, {weight.shape[1]}] disagree on H")
+    return dev
 
 
 def lce_flce_forward(hidden, weight, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
@@ -394,16 +466,22 @@ def lce_flce_forward(hidden, weight, labels, *, ignore_index: int = -100, label_
     """Loss, log-sum-exp, 1 - p_y, log p_y, entropy, argmax and counts of the logits hidden weight^T,
     formed tile by tile and never stored.  ``out`` (optional) supplies the output tensors."""
     import torch
-    _check_flce_operands(hidden, weight)
+    dev = _check_flce_operands(hidden, weight)
     n, H = hidden.shape
     V = weight.shape[0]
-    dev = hidden.device
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
     if out is None:
         f = lambda: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
         out = SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=dev), f(), f(),
                         torch.empty(n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
     if workspace is None:
         workspace = torch.empty(max(lce_flce_stats_bytes(n, V), 1), dtype=torch.uint8, device=dev)
+    for name in ("lse", "one_minus_py", "loss_tok", "logprob", "entropy"):
+        _buf(getattr(out, name), f"out.{name}", torch.float32, n, dev)
+    _buf(out.loss_out, "out.loss_out", torch.float32, 1, dev)
+    _buf(out.argmax, "out.argmax", torch.int64, n, dev)
+    _buf(out.counts, "out.counts", torch.int64, 3, dev, required=True)
+    _ws(workspace, lce_flce_stats_bytes(n, V), dev)
     _check(lib().lce_flce_forward(_ptr(hidden), _ptr(weight), _ptr(labels), n, H, V, int(ignore_index),
                                   float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(out.loss_tok),
                                   _ptr(out.loss_out), _ptr(out.lse), _ptr(out.one_minus_py), _ptr(out.logprob),
@@ -417,20 +495,23 @@ def lce_flce_backward(hidden, weight, labels, rows: SplitRows, *, ignore_index: 
                       chunk_tokens: int = 1024, grad_hidden=None, grad_weight=None, workspace=None, stream=None):
     """grad_hidden (bf16 [n, H]) and grad_weight (fp32 [V, H]) from the forward's rows."""
     import torch
-    _check_flce_operands(hidden, weight)
+    dev = _check_flce_operands(hidden, weight)
     n, H = hidden.shape
     V = weight.shape[0]
-    dev = hidden.device
-    if grad_out is not None and not torch.is_tensor(grad_out):
-        grad_out = torch.full((1,), float(grad_out), dtype=torch.float32, device=dev)
-    elif grad_out is not None and grad_out.dtype != torch.float32:
-        grad_out = grad_out.float()
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
+    grad_out = _grad_out(grad_out, reduction, n, dev)
+    _buf(rows.lse, "rows.lse", torch.float32, n, dev, required=True)
+    _buf(rows.one_minus_py, "rows.one_minus_py", torch.float32, n, dev, required=True)
+    _buf(rows.counts, "rows.counts", torch.int64, 3, dev, required=True)
     if grad_hidden is None:
         grad_hidden = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
     if grad_weight is None:
         grad_weight = torch.empty((V, H), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = torch.empty(lce_flce_workspace_bytes(n, H, V, chunk_tokens), dtype=torch.uint8, device=dev)
+    _buf(grad_hidden, "grad_hidden", torch.bfloat16, n * H, dev)
+    _buf(grad_weight, "grad_weight", torch.float32, V * H, dev)
+    _ws(workspace, 1, dev)   # the library checks the size against the layout it needs
     _check(lib().lce_flce_backward(_ptr(hidden), _ptr(weight), _ptr(labels), n, H, V, int(ignore_index),
                                    float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                                    int(chunk_tokens), _ptr(rows.lse), _ptr(rows.one_minus_py), _ptr(rows.counts),
