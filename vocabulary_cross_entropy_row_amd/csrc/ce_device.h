@@ -112,6 +112,58 @@ template <> struct Elt<false> {
 // Butterfly (xor) shuffles: every lane ends with the same value because each
 // step combines the same two operands (IEEE max/add are commutative).
 
+// DPP lane exchanges (VALU, no LDS round trip): within each quad the partner
+// at xor 1 and xor 2, then the mirror within each 8 lanes and within each 16
+// lanes.  After the four steps every lane of a 16-lane row holds the row's
+// combination; the four rows are then read out and combined in a fixed order.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// (m, s) pairs of an online softmax: s is a sum of exponentials relative to m.
+__device__ __forceinline__ void lse_combine(float &m, float &s, float m2, float s2) {
+    const float mx = fmaxf(m, m2);
+    s = s * exp2_fast((m - mx) * kLog2e) + s2 * exp2_fast((m2 - mx) * kLog2e);
+    m = mx;
+}
+template <int CTRL>
+__device__ __forceinline__ void lse_step(float &m, float &s) {
+    const float m2 = dpp_f<CTRL>(m), s2 = dpp_f<CTRL>(s);
+    lse_combine(m, s, m2, s2);
+}
+// the wave's combined (m, s), the same in every lane
+__device__ __forceinline__ void wave_lse(float &m, float &s) {
+    lse_step<kDppXor1>(m, s);
+    lse_step<kDppXor2>(m, s);
+    lse_step<kDppHalfMirror>(m, s);
+    lse_step<kDppMirror>(m, s);
+    float m0 = lane_f(m, 0), s0 = lane_f(s, 0);
+    float m1 = lane_f(m, 32), s1 = lane_f(s, 32);
+    lse_combine(m0, s0, lane_f(m, 16), lane_f(s, 16));
+    lse_combine(m1, s1, lane_f(m, 48), lane_f(s, 48));
+    lse_combine(m0, s0, m1, s1);
+    m = m0;
+    s = s0;
+}
+// the wave's sum, the same in every lane
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -151,6 +203,27 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
         const int i2 = __shfl_xor(i, o, 64);
         argmax_combine(v, i, v2, i2);
     }
+}
+
+// the wave's (value, first index), the same in every lane, on the DPP path
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float &v, int &i) {
+    const float v2 = dpp_f<CTRL>(v);
+    const int i2 = dpp_i<CTRL>(i);
+    argmax_combine(v, i, v2, i2);
+}
+__device__ __forceinline__ void wave_argmax_dpp(float &v, int &i) {
+    argmax_step<kDppXor1>(v, i);
+    argmax_step<kDppXor2>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    float v0 = lane_f(v, 0), v1 = lane_f(v, 32);
+    int i0 = __builtin_amdgcn_readlane(i, 0), i1 = __builtin_amdgcn_readlane(i, 32);
+    argmax_combine(v0, i0, lane_f(v, 16), __builtin_amdgcn_readlane(i, 16));
+    argmax_combine(v1, i1, lane_f(v, 48), __builtin_amdgcn_readlane(i, 48));
+    argmax_combine(v0, i0, v1, i1);
+    v = v0;
+    i = i0;
 }
 
 // Block reductions: one LDS slot per wave, then every thread folds the slots

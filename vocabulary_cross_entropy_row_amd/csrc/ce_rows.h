@@ -300,27 +300,21 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         // combine the threads' (m, s) pairs, then the argmax and sum z
         {
             float mw = m, sw = s;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float m2 = __shfl_xor(mw, o, 64), s2 = __shfl_xor(sw, o, 64);
-                const float mx = fmaxf(mw, m2);
-                sw = sw * exp2_fast((mw - mx) * kLog2e) + s2 * exp2_fast((m2 - mx) * kLog2e);
-                mw = mx;
-            }
+            wave_lse(mw, sw);   // DPP exchanges, no LDS round trips
             if ((tid & 63) == 0) {
                 sh_m[pb][tid >> 6] = mw;
                 sh_s[pb][tid >> 6] = sw;
             }
             if constexpr (ARGMAX) {
                 am = am_k < 0 ? 0x7fffffff : (am_k * NT + tid) * E + am_e;
-                wave_argmax(amv, am);
+                wave_argmax_dpp(amv, am);
                 if ((tid & 63) == 0) {
                     sh_z[pb][tid >> 6] = amv;
                     sh_i[pb][tid >> 6] = am;
                 }
             }
             if constexpr (SMOOTH) {
-                zs = wave_sum(zs);
+                zs = wave_sum_dpp(zs);
                 if ((tid & 63) == 0) sh_zs[pb][tid >> 6] = zs;
             }
             __syncthreads();

@@ -54,6 +54,40 @@ __device__ __forceinline__ void combine(Part &a, float m2, float s2, float e2) {
     a.m = M;
 }
 
+template <int CTRL>
+__device__ __forceinline__ void part_step(Part &p) {
+    const float m2 = dev::dpp_f<CTRL>(p.m), s2 = dev::dpp_f<CTRL>(p.s), e2 = dev::dpp_f<CTRL>(p.e);
+    const float z2 = dev::dpp_f<CTRL>(p.zs);
+    combine(p, m2, s2, e2);
+    p.zs += z2;
+}
+// the wave's (m, s, e, sum z), the same in every lane (each step combines the
+// same two operands in both lanes)
+__device__ __forceinline__ void wave_part(Part &p) {
+    part_step<dev::kDppXor1>(p);
+    part_step<dev::kDppXor2>(p);
+    part_step<dev::kDppHalfMirror>(p);
+    part_step<dev::kDppMirror>(p);
+    Part r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        r[q].m = dev::lane_f(p.m, 16 * q);
+        r[q].s = dev::lane_f(p.s, 16 * q);
+        r[q].e = dev::lane_f(p.e, 16 * q);
+        r[q].zs = dev::lane_f(p.zs, 16 * q);
+    }
+    combine(r[0], r[1].m, r[1].s, r[1].e);
+    r[0].zs += r[1].zs;
+    combine(r[2], r[3].m, r[3].s, r[3].e);
+    r[2].zs += r[3].zs;
+    combine(r[0], r[2].m, r[2].s, r[2].e);
+    r[0].zs += r[2].zs;
+    p.m = r[0].m;
+    p.s = r[0].s;
+    p.e = r[0].e;
+    p.zs = r[0].zs;
+}
+
 constexpr int kStatsThreads = 256;                    // four waves per row: several rows per CU
 constexpr int kStatsWaves = kStatsThreads / 64;
 constexpr int kStatsAhead = 8;                        // 16-byte vectors each thread keeps in flight
@@ -132,13 +166,9 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
             p.m = mn;
         }
     }
-    // wave, then workgroup
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        combine(p, __shfl_xor(p.m, o, 64), __shfl_xor(p.s, o, 64), __shfl_xor(p.e, o, 64));
-        p.zs += __shfl_xor(p.zs, o, 64);
-    }
-    dev::wave_argmax(p.amv, p.am);
+    // wave (DPP exchanges, then the four 16-lane rows in a fixed order), then workgroup
+    wave_part(p);
+    dev::wave_argmax_dpp(p.amv, p.am);
     const int w = tid >> 6;
     if ((tid & 63) == 0) {
         sh[0][w] = p.m;
