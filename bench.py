@@ -48,6 +48,13 @@ CSRC = os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def call_percentiles(ms, nd: int) -> dict:
+    """Median and 10th / 90th percentiles of the per-call times (HIP events)."""
+    import numpy as np
+    return {"call_ms_median": round(float(np.median(ms)), nd), "call_ms_p10": round(float(np.percentile(ms, 10)), nd),
+            "call_ms_p90": round(float(np.percentile(ms, 90)), nd)}
+
+
 def algorithmic_bytes(w) -> int:
     # one read + one write of the logits, 8 B label read + 4 B loss write per token
     return 2 * w.n * w.V * w.elem_bytes + 12 * w.n
@@ -361,7 +368,8 @@ def bench_flce(args, w) -> int:
                      "kernel": ("lce_flce_forward + lce_flce_backward" if resident else "lce_flce_fwd_bwd call") +
                                " (all GEMM, CE and transpose launches), HIP events per step",
                      "call_ms_mean": round(call_ms, 4), "call_ms_min": round(min(per_call_ms), 4),
-                     "call_ms_max": round(max(per_call_ms), 4), "algorithmic_flops": flops},
+                     "call_ms_max": round(max(per_call_ms), 4), **call_percentiles(per_call_ms, 4),
+                     "algorithmic_flops": flops},
         "cpu_baseline": None,
     }
     if resident:
@@ -725,7 +733,8 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "lce_ce_fwd_bwd call = one persistent row-kernel launch, HIP events per call",
                      "call_ms_mean": round(call_ms, 5), "call_ms_min": round(min(per_call_ms), 5),
-                     "call_ms_max": round(max(per_call_ms), 5), "algorithmic_bytes": nbytes,
+                     "call_ms_max": round(max(per_call_ms), 5), **call_percentiles(per_call_ms, 5),
+                     "algorithmic_bytes": nbytes,
                      "copy_GBps_same_bytes": round(2 * w.n * w.V * w.elem_bytes / (copy_ms * 1e-3) / 1e9, 1),
                      "workspace_bytes": int(ws.numel())},
         "cpu_baseline": None,
