@@ -185,18 +185,19 @@ lce_status lce_ce_grad(void *logits_inout, int64_t ld, lce_dtype dtype, const in
 
 /*
  * Bytes of device workspace lce_flce_fwd_bwd uses by default (0 for invalid
- * sizes).  It holds W^T [H, V], one chunk of logits [C, V], split-K partials
- * [16, C, H] fp32, and the transposed gradients and hidden states of one
- * grad_weight group, [V + H, G] bf16: about 2 H V + 2 C V + 64 C H + 2 (V + H) G
- * bytes with C = min(chunk, n).  The default group G is as many chunks as
+ * sizes), the fastest layout.  It holds W^T [H, V] bf16 (so that the
+ * grad_hidden GEMM reads W K-contiguous), one chunk of logits [C, V], split-K
+ * partials [16, C, H] fp32, and the transposed gradients and hidden states of
+ * one grad_weight group, [V + H, G] bf16: about 2 H V + 2 C V + 64 C H +
+ * 2 (V + H) G bytes with C = min(chunk, n).  The default group G is as many chunks as
  * 2 GiB holds (at least one, at most all n tokens); grad_weight is written once
  * per group, so fewer groups mean less grad_weight traffic.
  */
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens);
 
 /*
- * Bytes of workspace for grad_weight groups of group_chunks chunks (0 for
- * invalid sizes); group_chunks = 1 is the smallest workspace
+ * Bytes of workspace for grad_weight groups of group_chunks chunks without the
+ * W^T copy (0 for invalid sizes); group_chunks = 1 is the smallest workspace
  * lce_flce_fwd_bwd accepts.
  */
 size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens,
@@ -224,7 +225,10 @@ size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t
  *                lce_flce_workspace_bytes_grouped(n, H, V, chunk_tokens, 1)
  *                bytes (LCE_ERR_INVALID_ARG otherwise).  The call uses the
  *                largest grad_weight group, up to the default one, whose
- *                layout fits workspace_bytes.
+ *                layout fits workspace_bytes without W^T, and adds the W^T
+ *                copy when the rest of the workspace holds it too; without
+ *                it the grad_hidden GEMM reads W in place (about 15% slower
+ *                for that GEMM, 2 H V bytes less workspace).
  * Logits are formed in fp32 by bf16 MFMA and stored as bf16 for the row
  * kernel.  H and V must be multiples of 8 (LCE_ERR_UNSUPPORTED otherwise).
  */

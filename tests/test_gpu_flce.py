@@ -125,6 +125,22 @@ def test_flce_grad_weight_groups(group_chunks):
     assert torch.equal(grouped.grad_hidden, one_pass.grad_hidden)
 
 
+@pytest.mark.parametrize("n,H,V", [(300, 520, 1000), (130, 136, 4104)])
+def test_flce_weight_read_in_place(n, H, V):
+    """A workspace without room for W^T makes the grad_hidden GEMM read W in place (k-major operand,
+    transposing LDS reads): the same eight k values reach every lane in the same order, so grad_hidden is
+    bitwise that of the W^T path, and everything matches the oracle."""
+    hb, wb, y = gen(n, H, V, seed=n + V)
+    chunks = -(-n // 64)
+    _, o, _, _ = check_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64, group_chunks=chunks)
+    in_place = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64, group_chunks=chunks)
+    with_wt = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64)
+    assert lce.lce_flce_workspace_bytes(n, H, V, 64) - lce.lce_flce_workspace_bytes_grouped(n, H, V, 64, chunks) \
+        >= H * V * 2
+    assert torch.equal(in_place.grad_hidden, with_wt.grad_hidden)
+    assert torch.equal(in_place.grad_weight, with_wt.grad_weight)
+
+
 def test_flce_chunk_invariance():
     """The chunk size changes only the order of fp32 accumulation in grad_weight."""
     hb, wb, y = gen(192, 256, 2048, seed=5)

@@ -8,14 +8,19 @@
 //   Z_c  = H_c W^T           bf16 MFMA GEMM, fp32 accumulate, stored bf16 [chunk, V]
 //   G_c  = CE(Z_c)           the resident row kernel, in place, with the mean
 //                            scale of all n tokens; per-token losses
-//   dH_c = G_c W             split-K MFMA GEMM into fp32 partials, folded to bf16
+//   dH_c = G_c W             split-K MFMA GEMM into fp32 partials, folded to bf16;
+//                            from W^T (transposed once per call) when the
+//                            workspace holds it, else from W in place (k-major
+//                            B operand, transposing LDS reads: 2 H V bytes less
+//                            workspace, ~15% slower GEMM)
 //   G_c^T, H_c^T             appended to the current group's transposed buffers
 // and once per group of chunks (as many as kFlceGroupBytes holds):
 //   dW (+)= G_g^T H_g        MFMA GEMM over the group's tokens, fp32 (written
 //                            by the first group, read-modify-written by later ones)
-// Every GEMM runs in the one "A K-contiguous, B K-contiguous" form, so W^T
-// (once per call), H_c^T and G_c^T are produced by a bandwidth-bound
-// transpose first.  Only one chunk of logits exists at a time.
+// The dW GEMM runs in the "A K-contiguous, B K-contiguous" form, so H_c^T and
+// G_c^T come from a bandwidth-bound transpose (reading both dW operands
+// k-major measured 15% slower than transposing them).  Only one chunk of
+// logits exists at a time.
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <stdint.h>
@@ -152,25 +157,30 @@ hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, i
     return hipGetLastError();
 }
 
-template <int MODE, bool SOFTCAP = false>
+template <int MODE, bool SOFTCAP = false, bool B_KN = false>
 void launch_gemm(const GemmArgs &g, bool ktail, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u), block(gemm::NTHR);
-    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true, SOFTCAP>), grid, block, 0, st, g);
-    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false, SOFTCAP>), grid, block, 0, st, g);
+    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true, SOFTCAP, false, B_KN>), grid, block, 0, st, g);
+    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false, SOFTCAP, false, B_KN>), grid, block, 0, st, g);
 }
 
 // C (+)= A B^T over [M, N] with K split into `splits` ranges; the cross-entropy
-// modes (OUT_STATS, OUT_GRAD) take their inputs from *ce and run unsplit.
+// modes (OUT_STATS, OUT_GRAD) take their inputs from *ce and run unsplit.  With
+// b_kn, B is stored k-major ([K][N], row stride ldb: C (+)= A B) and is read in
+// place through transposing LDS reads (OUT_F32 only).
 hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, int M,
                    int N, int K, int splits, int64_t c_split_stride, hipStream_t st,
-                   const gemm::CeEpi *ce = nullptr) {
+                   const gemm::CeEpi *ce = nullptr, bool b_kn = false) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if ((K & 7) || (lda & 7) || (ldb & 7) || (reinterpret_cast<uintptr_t>(A) & 15) ||
         (reinterpret_cast<uintptr_t>(B) & 15))
         return hipErrorInvalidValue;
-    // 32-bit buffer offsets: a tile's rows plus one step of K read ahead
-    const int64_t ldmax = lda > ldb ? lda : ldb;
+    // 32-bit buffer offsets: a tile's rows plus one step of K read ahead (K-contiguous operands);
+    // the whole [K][ldb] matrix (k-major B, whose N must be whole 16-byte chunks)
+    const int64_t ldmax = b_kn ? lda : (lda > ldb ? lda : ldb);
     if (256 * ldmax * 2 + (static_cast<int64_t>(K) + 2 * gemm::BK) * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    if (b_kn && ((N & 7) || static_cast<int64_t>(K) * ldb * 2 >= (int64_t(1) << 32) || mode != gemm::OUT_F32))
+        return hipErrorInvalidValue;
     GemmArgs g;
     g.A = static_cast<const uint16_t *>(A);
     g.B = static_cast<const uint16_t *>(B);
@@ -199,7 +209,8 @@ hipError_t gemm_nt(int mode, const void *A, int64_t lda, const void *B, int64_t 
             if (sc) launch_gemm<gemm::OUT_GRAD, true>(g, ktail, st);
             else launch_gemm<gemm::OUT_GRAD, false>(g, ktail, st);
         }
-    } else if (mode == gemm::OUT_BF16) launch_gemm<gemm::OUT_BF16>(g, ktail, st);
+    } else if (b_kn) launch_gemm<gemm::OUT_F32, false, true>(g, ktail, st);
+    else if (mode == gemm::OUT_BF16) launch_gemm<gemm::OUT_BF16>(g, ktail, st);
     else if (mode == gemm::OUT_F32) launch_gemm<gemm::OUT_F32>(g, ktail, st);
     else launch_gemm<gemm::OUT_F32_ACC>(g, ktail, st);
     return hipGetLastError();
@@ -244,7 +255,7 @@ int64_t flce_default_group_chunks(int64_t n, int64_t H, int64_t V, int64_t chunk
     return cpg < 1 ? 1 : (cpg > nchunks ? nchunks : cpg);
 }
 
-FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t group_chunks) {
+FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t group_chunks, bool with_wt) {
     FlceLayout L;
     const int64_t C = chunk < n ? chunk : (n > 0 ? n : 1);
     L.chunk = C;
@@ -253,7 +264,8 @@ FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t g
     L.group = cpg * C;
     L.ldg = round_up(L.group, 64);
     size_t off = 0;
-    L.off_wt = off;    off += align256(static_cast<size_t>(H) * V * 2);
+    L.off_wt = off;
+    if (with_wt) off += align256(static_cast<size_t>(H) * V * 2);
     L.off_z = off;     off += align256(static_cast<size_t>(C) * V * 2);
     L.off_gt = off;    off += align256(static_cast<size_t>(V) * L.ldg * 2);
     L.off_ht = off;    off += align256(static_cast<size_t>(H) * L.ldg * 2);
@@ -263,11 +275,18 @@ FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t g
     return L;
 }
 
+bool flce_plan(int64_t n, int64_t H, int64_t V, int64_t chunk, size_t bytes, int64_t *group_chunks, bool *with_wt) {
+    int64_t group = flce_default_group_chunks(n, H, V, chunk);
+    while (group > 1 && flce_layout(n, H, V, chunk, group, false).bytes > bytes) --group;
+    *group_chunks = group;
+    *with_wt = flce_layout(n, H, V, chunk, group, true).bytes <= bytes;
+    return flce_layout(n, H, V, chunk, group, false).bytes <= bytes;
+}
+
 hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     hipError_t e;
-    const FlceLayout L = flce_layout(f.n, f.H, f.V, f.chunk, f.group_chunks);
+    const FlceLayout L = flce_layout(f.n, f.H, f.V, f.chunk, f.group_chunks, f.with_wt);
     char *ws = static_cast<char *>(f.workspace);
-    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
     uint16_t *z = reinterpret_cast<uint16_t *>(ws + L.off_z);
     uint16_t *gt = reinterpret_cast<uint16_t *>(ws + L.off_gt);
     uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.off_ht);
@@ -286,9 +305,10 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
         hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(2048), dim3(256), 0, st, f.grad_weight, tot);
         return hipGetLastError();
     }
-    // W^T [H, V]
-    if ((e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), st)) !=
-        hipSuccess)
+    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
+    if (f.with_wt &&
+        (e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), st)) !=
+            hipSuccess)   // W^T [H, V]
         return e;
     const int tiles_dh = static_cast<int>(((C + gemm::BM - 1) / gemm::BM) * ((H + gemm::BN - 1) / gemm::BN));
     const int splits = choose_splits(tiles_dh, V);
@@ -346,8 +366,12 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
                 if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
             }
             // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
-            if ((e = gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H), static_cast<int>(V), splits,
-                             C * H, st)) != hipSuccess)
+            // (W^T K-contiguous when the workspace holds it, else W itself, k-major)
+            if ((e = f.with_wt ? gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H),
+                                         static_cast<int>(V), splits, C * H, st)
+                               : gemm_nt(gemm::OUT_F32, z, V, f.weight, H, part, H, cn, static_cast<int>(H),
+                                         static_cast<int>(V), splits, C * H, st, nullptr, /*b_kn=*/true)) !=
+                hipSuccess)
                 return e;
             {
                 const int64_t quads = static_cast<int64_t>(cn) * H / 4;

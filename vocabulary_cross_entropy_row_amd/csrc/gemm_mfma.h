@@ -105,6 +105,35 @@ struct GemmArgs {
 // land on 16 distinct 16-byte bank groups of the 256-byte bank window.
 __device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
 
+// k-major operand tiles ([k][256 columns], 512 bytes per k-row): the 16-byte chunk c of k-row kr sits
+// at position c ^ kmswz(kr), so the four k-rows one transposing read touches fall in different bank
+// windows.
+__device__ __forceinline__ int kmswz(int kr) { return (kr & 3) << 2; }
+
+// The MFMA operand fragment of columns cb .. cb + 31 for K sub-step kk from a k-major tile: lane l
+// gets column cb + l % 32 at k = kk * 16 + (l / 32) * 8 + 0..7.  ds_read_b64_tr_b16 transposes
+// 16-bit elements within each 16-lane group: result element j of lane d is element d % 4 of the
+// 8 bytes that lane 4 j + d / 4 of the group addressed (checked on the device).  So source lane
+// 4 j + q of group g addresses k-row kk * 16 + (g / 2) * 8 + t * 4 + j, columns
+// cb + (g % 2) * 16 + 4 q .. + 3, and two reads (t = 0, 1) give the eight k values.
+__device__ __forceinline__ bf8 km_frag(const unsigned char *tile, int kk, int cb, int lane) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s *lp4;
+    const int g = lane >> 4, sl = lane & 15;
+    const int col = cb + (g & 1) * 16 + (sl & 3) * 4;
+    v4s h[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int kr = kk * 16 + (g >> 1) * 8 + t * 4 + (sl >> 2);
+        const unsigned char *p = tile + kr * 512 + (((col >> 3) ^ kmswz(kr)) * 16) + (col & 7) * 2;
+        h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(p));
+    }
+    const v4s lo = h[0], hi = h[1];
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s r = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    return __builtin_bit_cast(bf8, r);
+}
+
 // A buffer descriptor built from wave-uniform values, so it lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, uint32_t nrec) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
@@ -319,7 +348,7 @@ __device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI]
 
 // KTAIL: K is not a multiple of BK, so each load checks its K column; otherwise
 // the K position rides in the scalar offset and the per-lane offsets are fixed.
-template <int MODE, bool KTAIL, bool SOFTCAP = false>
+template <int MODE, bool KTAIL, bool SOFTCAP = false, bool A_KM = false, bool B_KN = false>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_nt_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
@@ -349,16 +378,25 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    // the descriptors cover exactly the tiles' valid rows: rows past M or N read as zeros
+    // K-contiguous operands: the descriptors cover exactly the tile's valid rows, so rows past M or N
+    // read as zeros.  k-major operands ([K][rows], A_KM / B_KN): the descriptor starts at the tile's
+    // first column and covers rows k < K, so rows past K read as zeros; columns past M or N are masked
+    // per lane.
     const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
-    const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(g.A + static_cast<int64_t>(m0) * g.lda,
-                                                    static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(g.lda) * 2u);
-    const __amdgpu_buffer_rsrc_t rsB = uniform_rsrc(g.B + static_cast<int64_t>(n0) * g.ldb,
-                                                    static_cast<uint32_t>(b_rows) * static_cast<uint32_t>(g.ldb) * 2u);
+    const __amdgpu_buffer_rsrc_t rsA =
+        A_KM ? uniform_rsrc(g.A + m0, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.lda - m0) * 2u)
+             : uniform_rsrc(g.A + static_cast<int64_t>(m0) * g.lda,
+                            static_cast<uint32_t>(a_rows) * static_cast<uint32_t>(g.lda) * 2u);
+    const __amdgpu_buffer_rsrc_t rsB =
+        B_KN ? uniform_rsrc(g.B + n0, static_cast<uint32_t>(static_cast<int64_t>(g.K) * g.ldb - n0) * 2u)
+             : uniform_rsrc(g.B + static_cast<int64_t>(n0) * g.ldb,
+                            static_cast<uint32_t>(b_rows) * static_cast<uint32_t>(g.ldb) * 2u);
 
-    // this wave's load blocks: byte offsets at k = 0 and their K columns
+    // this wave's load blocks: byte offsets at k = 0 and their K columns (K-contiguous), or their
+    // column validity (k-major: block b holds k-rows 2b, 2b+1 of 32 swizzled 16-byte chunks)
     uint32_t voffA[LOADS], voffB[LOADS];
     int kcol[LOADS];
+    bool okA[LOADS], okB[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         const int r = (j * NWAVES + wave) * (64 / CPR) + lane / CPR;
@@ -366,13 +404,29 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         kcol[j] = c * 8;
         voffA[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(g.lda) * 2u + c * 16u;
         voffB[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(g.ldb) * 2u + c * 16u;
+        const int kr = 2 * (j * NWAVES + wave) + (lane >> 5);
+        const int kc = (lane & 31) ^ kmswz(kr);
+        if constexpr (A_KM) {
+            voffA[j] = (static_cast<uint32_t>(kr) * static_cast<uint32_t>(g.lda) + kc * 8u) * 2u;
+            okA[j] = m0 + kc * 8 < g.M;
+        }
+        if constexpr (B_KN) {
+            voffB[j] = (static_cast<uint32_t>(kr) * static_cast<uint32_t>(g.ldb) + kc * 8u) * 2u;
+            okB[j] = n0 + kc * 8 < g.N;
+        }
     }
 
     // load j of one operand of step `step` into stage `st`
     auto issue = [&](int step, int st, int j, bool isB) {
         unsigned char *dst = lds + st * STAGE_BYTES + (isB ? TILE_BYTES : 0) + (j * NWAVES + wave) * 1024;
         const int k0 = step * BK;
-        if constexpr (KTAIL) {
+        if ((isB && B_KN) || (!isB && A_KM)) {
+            // k-major: the step's rows are k0 .. k0 + 63 (past K: outside the descriptor)
+            uint32_t v = (isB ? voffB[j] : voffA[j]) +
+                         static_cast<uint32_t>(k0) * static_cast<uint32_t>(isB ? g.ldb : g.lda) * 2u;
+            if (!(isB ? okB[j] : okA[j])) v = 0xFFFFFFF0u;   // past M or N: out of range, reads zeros
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_ptr)dst, 16, v, 0, 0, 0);
+        } else if constexpr (KTAIL) {
             uint32_t v = (isB ? voffB[j] : voffA[j]) + static_cast<uint32_t>(k0) * 2u;
             if (k0 + kcol[j] >= g.K) v = 0xFFFFFFF0u;   // past K: out of range, reads zeros
             __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_ptr)dst, 16, v, 0, 0, 0);
@@ -387,13 +441,21 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         const int c = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
-            const int r = wm * 64 + i * 32 + (lane & 31);
-            af[i] = *reinterpret_cast<const bf8 *>(At + (r * CPR + (c ^ swz(r))) * 16);
+            if constexpr (A_KM) {
+                af[i] = km_frag(At, kk, wm * 64 + i * 32, lane);
+            } else {
+                const int r = wm * 64 + i * 32 + (lane & 31);
+                af[i] = *reinterpret_cast<const bf8 *>(At + (r * CPR + (c ^ swz(r))) * 16);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = wn * 128 + j * 32 + (lane & 31);
-            bfr[j] = *reinterpret_cast<const bf8 *>(Bt + (r * CPR + (c ^ swz(r))) * 16);
+            if constexpr (B_KN) {
+                bfr[j] = km_frag(Bt, kk, wn * 128 + j * 32, lane);
+            } else {
+                const int r = wn * 128 + j * 32 + (lane & 31);
+                bfr[j] = *reinterpret_cast<const bf8 *>(Bt + (r * CPR + (c ^ swz(r))) * 16);
+            }
         }
     };
     // wait until at most `steps` steps of this wave's loads are outstanding
@@ -469,7 +531,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
-                if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     // LDS read
+                if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
                 if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
             }
         }

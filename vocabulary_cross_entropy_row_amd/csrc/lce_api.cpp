@@ -240,12 +240,12 @@ lce_status lce_ce_grad(void *logits_inout, int64_t ld, lce_dtype dtype, const in
 
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens) {
     if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1) return 0;
-    return lce::flce_layout(n, H, V, chunk_tokens, lce::flce_default_group_chunks(n, H, V, chunk_tokens)).bytes;
+    return lce::flce_layout(n, H, V, chunk_tokens, lce::flce_default_group_chunks(n, H, V, chunk_tokens), true).bytes;
 }
 
 size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens, int64_t group_chunks) {
     if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1 || group_chunks < 1) return 0;
-    return lce::flce_layout(n, H, V, chunk_tokens, group_chunks).bytes;
+    return lce::flce_layout(n, H, V, chunk_tokens, group_chunks, false).bytes;
 }
 
 lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
@@ -269,10 +269,11 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
     if (n > 0 && (!hidden || !labels || !loss_tok || !grad_hidden))
         return fail(LCE_ERR_INVALID_ARG, "%s: hidden, labels, loss_tok and grad_hidden are required", fn);
     // the largest grad_weight group (up to the default) whose layout fits the workspace
-    int64_t group = lce::flce_default_group_chunks(n, H, V, chunk_tokens);
-    while (group > 1 && lce::flce_layout(n, H, V, chunk_tokens, group).bytes > workspace_bytes) --group;
-    const size_t need = lce::flce_layout(n, H, V, chunk_tokens, group).bytes;
-    if (workspace_bytes < need)
+    int64_t group = 1;
+    bool with_wt = false;
+    const bool fits = lce::flce_plan(n, H, V, chunk_tokens, workspace_bytes, &group, &with_wt);
+    const size_t need = lce::flce_layout(n, H, V, chunk_tokens, 1, false).bytes;
+    if (!fits)
         return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < minimum %zu", fn, workspace_bytes, need);
     if (!is_aligned(workspace, 256)) return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     if (H % 8 != 0 || V % 8 != 0)
@@ -306,6 +307,7 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
     f.counts = counts;
     f.workspace = workspace;
     f.group_chunks = group;
+    f.with_wt = with_wt;
     return hip_status(lce::launch_flce(f, stream), "lce_flce_fwd_bwd launch");
 }
 
@@ -368,10 +370,11 @@ lce_status lce_flce_backward(const void *hidden, const void *weight, const int64
         return fail(LCE_ERR_INVALID_ARG, "%s: grad_hidden, lse and one_minus_py are required", fn);
     if ((grad_hidden && !is_aligned(grad_hidden, 16)) || !is_aligned(grad_weight, 16))
         return fail(LCE_ERR_UNSUPPORTED, "%s: grad_hidden and grad_weight must be 16-byte aligned", fn);
-    int64_t group = lce::flce_default_group_chunks(n, H, V, chunk_tokens);
-    while (group > 1 && lce::flce_layout(n, H, V, chunk_tokens, group).bytes > workspace_bytes) --group;
-    const size_t need = lce::flce_layout(n, H, V, chunk_tokens, group).bytes;
-    if (workspace_bytes < need)
+    int64_t group = 1;
+    bool with_wt = false;
+    const bool fits = lce::flce_plan(n, H, V, chunk_tokens, workspace_bytes, &group, &with_wt);
+    const size_t need = lce::flce_layout(n, H, V, chunk_tokens, 1, false).bytes;
+    if (!fits)
         return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < minimum %zu", fn, workspace_bytes, need);
     if (!is_aligned(workspace, 256)) return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     const int64_t C = chunk_tokens < n ? chunk_tokens : n;
@@ -397,6 +400,7 @@ lce_status lce_flce_backward(const void *hidden, const void *weight, const int64
     f.counts = const_cast<int64_t *>(counts);   // read only on this path
     f.workspace = workspace;
     f.group_chunks = group;
+    f.with_wt = with_wt;
     f.lse = lse;
     f.q = one_minus_py;
     return hip_status(lce::launch_flce(f, stream), "lce_flce_backward launch");

@@ -114,6 +114,7 @@ struct FlceArgs {
     int64_t *counts;         // [3]
     void *workspace;
     int64_t group_chunks;    // chunks per grad_weight group (the workspace was sized for it)
+    bool with_wt = true;     // the workspace holds W^T (else dH reads W in place, k-major)
     // Tile-resident backward: with lse and q (1 - p_y) of every token from the
     // stats pass, each chunk's gradient is formed in the logits GEMM's epilogue
     // (no logits stored, no losses written, counts read as given).
@@ -147,9 +148,15 @@ struct FlceLayout {
     int64_t chunk;        // tokens per logits chunk
     int64_t group;        // tokens per grad_weight group (a multiple of chunk)
     int64_t ldg;          // row stride of the transposed group buffers (multiple of 8)
-    size_t off_wt, off_z, off_gt, off_ht, off_part, off_ce, bytes;
+    size_t off_wt, off_z, off_gt, off_ht, off_part, off_ce, bytes;   // off_wt: with_wt only
 };
-FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t group_chunks);
+// with_wt: room for W^T [H, V] bf16, which makes dH's GEMM read W K-contiguous
+// (faster than reading W in place through transposing LDS reads, 2 H V bytes more)
+FlceLayout flce_layout(int64_t n, int64_t H, int64_t V, int64_t chunk, int64_t group_chunks, bool with_wt);
+// The layout a workspace of `bytes` gets: the largest grad_weight group (up to
+// the default) that fits without W^T, plus W^T when there is room for it too.
+// False when not even one chunk per group fits.
+bool flce_plan(int64_t n, int64_t H, int64_t V, int64_t chunk, size_t bytes, int64_t *group_chunks, bool *with_wt);
 // Chunks per grad_weight group that kFlceGroupBytes holds (at least 1, at most all chunks).
 int64_t flce_default_group_chunks(int64_t n, int64_t H, int64_t V, int64_t chunk);
 hipError_t launch_flce(const FlceArgs &f, hipStream_t stream);
