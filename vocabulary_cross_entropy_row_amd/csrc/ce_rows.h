@@ -25,10 +25,15 @@
 // out, and pass A of that row starts on its (by then resident) LDS rounds.
 // So the HBM traffic of one row overlaps the arithmetic of the previous one.
 //
+// Rows are handed out dynamically: a workgroup starts on row blockIdx.x and
+// then draws row numbers from a counter in the workspace, one row ahead of
+// need, so CUs that stream faster (the XCDs differ by a few percent) take more
+// rows and all workgroups finish within about one row of each other.
+//
 // The workgroups count the labels themselves (the mean scale needs n_valid
-// before any gradient is written), keep per-workgroup loss / n_correct
-// partials in the workspace, and the last workgroup to finish folds them in
-// workgroup order, so every reduction is deterministic.
+// before any gradient is written).  The last workgroup to finish sums the
+// per-token losses in row order and the per-workgroup n_correct counts, so
+// every reduction is deterministic whichever workgroup took which row.
 #pragma once
 
 #include "ce_device.h"
@@ -36,9 +41,12 @@
 namespace lce {
 namespace dev {
 
-// Workspace layout: [0,4) completion counter (zero between calls), [256, 256 + 8G)
-// fp64 loss partials, then G int64 n_correct partials.
+// Workspace layout: [0,4) completion counter, [4,8) row counter (both zero
+// between calls), [256, 256 + 8G) int64 n_correct partials.
 constexpr size_t kWsPartials = 256;
+// Ignored rows one draw may step over (their zeroing is queued for the drawing
+// workgroup); past that the ignored row is processed with scale 0.
+constexpr int kZeroMax = 16;
 
 // Word 3 of a gfx9-family buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
@@ -46,11 +54,24 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ unsigned *ws_ticket(void *ws) { return static_cast<unsigned *>(ws); }
-__device__ __forceinline__ double *ws_loss(void *ws) {
-    return reinterpret_cast<double *>(static_cast<char *>(ws) + kWsPartials);
+__device__ __forceinline__ unsigned *ws_rows(void *ws) { return static_cast<unsigned *>(ws) + 1; }
+__device__ __forceinline__ long long *ws_correct(void *ws) {
+    return reinterpret_cast<long long *>(static_cast<char *>(ws) + kWsPartials);
 }
-__device__ __forceinline__ long long *ws_correct(void *ws, int G) {
-    return reinterpret_cast<long long *>(static_cast<char *>(ws) + kWsPartials + 8 * static_cast<size_t>(G));
+// Row draws and the final fold's operands go through system-scope atomics:
+// they are performed at, or written through to, memory, so workgroups on
+// different XCDs (each with its own L2) see each other's values without a
+// cache-wide writeback or invalidate.
+// The draw is a wrapping increment (never reaching its 2^32 - 1 bound) rather
+// than an add: the compiler rewrites a one-lane add into a wave-level form
+// that consumes the result at once, i.e. waits right there for every memory
+// operation issued before it, the row loads included.
+__device__ __forceinline__ unsigned draw_row(void *ws) {
+    return __builtin_amdgcn_atomic_inc32(ws_rows(ws), 0xffffffffu, __ATOMIC_RELAXED, "");
+}
+__device__ __forceinline__ void store_through(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 template <bool BF16, int KR, int KL, bool SOFTCAP, bool ARGMAX, bool SMOOTH>
@@ -70,6 +91,11 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     __shared__ double sh_d[NWAVE];
     __shared__ float sh_xy[2];
     __shared__ int sh_flag;
+    // the schedule, published by thread 0 at each row's combine barrier: the next
+    // row, and the ignored rows its draws stepped over (zeroed by this workgroup)
+    __shared__ int64_t sh_next[2];
+    __shared__ int sh_nz[2];
+    __shared__ int64_t sh_zero[2][kZeroMax];
 
     const int tid = threadIdx.x;
     const int wave_base = tid & ~63;
@@ -91,13 +117,6 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
 
 
     auto valid_label = [&](int64_t y) { return y != a.ignore_index && y >= 0 && y < a.V; };
-    // the next row >= r of this workgroup's sequence that takes the full path:
-    // every row when the argmax is wanted, otherwise only rows with a valid label
-    auto next_row = [&](int64_t r) {
-        if constexpr (!ARGMAX)
-            while (r < n && !valid_label(lab[r])) r += G;
-        return r;
-    };
 
     // Row memory goes through buffer instructions: the row base sits in a
     // uniform descriptor (SGPRs), every round shares one VGPR offset
@@ -129,24 +148,28 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // stores of a partial last round need no guard: lanes past the row are
     // outside the descriptor and dropped.  Every wave therefore issues the
     // same memory operations, which the LDS waits below count on.
+    // The round offset rides in the VGPR offset, not in soffset: a 16-byte
+    // store's data registers can still be read after the store has issued,
+    // and the compiler only keeps the next VALU writes of those registers
+    // back when soffset is not a register.  With the offset in an SGPR, lanes
+    // 12-15 of each 16-lane group have stored what the next instruction wrote.
+    // (The add is formed at each store: hoisted, every round would hold its
+    // own offset register.)
     auto store_round = [&](int k, __amdgpu_buffer_rsrc_t dst, u32x4 val) {
-        __builtin_amdgcn_raw_buffer_store_b128(val, dst, voff, k * NT * 16, kNonTemporal);
+        int vo = voff;
+        asm volatile("" : "+v"(vo));
+        __builtin_amdgcn_raw_buffer_store_b128(val, dst, vo + k * NT * 16, 0, kNonTemporal);
     };
     // a round of the resident row as a 16-byte vector
     auto round_vec = [&](int k) -> u32x4 { return k >= KL ? v[k >= KL ? k - KL : 0] : lds_rows[k * NT + tid]; };
 
-    // zero gradient and loss for the ignored rows r0, r0 + G, ... before r1 (the
-    // rows next_row stepped over): stores only, issued where they are met so
-    // they overlap the other rows' traffic
-    auto zero_rows = [&](int64_t r0, int64_t r1) {
-        if constexpr (!ARGMAX) {
-            for (int64_t r = r0; r < r1; r += G) {
-                const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
+    // zero gradient and loss of an ignored row the schedule stepped over:
+    // stores only, issued after a row's own stores so they overlap its traffic
+    auto zero_row = [&](int64_t r) {
+        const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
 #pragma unroll
-                for (int k = 0; k < K; ++k) store_round(k, rz, zero4);
-                if (tid == 0) a.loss_tok[r] = 0.0f;
-            }
-        }
+        for (int k = 0; k < K; ++k) store_round(k, rz, zero4);
+        if (tid == 0) store_through(a.loss_tok + r, 0.0f);
     };
 
     // The mean scale needs every label counted before any gradient is written.
@@ -155,11 +178,17 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     const int64_t yc0 = tid < a.count_n ? a.count_labels[tid] : a.ignore_index;
     const int64_t yc1 = tid + NT < a.count_n ? a.count_labels[tid + NT] : a.ignore_index;
     __builtin_amdgcn_sched_barrier(0);
-    int64_t row = next_row(blockIdx.x);
+    // the first row is this workgroup's own (the grid never exceeds n); an
+    // ignored one is carried through with scale 0
+    int64_t row = blockIdx.x;
+    // thread 0's draw of the row after the next one: requested behind the LDS
+    // rounds of a row, so it has landed when they have
+    unsigned draw = 0;
     {
         const __amdgpu_buffer_rsrc_t src = row_rsrc(row, row < n);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
+            if (k == KL && tid == 0 && G < n) draw = draw_row(a.workspace);
             issue_round(k, src);
             __builtin_amdgcn_sched_barrier(0);   // issue in the order pass A consumes
         }
@@ -170,7 +199,6 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
 #pragma unroll
         for (int k = KL; k < K; ++k) store_round(k, none, zero4);
     }
-    zero_rows(blockIdx.x, row < n ? row : n);
 
     count_labels_publish(a, sh_c, yc0, yc1);
     __syncthreads();
@@ -184,13 +212,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         if (a.reduction == 1) red_scale = nv0 > 0 ? g_all / static_cast<float>(nv0) : 0.0f;
     }
 
-    double loss_acc = 0.0;
     long long correct = 0;
 
     int pb = 0;   // parity of the row iteration (selects the combine slots)
     for (int64_t nxt; row < n; row = nxt, pb ^= 1) {
-        nxt = next_row(row + G);
-        const __amdgpu_buffer_rsrc_t rn = row_rsrc(nxt, nxt < n);
         const __amdgpu_buffer_rsrc_t rp = row_rsrc(row, true);
         const int64_t y64 = lab[row];
         const bool valid = valid_label(y64);     // always true unless ARGMAX
@@ -215,9 +240,17 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         if constexpr (KL > 0) {
             // this wave's LDS rounds have landed once at most the 2 KR memory
             // operations issued after them (KR register-round stores, then the KR
-            // register loads) are outstanding; ignored rows' stores come later still
+            // register loads) are outstanding; the target element's store, thread
+            // 0's row outputs and ignored rows' stores come later still
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KR) : "memory");
         }
+        // thread 0: the drawn row and its label, requested now so both have
+        // landed by the combine barrier (the draw was issued before the row's
+        // register rounds, so it is complete once they are)
+        int64_t nx = static_cast<int64_t>(G) + static_cast<int64_t>(draw);
+        int64_t ynx = 0;
+        if constexpr (!ARGMAX)
+            if (tid == 0 && nx < n) ynx = a.labels[nx];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int idx = k * NT + tid;
@@ -317,6 +350,20 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 zs = wave_sum_dpp(zs);
                 if ((tid & 63) == 0) sh_zs[pb][tid >> 6] = zs;
             }
+            if (tid == 0) {
+                // resolve the schedule: without the argmax, ignored rows are
+                // not read; they are zeroed by this workgroup after its row
+                int nz = 0;
+                if constexpr (!ARGMAX) {
+                    while (nx < n && !valid_label(ynx) && nz < kZeroMax) {
+                        sh_zero[pb][nz++] = nx;
+                        nx = static_cast<int64_t>(G) + static_cast<int64_t>(draw_row(a.workspace));
+                        if (nx < n) ynx = a.labels[nx];
+                    }
+                }
+                sh_next[pb] = nx;
+                sh_nz[pb] = nz;
+            }
             __syncthreads();
             float M = sh_m[pb][0];
 #pragma unroll
@@ -331,10 +378,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 am = sh_i[pb][0];
 #pragma unroll
                 for (int w = 1; w < NWAVE; ++w) argmax_combine(amv, am, sh_z[pb][w], sh_i[pb][w]);
-                if (tid == 0) {
-                    a.argmax_out[row] = am;
-                    if (valid && am == y) ++correct;
-                }
+                if (tid == 0 && valid && am == y) ++correct;
             }
             if constexpr (SMOOTH) {
                 float t = sh_zs[pb][0];
@@ -349,16 +393,18 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const float e_y = exp2_fast(fmaf(zy, kLog2e, -Mz * kLog2e));
         const float S = s + e_y;
         const float lse = Mz + logf(S);
-        if (tid == 0) {
-            float loss = lse - (1.0f - eps) * zy;
-            if constexpr (SMOOTH) loss -= eps * invV * zs;
-            if (!valid) loss = 0.0f;
-            a.loss_tok[row] = loss;
-            loss_acc += static_cast<double>(loss);
-        }
+        // thread 0's row outputs are stored only after the next row's loads
+        // are out: a store here would be the one memory operation this wave
+        // has in flight when pass B starts waiting on its register rounds, so
+        // the whole workgroup would wait for its round trip at the next barrier
+        float loss = lse - (1.0f - eps) * zy;
+        if constexpr (SMOOTH) loss -= eps * invV * zs;
+        if (!valid) loss = 0.0f;
 
         // ---- pass B: gradient over the logits.  |s_i| is folded into the
         // exponent (exp(z - lse + ln|s_i|)) and its sign applied afterwards
+        nxt = sh_next[pb];
+        const __amdgpu_buffer_rsrc_t rn = row_rsrc(nxt, nxt < n);
         const float ascale = fabsf(scale);
         const bool negate = scale < 0.0f;
         const float l2s = log2f(ascale);                  // -inf when the scale is 0
@@ -389,8 +435,6 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) g[e] = -g[e];
             }
-            // the packed result goes straight to the store: a VALU operation on
-            // the output of v_cvt_pk_bf16_f32 has been seen to read stale data
             store_round(k, rp, EL::pack(g));
             // keep the rounds in order: hoisted loads or conversions of later
             // rounds would hold extra row data in registers
@@ -410,6 +454,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             issue_round(k, rn);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the row after the next (none to draw once the schedule has run out: a
+        // draw still in flight would delay this workgroup's final publish)
+        if (tid == 0 && nxt < n) draw = draw_row(a.workspace);
+        __builtin_amdgcn_sched_barrier(0);
         // the register rounds, then the next row's register rounds
 #pragma unroll
         for (int k = KL; k < K; ++k) grad_round(k);
@@ -421,19 +469,23 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         // the target element's own gradient replaces what its round stored
         // (one thread, after that round's store, to the same address)
         if (owner) EL::template store_one<kNonTemporal>(rp, y, gy);
-        // ignored rows between this row and the next valid one
-        zero_rows(row + G, nxt < n ? nxt : n);
+        if (tid == 0) {
+            store_through(a.loss_tok + row, loss);
+            if constexpr (ARGMAX) a.argmax_out[row] = am;
+        }
+        // ignored rows the draws stepped over
+        if constexpr (!ARGMAX) {
+            const int nz = sh_nz[pb];
+            for (int i = 0; i < nz; ++i) zero_row(sh_zero[pb][i]);
+        }
     }
 
-    // ---- publish this workgroup's partials; the last workgroup folds them.
-    // The partials are written through to memory (system-scope stores) and
-    // acknowledged before the ticket is taken, and the last workgroup reads
-    // them past its own L2: no cache-wide writeback or invalidate is needed.
+    // ---- publish this workgroup's n_correct; the last workgroup folds the
+    // per-token losses and these counts.  Both were written through to memory
+    // (system-scope stores) and are acknowledged before the ticket is taken,
+    // and the last workgroup reads them past its own L2.
     if (tid == 0) {
-        __hip_atomic_store(reinterpret_cast<unsigned long long *>(ws_loss(a.workspace)) + blockIdx.x,
-                           __builtin_bit_cast(unsigned long long, loss_acc), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
-        __hip_atomic_store(ws_correct(a.workspace, G) + blockIdx.x, correct, __ATOMIC_RELAXED,
+        __hip_atomic_store(ws_correct(a.workspace) + blockIdx.x, correct, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const unsigned t = __hip_atomic_fetch_add(ws_ticket(a.workspace), 1u, __ATOMIC_RELAXED,
@@ -444,13 +496,15 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     if (!sh_flag) return;
     long long n_valid, n_bad;
     count_labels_read(sh_c, n_valid, n_bad);
+    // fixed order: thread t sums rows t, t + NT, ... in fp64, then the waves'
+    // sums are combined in wave order
     double acc = 0.0;
     long long cor = 0;
-    for (int w = tid; w < G; w += NT) {
-        acc += __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<unsigned long long *>(ws_loss(a.workspace)) + w,
-                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
-        cor += __hip_atomic_load(ws_correct(a.workspace, G) + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
+    for (int64_t r = tid; r < n; r += NT)
+        acc += static_cast<double>(__uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned *>(a.loss_tok) + r,
+                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)));
+    for (int w = tid; w < G; w += NT)
+        cor += __hip_atomic_load(ws_correct(a.workspace) + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     acc = wave_sum_d(acc);
     cor = wave_sum_ll(cor);
     if ((tid & 63) == 0) {
@@ -475,6 +529,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         a.counts[1] = c;
         a.counts[2] = n_bad;
         *ws_ticket(a.workspace) = 0u;
+        *ws_rows(a.workspace) = 0u;
     }
 }
 
