@@ -173,6 +173,24 @@ def test_flce_deterministic():
     assert torch.equal(a.loss_tok, b.loss_tok)
 
 
+def test_flce_clobbered_workspace():
+    """The fused linear call's workspace is caller-clobbered: a workspace full of 0xFF bytes
+    (the chunk row kernel's completion and row counters included) gives bitwise the results
+    of a zeroed one."""
+    hb, wb, y = gen(300, 256, 4096, seed=12)
+    n, H = hb.shape
+    wsb = lce.lce_flce_workspace_bytes(n, H, wb.shape[0], 64)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((wsb,), fill, dtype=torch.uint8, device=DEV)
+        res = lce.lce_flce_fwd_bwd(bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV), chunk_tokens=64,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(res)
+    for name in ("loss_tok", "loss_out", "grad_hidden", "grad_weight", "counts"):
+        assert torch.equal(getattr(outs[0], name), getattr(outs[1], name)), name
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_flce_full_size_sampled():
