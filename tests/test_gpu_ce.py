@@ -265,6 +265,27 @@ def test_deterministic_replay(want_argmax):
     run_and_check(x, y, V, want_argmax=want_argmax, rows=np.arange(0, n, 97))
 
 
+@pytest.mark.parametrize("pattern", ["long_ignored_runs", "all_ignored"])
+@pytest.mark.parametrize("want_argmax", [False, True], ids=["plain", "argmax"])
+def test_dynamic_schedule_ignored_runs(pattern, want_argmax):
+    """More rows than workgroups, so rows are drawn from the workspace counter.  Long runs of
+    ignored rows make one draw step over more ignored rows than its queue holds (those
+    rows are then processed with scale 0); every output must still match the oracle."""
+    rng = np.random.default_rng(21)
+    n, V = 2048, 4096
+    x = make_logits(rng, n, V, V, "bf16")
+    y = rng.integers(0, V, n).astype(np.int64)
+    if pattern == "all_ignored":
+        y[:] = -100
+    else:
+        y[300:] = -100
+        y[300::97] = rng.integers(0, V, len(y[300::97]))
+    res, out = run_and_check(x, y, V, want_argmax=want_argmax)
+    ign = y == -100
+    assert np.all(out[ign].view(np.int16) & 0x7FFF == 0)
+    assert np.all(res.loss_tok.cpu().numpy()[ign] == 0.0)
+
+
 @pytest.mark.parametrize("n,V,ld", [(16, 32768, 32768 + 64), (8, 131072, 131072)], ids=["16x32768ld32832", "8x131072"])
 def test_repeated_calls_store_the_same_bytes(n, V, ld):
     """Regression: with the round offset of the 16-byte gradient stores in soffset, the
