@@ -394,9 +394,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const float S = s + e_y;
         const float lse = Mz + logf(S);
         // thread 0's row outputs are stored only after the next row's loads
-        // are out: a store here would be the one memory operation this wave
-        // has in flight when pass B starts waiting on its register rounds, so
-        // the whole workgroup would wait for its round trip at the next barrier
+        // are out, so that the wait on the register rounds at the start of
+        // pass B never includes a store's round trip
         float loss = lse - (1.0f - eps) * zy;
         if constexpr (SMOOTH) loss -= eps * invV * zs;
         if (!valid) loss = 0.0f;
@@ -497,12 +496,25 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     long long n_valid, n_bad;
     count_labels_read(sh_c, n_valid, n_bad);
     // fixed order: thread t sums rows t, t + NT, ... in fp64, then the waves'
-    // sums are combined in wave order
+    // sums are combined in wave order.  Eight loads go out before the first
+    // is added, so the fold waits for one round trip per eight rows per thread.
     double acc = 0.0;
     long long cor = 0;
-    for (int64_t r = tid; r < n; r += NT)
-        acc += static_cast<double>(__uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned *>(a.loss_tok) + r,
-                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)));
+    constexpr int kFold = 8;
+    for (int64_t r0 = 0; r0 < n; r0 += kFold * NT) {
+        float lv[kFold];
+        // (unconditional loads of a clamped row, masked when added: a load
+        // under a branch would be waited for at the branch's end)
+#pragma unroll
+        for (int u = 0; u < kFold; ++u) {
+            const int64_t r = r0 + u * NT + tid;
+            lv[u] = __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned *>(a.loss_tok) + (r < n ? r : n - 1),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+        }
+#pragma unroll
+        for (int u = 0; u < kFold; ++u)
+            if (r0 + u * NT + tid < n) acc += static_cast<double>(lv[u]);
+    }
     for (int w = tid; w < G; w += NT)
         cor += __hip_atomic_load(ws_correct(a.workspace) + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     acc = wave_sum_d(acc);
