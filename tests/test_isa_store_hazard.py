@@ -1,0 +1,47 @@
+"""Build-time guard against a silent store-data hazard on gfx950.
+
+A 16-byte (or 12-byte) buffer store whose soffset operand is an SGPR gets no
+wait states from the compiler before the next VALU write of its data
+registers, and on gfx950 lanes 12-15 of each 16-lane group have then stored
+what that next instruction wrote.  The kernels keep such offsets in the VGPR
+offset instead; this test compiles the kernels that use buffer stores to
+gfx950 assembly and checks that no wide buffer store takes an SGPR soffset.
+"""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+# buffer_store_dwordx3/x4 <vdata>, <vaddr>, s[desc], s<N> ...  (soffset an SGPR, not an inline 0)
+RISKY = re.compile(r"buffer_store_dwordx[34]\s+[^,]+,\s*[^,]+,\s*s\[\d+:\d+\],\s*s\d+\b")
+WIDE = re.compile(r"buffer_store_dwordx[34]\b")
+
+CASES = [
+    ("ce_rows_inst.hip", ["-DLCE_BF16=1", "-DLCE_KR=8", "-DLCE_KL=8"]),
+    ("ce_rows_inst.hip", ["-DLCE_BF16=1", "-DLCE_KR=16", "-DLCE_KL=9"]),
+    ("ce_rows_inst.hip", ["-DLCE_BF16=0", "-DLCE_KR=4", "-DLCE_KL=0"]),
+    ("ce_split.hip", []),
+]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src,defs", CASES, ids=[f"{c[0]}{''.join(c[1])}" for c in CASES])
+def test_no_wide_buffer_store_with_sgpr_soffset(tmp_path, src, defs):
+    out = tmp_path / "k.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", *defs, os.path.join(CSRC, src), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    asm = out.read_text()
+    assert WIDE.search(asm), "expected the kernels to use wide buffer stores"
+    bad = [line.strip() for line in asm.splitlines() if RISKY.search(line)]
+    assert not bad, f"{len(bad)} wide buffer stores with an SGPR soffset, e.g. {bad[0]}"
