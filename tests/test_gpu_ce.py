@@ -265,6 +265,54 @@ def test_deterministic_replay(want_argmax):
     run_and_check(x, y, V, want_argmax=want_argmax, rows=np.arange(0, n, 97))
 
 
+def test_graph_replay():
+    """The call captured in a HIP graph (torch's stream capture): the kernel leaves its
+    workspace counters at zero, so every replay, with eager work and host syncs in between,
+    gives bitwise the eager result.  1024 rows make the replays draw rows dynamically."""
+    rng = np.random.default_rng(31)
+    n, V = 1024, 32768
+    x = make_logits(rng, n, V, V, "bf16")
+    y = _labels(rng, n, V)
+    pristine = to_dev(x)
+    lab = torch.from_numpy(y).to(DEV)
+    buf = torch.empty_like(pristine)
+    loss_tok = torch.empty(n, dtype=torch.float32, device=DEV)
+    loss_out = torch.empty(1, dtype=torch.float32, device=DEV)
+    counts = torch.empty(3, dtype=torch.int64, device=DEV)
+    go = torch.full((1,), 0.5, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(lce.lce_ce_workspace_bytes(n, V), dtype=torch.uint8, device=DEV)
+
+    def call():
+        lce.lce_ce_fwd_bwd(buf, lab, label_smoothing=0.1, grad_out=go, loss_tok=loss_tok, loss_out=loss_out,
+                           counts=counts, workspace=ws, stream=torch.cuda.current_stream())
+
+    buf.copy_(pristine)
+    call()
+    torch.cuda.synchronize()
+    want = [from_dev(buf), loss_tok.cpu().numpy(), loss_out.cpu().numpy(), counts.cpu().numpy()]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        buf.copy_(pristine)
+        call()   # warm-up on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        buf.copy_(pristine)
+        loss_tok.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [from_dev(buf), loss_tok.cpu().numpy(), loss_out.cpu().numpy(), counts.cpu().numpy()]
+        for a, b in zip(want, got):
+            assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+    assert int(ws[:8].view(torch.int64).cpu()[0]) == 0
+
+
 @pytest.mark.parametrize("pattern", ["long_ignored_runs", "all_ignored"])
 @pytest.mark.parametrize("want_argmax", [False, True], ids=["plain", "argmax"])
 def test_dynamic_schedule_ignored_runs(pattern, want_argmax):
