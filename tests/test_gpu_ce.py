@@ -189,6 +189,20 @@ def test_label_dominated_rows():
         run_and_check(xx, y, V, red="sum", eps=0.05)
 
 
+@pytest.mark.parametrize("n,V,ld,dt", [(24, 4096, 4096, "bf16"), (8, 131072, 131072, "bf16"), (16, 4099, 4099, "bf16"),
+                                        (16, 4096, 4096, "f32")], ids=["bf16-4096", "bf16-131072", "generic-4099", "f32-4096"])
+@pytest.mark.parametrize("eps,T", [(1.0, 0.0), (0.0, 0.5), (1.0, 1.0), (0.3, 0.25)],
+                         ids=["eps1", "cap0.5", "eps1-cap1", "eps0.3-cap0.25"])
+def test_full_smoothing_and_strong_cap(n, V, ld, dt, eps, T):
+    """eps = 1 (a uniform target: the label only selects the row) and strong softcaps
+    (T <= 1, where most logits sit in the flat part of tanh), for every reduction."""
+    rng = np.random.default_rng([n, V, int(eps * 10), int(T * 100)])
+    x = make_logits(rng, n, V, ld, dt, sigma=3.0)
+    y = _labels(rng, n, V)
+    for red, go in (("mean", [1.0]), ("sum", [0.5]), ("none", rng.normal(size=n))):
+        run_and_check(x, y, V, eps=eps, T=T, red=red, grad_out=go, want_argmax=T > 0)
+
+
 def test_uniform_rows_give_log_v():
     V = 131072
     x = np.zeros((4, V), dtype=np.uint16)

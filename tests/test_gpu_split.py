@@ -113,6 +113,7 @@ FEATS = {
     "smooth_sum": dict(eps=0.1, red="sum", grad_out=[0.5]),
     "cap_none": dict(T=5.0, red="none"),
     "all": dict(eps=0.2, T=30.0, red="mean", grad_out=[-1.5]),
+    "strong_cap": dict(eps=0.1, T=0.5, red="sum", grad_out=[2.0]),   # tanh saturated for most logits
 }
 
 

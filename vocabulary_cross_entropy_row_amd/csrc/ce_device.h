@@ -42,7 +42,17 @@ struct Cap {
     float T;
     __device__ __forceinline__ float r_of(float x) const { return rcp_fast(1.0f + exp2_fast(x * c2)); }
     __device__ __forceinline__ float z_of_r(float r) const { return fmaf(-2.0f * T, r, T); }
-    __device__ __forceinline__ static float chain_of_r(float r) { return 4.0f * r * (1.0f - r); }
+    // r and q = 1 - r for the chain factor.  q is formed as r e (e = e^{2u}), not
+    // as 1 - r: where tanh saturates below zero r rounds towards 1 and 1 - r would
+    // lose all its digits, while r e keeps full relative precision.  e is capped
+    // at 2^126 so that r e stays finite where tanh saturates above zero (there
+    // r = 2^-126, q = 1, and the factor underflows as the exact one does).
+    __device__ __forceinline__ void r_q(float x, float &r, float &q) const {
+        const float e = exp2_fast(fminf(x * c2, 126.0f));
+        r = rcp_fast(1.0f + e);
+        q = r * e;
+    }
+    __device__ __forceinline__ static float chain(float r, float q) { return 4.0f * r * q; }
 };
 
 // ---- element access ---------------------------------------------------------

@@ -213,9 +213,10 @@ __global__ __launch_bounds__(NT) void ce_row_generic(CEArgs a) {
         float chain = 1.0f;
         float z = x;
         if constexpr (SOFTCAP) {
-            const float r = cap.r_of(x);
+            float r, q;
+            cap.r_q(x, r, q);
             z = cap.z_of_r(r);
-            chain = Cap::chain_of_r(r);
+            chain = Cap::chain(r, q);
         }
         if (j == ri.y) g = scale * (eps - s / S - epsV) * chain;
         else g = scale * (exp2_fast(fmaf(z, kLog2e, -lseL)) - epsV) * chain;

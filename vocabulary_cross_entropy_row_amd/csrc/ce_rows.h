@@ -411,7 +411,11 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const float lseL = lse * kLog2e - l2s;
         const float capb2 = (a.softcap - lse) * kLog2e + l2s;
         float gy = scale * (eps - s / S - (SMOOTH ? eps * invV : 0.0f));   // s_i (p_y - (1 - eps) - eps/V)
-        if constexpr (SOFTCAP) gy *= Cap::chain_of_r(cap.r_of(xy));
+        if constexpr (SOFTCAP) {
+            float ry, qy;
+            cap.r_q(xy, ry, qy);
+            gy *= Cap::chain(ry, qy);
+        }
         opaque_regs(v);
         auto grad_round = [&](int k) {
             const u32x4 vk = round_vec(k);
@@ -421,9 +425,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 const float x = EL::get(vk, e);
                 if constexpr (SOFTCAP) {
                     // chain 4 r (1 - r): the 4 rides in the exponent (capb2 + 2)
-                    const float r = cap.r_of(x);
+                    float r, q;
+                    cap.r_q(x, r, q);
                     const float p4 = exp2_fast(fmaf(r, capk, capb2 + 2.0f));   // 4 |s_i| p_j
-                    g[e] = (SMOOTH ? p4 - 4.0f * epsV : p4) * fmaf(-r, r, r);
+                    g[e] = (SMOOTH ? p4 - 4.0f * epsV : p4) * (r * q);
                 } else {
                     const float p = exp2_fast(fmaf(x, kLog2e, -lseL));      // |s_i| p_j
                     g[e] = SMOOTH ? p - epsV : p;

@@ -350,9 +350,10 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(void *logits, int64_t ld, 
         for (int k = 0; k < E; ++k) {
             const float x = EL::get(v[u], k);
             if constexpr (SOFTCAP) {
-                const float r = cap.r_of(x);
+                float r, q;
+                cap.r_q(x, r, q);
                 const float pp = dev::exp2_fast(fmaf(r, capk, capb2));   // |s| p_j
-                gv[k] = (SMOOTH ? pp - epsV : pp) * dev::Cap::chain_of_r(r);
+                gv[k] = (SMOOTH ? pp - epsV : pp) * dev::Cap::chain(r, q);
             } else {
                 const float pp = dev::exp2_fast(fmaf(x, kLog2e, -lseL));
                 gv[k] = SMOOTH ? pp - epsV : pp;
@@ -362,7 +363,11 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(void *logits, int64_t ld, 
             // the target: s (p_y - (1 - eps) - eps / V) with p_y - 1 = -(1 - p_y)
             const int k = static_cast<int>(yl % E);
             float gy = ascale * (eps - q[row] - (SMOOTH ? eps / static_cast<float>(V) : 0.0f));
-            if constexpr (SOFTCAP) gy *= dev::Cap::chain_of_r(cap.r_of(EL::get(v[u], k)));
+            if constexpr (SOFTCAP) {
+                float ry, qy;
+                cap.r_q(EL::get(v[u], k), ry, qy);
+                gy *= dev::Cap::chain(ry, qy);
+            }
 #pragma unroll
             for (int kk = 0; kk < E; ++kk)
                 if (kk == k) gv[kk] = gy;

@@ -334,9 +334,10 @@ __device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI]
                 const float x = acc[i][j][r];
                 float z = x, ch = P.w;
                 if constexpr (SOFTCAP) {
-                    const float rr = cap.r_of(x);
+                    float rr, qq;
+                    cap.r_q(x, rr, qq);
                     z = cap.z_of_r(rr);
-                    ch *= dev::Cap::chain_of_r(rr);
+                    ch *= dev::Cap::chain(rr, qq);
                 }
                 const float pe = dev::exp2_fast(fmaf(z, kL2e, -P.x));
                 const float gval = c == yr ? P.z : pe - P.y;
