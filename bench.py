@@ -46,6 +46,8 @@ H100_CONTEXT = {"hardware": "H100 80GB, BF16, [2048, 131072], TP=1", "liger_ms":
                 "megatron_native_fused_ms": 3.646, "transformer_engine_ms": 0.711}
 CSRC = os.path.join(ROOT, "vocabulary_cross_entropy_row_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
+# raw rocprofv3 output of --collect-profiles (CSV files; only the summaries go to profiles/)
+RAW_PROFILES = os.environ.get("LCE_PROFILE_RAW_DIR", os.path.join(ROOT, "profiles_raw"))
 
 
 def call_percentiles(ms, nd: int) -> dict:
@@ -183,7 +185,7 @@ def _ours(name: str) -> bool:
 def collect_profiles(workload: str) -> int:
     import synth
     w = synth.WORKLOADS[workload]
-    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", workload)
+    raw = os.path.join(RAW_PROFILES, workload)
     os.makedirs(raw, exist_ok=True)
     base = ["--workload", workload, "--no-cpu-baseline"]
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
@@ -389,7 +391,7 @@ def bench_flce(args, w) -> int:
 def collect_profiles_flce(workload: str, resident: bool = False) -> int:
     import synth
     w = synth.FLCE_WORKLOADS[workload]
-    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", workload + ("_resident" if resident else ""))
+    raw = os.path.join(RAW_PROFILES, workload + ("_resident" if resident else ""))
     os.makedirs(raw, exist_ok=True)
     base = ["--workload", workload, "--no-cpu-baseline"] + (["--path", "resident"] if resident else [])
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "3", "--warmup", "1"], 600)
@@ -593,7 +595,7 @@ def collect_profiles_split(workload: str, tp: int) -> int:
     """Kernel trace of the split path's three kernels (stats per shard, combine, gradient per shard)."""
     import synth
     w = synth.WORKLOADS[workload]
-    raw = os.path.join(ROOT, "gpurun_out", "profiles_raw", f"{workload}_split_tp{tp}")
+    raw = os.path.join(RAW_PROFILES, f"{workload}_split_tp{tp}")
     os.makedirs(raw, exist_ok=True)
     base = ["--workload", workload, "--no-cpu-baseline", "--path", "split", "--tp", str(tp)]
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
