@@ -54,8 +54,8 @@ typedef enum { LCE_RED_NONE = 0, LCE_RED_MEAN = 1, LCE_RED_SUM = 2 } lce_reducti
 /*
  * Bytes of device workspace lce_ce_fwd_bwd needs for n rows of V columns
  * (256 + 16 * min(n, 4096); always > 0).  The workspace holds the completion
- * counter of the final reduction, the counter the workgroups draw rows from,
- * and per-workgroup partial counts.
+ * counter of the final reduction, the counters the workgroups draw rows and
+ * ignored-row chunks from, and per-workgroup partial counts.
  */
 size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
 
@@ -89,10 +89,10 @@ size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
  *                 n_correct = #{valid i : argmax_i == y_i} (0 when argmax_out
  *                 is NULL).  Token accuracy = n_correct / n_valid.
  *   workspace     device scratch of at least lce_ce_workspace_bytes(n, V)
- *                 bytes, 16-byte aligned.  Its first 8 bytes (a completion
- *                 counter and a row counter) must be zero before the first
- *                 call (zero-fill it once at allocation); every call leaves
- *                 them zero again.  Calls that share a
+ *                 bytes, 16-byte aligned.  Its first 16 bytes (counters)
+ *                 must be zero before the first call (zero-fill it once at
+ *                 allocation); every call leaves them zero again.  Calls
+ *                 that share a
  *                 workspace must not run concurrently.
  * loss_tok, argmax_out, counts, workspace and loss_out must not overlap the
  * logits or each other.  n == 0 is valid (counts and loss_out become 0).

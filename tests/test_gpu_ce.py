@@ -275,7 +275,7 @@ def test_deterministic_replay(want_argmax):
         for a, b in zip(outs[0], other):
             assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
     # the workspace's counters are back to zero after every call
-    assert int(ws[:8].view(torch.int64).cpu()[0]) == 0
+    assert ws[:16].view(torch.int64).cpu().tolist() == [0, 0]
     run_and_check(x, y, V, want_argmax=want_argmax, rows=np.arange(0, n, 97))
 
 
@@ -324,7 +324,7 @@ def test_graph_replay():
         got = [from_dev(buf), loss_tok.cpu().numpy(), loss_out.cpu().numpy(), counts.cpu().numpy()]
         for a, b in zip(want, got):
             assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
-    assert int(ws[:8].view(torch.int64).cpu()[0]) == 0
+    assert ws[:16].view(torch.int64).cpu().tolist() == [0, 0]
 
 
 @pytest.mark.parametrize("pattern", ["long_ignored_runs", "all_ignored"])

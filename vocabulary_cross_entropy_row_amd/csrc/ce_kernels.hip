@@ -124,10 +124,11 @@ __global__ __launch_bounds__(1024) void ce_count_kernel(const int64_t *labels, i
         counts[1] = 0;
         counts[2] = b;
         if (ticket) {
-            // the row kernel's completion and row counters: a caller-clobbered
-            // workspace (the fused linear call's) starts from zero
+            // the row kernel's completion, row and zeroing-chunk counters: a
+            // caller-clobbered workspace (the fused linear call's) starts from zero
             ticket[0] = 0u;
             ticket[1] = 0u;
+            ticket[2] = 0u;
         }
         if (loss_out) *loss_out = 0.0f;
     }

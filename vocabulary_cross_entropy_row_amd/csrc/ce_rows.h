@@ -41,12 +41,15 @@
 namespace lce {
 namespace dev {
 
-// Workspace layout: [0,4) completion counter, [4,8) row counter (both zero
-// between calls), [256, 256 + 8G) int64 n_correct partials.
+// Workspace layout: [0,4) completion counter, [4,8) row counter, [8,12) counter
+// of the ignored-row chunks (all zero between calls), [256, 256 + 8G) int64
+// n_correct partials.
 constexpr size_t kWsPartials = 256;
-// Ignored rows one draw may step over (their zeroing is queued for the drawing
-// workgroup); past that the ignored row is processed with scale 0.
-constexpr int kZeroMax = 16;
+// Ignored rows one draw may step over; past that the ignored row is processed
+// (with scale 0) instead of drawing again.
+constexpr int kSkipMax = 16;
+// Rows per chunk of the end-of-call pass that zeroes ignored rows.
+constexpr int kZeroChunk = 64;
 
 // Word 3 of a gfx9-family buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
@@ -55,6 +58,7 @@ constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ unsigned *ws_ticket(void *ws) { return static_cast<unsigned *>(ws); }
 __device__ __forceinline__ unsigned *ws_rows(void *ws) { return static_cast<unsigned *>(ws) + 1; }
+__device__ __forceinline__ unsigned *ws_zero_chunks(void *ws) { return static_cast<unsigned *>(ws) + 2; }
 __device__ __forceinline__ long long *ws_correct(void *ws) {
     return reinterpret_cast<long long *>(static_cast<char *>(ws) + kWsPartials);
 }
@@ -68,6 +72,9 @@ __device__ __forceinline__ long long *ws_correct(void *ws) {
 // operation issued before it, the row loads included.
 __device__ __forceinline__ unsigned draw_row(void *ws) {
     return __builtin_amdgcn_atomic_inc32(ws_rows(ws), 0xffffffffu, __ATOMIC_RELAXED, "");
+}
+__device__ __forceinline__ unsigned draw_zero_chunk(void *ws) {
+    return __builtin_amdgcn_atomic_inc32(ws_zero_chunks(ws), 0xffffffffu, __ATOMIC_RELAXED, "");
 }
 __device__ __forceinline__ void store_through(float *p, float v) {
     __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
@@ -91,11 +98,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     __shared__ double sh_d[NWAVE];
     __shared__ float sh_xy[2];
     __shared__ int sh_flag;
-    // the schedule, published by thread 0 at each row's combine barrier: the next
-    // row, and the ignored rows its draws stepped over (zeroed by this workgroup)
+    // the schedule, published by thread 0 at each row's combine barrier
     __shared__ int64_t sh_next[2];
-    __shared__ int sh_nz[2];
-    __shared__ int64_t sh_zero[2][kZeroMax];
+    __shared__ unsigned long long sh_ign[2];   // ignored rows of a zeroing chunk
+    __shared__ unsigned sh_chunk[2];
 
     const int tid = threadIdx.x;
     const int wave_base = tid & ~63;
@@ -163,8 +169,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // a round of the resident row as a 16-byte vector
     auto round_vec = [&](int k) -> u32x4 { return k >= KL ? v[k >= KL ? k - KL : 0] : lds_rows[k * NT + tid]; };
 
-    // zero gradient and loss of an ignored row the schedule stepped over:
-    // stores only, issued after a row's own stores so they overlap its traffic
+    // zero gradient and loss of an ignored row: stores only
     auto zero_row = [&](int64_t r) {
         const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
 #pragma unroll
@@ -352,17 +357,15 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             }
             if (tid == 0) {
                 // resolve the schedule: without the argmax, ignored rows are
-                // not read; they are zeroed by this workgroup after its row
-                int nz = 0;
+                // not read here; they are zeroed at the end of the call by the
+                // workgroups that have run out of rows
                 if constexpr (!ARGMAX) {
-                    while (nx < n && !valid_label(ynx) && nz < kZeroMax) {
-                        sh_zero[pb][nz++] = nx;
+                    for (int skips = 0; nx < n && !valid_label(ynx) && skips < kSkipMax; ++skips) {
                         nx = static_cast<int64_t>(G) + static_cast<int64_t>(draw_row(a.workspace));
                         if (nx < n) ynx = a.labels[nx];
                     }
                 }
                 sh_next[pb] = nx;
-                sh_nz[pb] = nz;
             }
             __syncthreads();
             float M = sh_m[pb][0];
@@ -416,6 +419,9 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             cap.r_q(xy, ry, qy);
             gy *= Cap::chain(ry, qy);
         }
+        // an ignored row's gradient is +0 everywhere (0 times a negative factor
+        // would store -0 here, while the end-of-call zeroing stores +0)
+        if (!valid) gy = 0.0f;
         opaque_regs(v);
         auto grad_round = [&](int k) {
             const u32x4 vk = round_vec(k);
@@ -477,10 +483,28 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
             store_through(a.loss_tok + row, loss);
             if constexpr (ARGMAX) a.argmax_out[row] = am;
         }
-        // ignored rows the draws stepped over
-        if constexpr (!ARGMAX) {
-            const int nz = sh_nz[pb];
-            for (int i = 0; i < nz; ++i) zero_row(sh_zero[pb][i]);
+    }
+
+    // ---- without the argmax, the ignored rows are zeroed last, in chunks of
+    // kZeroChunk rows drawn from their own counter, by the workgroups that have
+    // run out of rows: this moves the stores into the time that workgroups
+    // finishing early would otherwise sit idle.  An ignored row that was also
+    // carried through the row loop (a first row, or past kSkipMax skips) gets
+    // zeros twice: the same bytes.
+    if constexpr (!ARGMAX) {
+        for (int q = 0;; q ^= 1) {
+            if (tid == 0) sh_chunk[q] = draw_zero_chunk(a.workspace);
+            __syncthreads();
+            const int64_t c0 = static_cast<int64_t>(sh_chunk[q]) * kZeroChunk;
+            if (c0 >= n) break;
+            if (tid < 64) {
+                const int64_t r = c0 + tid;
+                const bool ign = r < n && !valid_label(a.labels[r]);
+                const unsigned long long m = __ballot(ign);
+                if (tid == 0) sh_ign[q] = m;
+            }
+            __syncthreads();
+            for (unsigned long long m = sh_ign[q]; m; m &= m - 1) zero_row(c0 + __builtin_ctzll(m));
         }
     }
 
@@ -547,6 +571,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         a.counts[2] = n_bad;
         *ws_ticket(a.workspace) = 0u;
         *ws_rows(a.workspace) = 0u;
+        *ws_zero_chunks(a.workspace) = 0u;
     }
 }
 
