@@ -485,17 +485,18 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         }
     }
 
-    // ---- without the argmax, the ignored rows are zeroed last, in chunks of
-    // kZeroChunk rows drawn from their own counter, by the workgroups that have
-    // run out of rows: this moves the stores into the time that workgroups
-    // finishing early would otherwise sit idle.  An ignored row that was also
-    // carried through the row loop (a first row, or past kSkipMax skips) gets
-    // zeros twice: the same bytes.
+    // ---- without the argmax, the ignored rows the walk stepped over (all at or
+    // past row G: the first rows are carried through) are zeroed last, in
+    // chunks of kZeroChunk rows drawn from their own counter, by the
+    // workgroups that have run out of rows: this moves the stores into the
+    // time that workgroups finishing early would otherwise sit idle.  An
+    // ignored row that was also carried through the row loop (past kSkipMax
+    // skips) gets zeros twice: the same bytes.
     if constexpr (!ARGMAX) {
-        for (int q = 0;; q ^= 1) {
+        for (int q = 0; G < n; q ^= 1) {
             if (tid == 0) sh_chunk[q] = draw_zero_chunk(a.workspace);
             __syncthreads();
-            const int64_t c0 = static_cast<int64_t>(sh_chunk[q]) * kZeroChunk;
+            const int64_t c0 = static_cast<int64_t>(G) + static_cast<int64_t>(sh_chunk[q]) * kZeroChunk;
             if (c0 >= n) break;
             if (tid < 64) {
                 const int64_t r = c0 + tid;
