@@ -543,6 +543,7 @@ def bench_split(args, w) -> int:
                    "parallelism": f"vocabulary split into {tp} shards on one GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "traffic_scope": "every kernel of one step (rocprofv3 FETCH_SIZE + WRITE_SIZE, profiles/)",
                      "kernel": "stats + combine + gradient calls of one step, HIP events", "phase_ms": phase,
                      "stats_GBps": round(w.n * w.V * w.elem_bytes / (phase["stats"] * 1e-3) / 1e9, 1),
                      "grad_GBps": round(2 * w.n * w.V * w.elem_bytes / (phase["grad"] * 1e-3) / 1e9, 1),
@@ -552,6 +553,8 @@ def bench_split(args, w) -> int:
     prof = read_split_profile(w.name, tp)
     if prof:
         out["roofline"]["rocprof_kernel_ns"] = {k: float(v) for k, v in prof.items() if k.endswith("_avg_ns")}
+        if "traffic_bytes_per_step" in prof:
+            out["roofline"]["traffic"] = int(float(prof["traffic_bytes_per_step"]))
     if not args.no_cpu_baseline:
         nthr = len(os.sched_getaffinity(0))
         if os.environ.get("OMP_NUM_THREADS"):
@@ -591,15 +594,33 @@ def read_split_profile(workload: str, tp: int) -> dict | None:
     return kv
 
 
+SPLIT_KERNELS = ("ce_stats_kernel", "ce_combine", "ce_grad_kernel", "ce_count_kernel", "loss_fold_kernel")
+
+
 def collect_profiles_split(workload: str, tp: int) -> int:
-    """Kernel trace of the split path's three kernels (stats per shard, combine, gradient per shard)."""
+    """Kernel trace of the split path's three kernels (stats per shard, combine, gradient per shard),
+    then FETCH_SIZE and WRITE_SIZE of every kernel a step launches, scaled like the fused path's."""
     import synth
     w = synth.WORKLOADS[workload]
     raw = os.path.join(RAW_PROFILES, f"{workload}_split_tp{tp}")
     os.makedirs(raw, exist_ok=True)
     base = ["--workload", workload, "--no-cpu-baseline", "--path", "split", "--tp", str(tp)]
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
+    _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "5", "--warmup", "2"], 180)
+    _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "5", "--warmup", "2"], 180)
     stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
+    copy_kib = w.n * w.V * w.elem_bytes / 1024.0          # the pristine copy made for each step
+
+    def counter(sub: str, cname: str):
+        rows = [r for r in csv.DictReader(open(os.path.join(raw, sub, "run_counter_collection.csv")))
+                if r["Counter_Name"] == cname]
+        ours = sum(float(r["Counter_Value"]) for r in rows if any(k in r["Kernel_Name"] for k in SPLIT_KERNELS))
+        c = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 4096]
+        return ours / 7.0, sum(c) / len(c)   # 2 warmup + 5 timed steps
+
+    fk, fc = counter("fetch", "FETCH_SIZE")
+    wk, wc = counter("write", "WRITE_SIZE")
+    traffic = (fk * copy_kib / fc + wk * copy_kib / wc) * 1024.0
     b = " ".join(base)
     lines = [
         f"# rocprofv3 summary: split cross-entropy (lce_ce_stats per shard, lce_ce_combine, lce_ce_grad per shard),",
@@ -607,6 +628,10 @@ def collect_profiles_split(workload: str, tp: int) -> int:
         f"# made by: python bench.py --collect-profiles --workload {workload} --path split --tp {tp}",
         "# which runs, from /tmp with TMPDIR=/tmp:",
         f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 10 --warmup 3",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <raw>/fetch -o run -- python bench.py {b} --steps 5 --warmup 2",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <raw>/write -o run -- python bench.py {b} --steps 5 --warmup 2",
+        "# Counter scale: what each counter reads for the plain copy (__amd_rocclr_copyBuffer) of the pristine",
+        f"# logits -- a known {copy_kib:.0f} KiB read + {copy_kib:.0f} KiB write -- divided into that size.",
         "# kernel trace (--stats), nanoseconds per launch (13 steps; stats and grad launch once per shard):",
     ]
     for r in stats:
@@ -619,6 +644,9 @@ def collect_profiles_split(workload: str, tp: int) -> int:
             lines.append(f"{key}_avg_ns: {ns:.1f}")
     shard_bytes = w.n * (w.V // tp) * w.elem_bytes
     lines += [f"stats_bytes_per_launch: {shard_bytes}", f"grad_bytes_per_launch: {2 * shard_bytes}",
+              f"fetch_kib_per_step: {fk:.1f}", f"fetch_scale: {copy_kib / fc:.4f}",
+              f"write_kib_per_step: {wk:.1f}", f"write_scale: {copy_kib / wc:.4f}",
+              f"traffic_bytes_per_step: {traffic:.0f}",
               f"kernel_source_sha256_16: {split_source_hash()}"]
     os.makedirs(PROFILES, exist_ok=True)
     with open(split_profile_path(workload, tp), "w") as f:
