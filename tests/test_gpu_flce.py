@@ -103,6 +103,7 @@ SHAPES = [
     (77, 136, 520, 32, 0.0, 30.0, "mean"),
     (1, 64, 512, 1024, 0.0, 0.0, "mean"),
     (512, 1024, 3072, 256, 0.2, 30.0, "mean"),
+    (200, 264, 2056, 64, 0.1, 0.1, "sum"),     # strong cap: tanh saturated for most logits
 ]
 
 

@@ -135,6 +135,7 @@ SHAPES = [
     (1, 64, 512, 1024, 0.0, 0.0, "mean"),
     (512, 1024, 3072, 256, 0.2, 30.0, "mean"),
     (257, 72, 264, 100, 0.05, 0.0, "mean"),
+    (200, 264, 2056, 64, 0.1, 0.1, "sum"),     # strong cap: tanh saturated for most logits
 ]
 
 
