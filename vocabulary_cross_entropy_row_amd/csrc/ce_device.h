@@ -44,13 +44,14 @@ struct Cap {
     __device__ __forceinline__ float z_of_r(float r) const { return fmaf(-2.0f * T, r, T); }
     // r and q = 1 - r for the chain factor.  q is formed as r e (e = e^{2u}), not
     // as 1 - r: where tanh saturates below zero r rounds towards 1 and 1 - r would
-    // lose all its digits, while r e keeps full relative precision.  e is capped
-    // at 2^126 so that r e stays finite where tanh saturates above zero (there
-    // r = 2^-126, q = 1, and the factor underflows as the exact one does).
+    // lose all its digits, while r e keeps full relative precision.  Where tanh
+    // saturates above zero e overflows to inf and r to 0; r e is then NaN, and
+    // the min turns it into q = 1, so the factor 4 r q is 0 as the exact one
+    // (4 e^{-2u} there) rounds to.
     __device__ __forceinline__ void r_q(float x, float &r, float &q) const {
-        const float e = exp2_fast(fminf(x * c2, 126.0f));
+        const float e = exp2_fast(x * c2);
         r = rcp_fast(1.0f + e);
-        q = r * e;
+        q = fminf(r * e, 1.0f);
     }
     __device__ __forceinline__ static float chain(float r, float q) { return 4.0f * r * q; }
 };
