@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from parity import check_bf16_grad, check_f32_grad, check_loss, row_scales, smoothing_allowance
+from parity import check_bf16_grad, check_f32_grad, check_loss, lse_rounding, row_scales, smoothing_allowance
 
 torch = pytest.importorskip("torch")
 
@@ -87,7 +87,8 @@ def run_and_check(x: np.ndarray, y: np.ndarray, V: int, *, eps=0.0, T=0.0, red="
         # the cancellation allowance is for isolated elements with p_j ~ eps/V only
         assert n_allow <= max(4, g.size // 1000), f"{n_allow} of {g.size} entries needed the allowance"
     else:
-        check_f32_grad(g, o["grad"], row_scales(red, grad_out, y, V)[idx])
+        zmax = np.abs(x[idx, :V].astype(np.float64)).max(axis=1) if T == 0 else np.full(len(idx), float(T))
+        check_f32_grad(g, o["grad"], row_scales(red, grad_out, y, V)[idx], lse_rel=lse_rounding(zmax, V))
     if ld > V:   # padding columns are never touched
         assert np.array_equal(out[:, V:].view(np.uint8), x[:, V:].view(np.uint8)), "padding modified"
     return res, out
@@ -201,6 +202,25 @@ def test_full_smoothing_and_strong_cap(n, V, ld, dt, eps, T):
     y = _labels(rng, n, V)
     for red, go in (("mean", [1.0]), ("sum", [0.5]), ("none", rng.normal(size=n))):
         run_and_check(x, y, V, eps=eps, T=T, red=red, grad_out=go, want_argmax=T > 0)
+
+
+@pytest.mark.parametrize("dt,V", [("bf16", 131072), ("bf16", 4096), ("f32", 4096)], ids=["bf16-131072", "bf16-4096", "f32-4096"])
+def test_large_magnitudes(dt, V):
+    """Logits of magnitude ~1e3 (the running max jumps by hundreds, so the rescale factors
+    underflow to zero), rows with one +1e4 spike at a random column (a one-hot softmax,
+    the target on or off the spike), and a softcap over the same rows (tanh fully saturated)."""
+    rng = np.random.default_rng([V, 41])
+    n = 12
+    x = (rng.standard_normal((n, V)) * 1000.0).astype(np.float32)
+    y = rng.integers(0, V, n).astype(np.int64)
+    spikes = rng.integers(0, V, n)
+    for i in range(6, n):
+        x[i, spikes[i]] = 1.0e4
+    y[6:9] = spikes[6:9]          # target on the spike: loss ~ 0, gradient ~ 0
+    xx = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    run_and_check(xx, y, V, want_argmax=True)
+    run_and_check(xx, y, V, eps=0.1, red="sum", grad_out=[0.5])
+    run_and_check(xx, y, V, T=30.0, want_argmax=True)
 
 
 def test_uniform_rows_give_log_v():
