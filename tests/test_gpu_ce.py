@@ -223,6 +223,26 @@ def test_large_magnitudes(dt, V):
     run_and_check(xx, y, V, T=30.0, want_argmax=True)
 
 
+def test_subnormal_gradients_flush_to_zero():
+    """Rows where some p_j fall just below the smallest normal number (z_j - LSE ~ -90, so
+    p_j ~ 8e-40, a bf16 subnormal in the oracle) next to elements just above it (z_j - LSE ~ -85):
+    the former are stored as 0 (flush to zero), the latter within 2 ulps."""
+    V = 4096
+    x = np.full((4, V), -1000.0, dtype=np.float32)
+    x[:, 0] = 0.0
+    x[:, 1:9] = -90.0
+    x[:, 9:17] = -85.0
+    x[:, 17:25] = -87.0
+    y = np.array([0, 5, 12, 3000])
+    xb = synth.f32_to_bf16_bits(x)
+    res, out = run_and_check(xb, y, V, red="sum")
+    bits = out.view(np.uint16)
+    # (row 1's target, column 5, and row 2's, column 12, sit inside the blocks: left out below)
+    assert np.all(bits[[0, 2, 3]][:, 1:9] & 0x7FFF == 0)    # e^-90 < 2^-126: flushed to (+/-)0
+    assert np.all(bits[[0, 1, 3]][:, 9:17] & 0x7F80 != 0)   # e^-85 > 2^-126: stored as a normal number
+    assert np.all(bits[:, 17:25] & 0x7F80 != 0)              # e^-87 = 1.6e-38, just above 2^-126: stored
+
+
 def test_uniform_rows_give_log_v():
     V = 131072
     x = np.zeros((4, V), dtype=np.uint16)
