@@ -223,6 +223,20 @@ def test_large_magnitudes(dt, V):
     run_and_check(xx, y, V, T=30.0, want_argmax=True)
 
 
+@pytest.mark.parametrize("n,V", [(20000, 64), (257, 4096), (513, 8192)], ids=["20000x64", "257x4096", "513x8192"])
+@pytest.mark.parametrize("feat", ["plain", "argmax_smooth_cap"])
+def test_schedule_many_rows_and_edges(n, V, feat):
+    """The dynamic row schedule with many short rows (~80 draws per workgroup, hundreds of
+    zeroing chunks) and with one or two rows past the grid; 15 % ignored rows."""
+    rng = np.random.default_rng([n, V, len(feat)])
+    x = make_logits(rng, n, V, V, "bf16")
+    y = _labels(rng, n, V, ignore_frac=0.15)
+    if feat == "plain":
+        run_and_check(x, y, V)
+    else:
+        run_and_check(x, y, V, eps=0.1, T=20.0, red="sum", grad_out=[0.7], want_argmax=True)
+
+
 def test_subnormal_gradients_flush_to_zero():
     """Rows where some p_j fall just below the smallest normal number (z_j - LSE ~ -90, so
     p_j ~ 8e-40, a bf16 subnormal in the oracle) next to elements just above it (z_j - LSE ~ -85):
