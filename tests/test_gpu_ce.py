@@ -237,6 +237,23 @@ def test_schedule_many_rows_and_edges(n, V, feat):
         run_and_check(x, y, V, eps=0.1, T=20.0, red="sum", grad_out=[0.7], want_argmax=True)
 
 
+@pytest.mark.parametrize("V,dt", [(8 * 1024 * 18 + 8 * 5, "bf16"), (131072, "bf16"), (60000, "f32")],
+                         ids=["bf16-147496", "bf16-131072", "f32-60000"])
+def test_labels_at_round_boundaries(V, dt):
+    """Targets on the first and last element of a row, of a 16-byte vector, of a round of
+    1024 vectors (the LDS / register boundary included) and of a partial last round: the
+    owner thread and element of the target are computed, not looked up."""
+    E = 8 if dt == "bf16" else 4
+    R = 1024 * E
+    cand = {0, 1, E - 1, E, R - 1, R, 2 * R - 1, 2 * R, 8 * R - 1, 8 * R, 9 * R - 1, 9 * R, V - E, V - 1}
+    y = np.array(sorted(c for c in cand if 0 <= c < V), dtype=np.int64)
+    n = len(y)
+    rng = np.random.default_rng([V, 51])
+    x = make_logits(rng, n, V, V, dt)
+    run_and_check(x, y, V, want_argmax=True)
+    run_and_check(x, y, V, eps=0.2, T=10.0, red="none", grad_out=rng.normal(size=n))
+
+
 def test_subnormal_gradients_flush_to_zero():
     """Rows where some p_j fall just below the smallest normal number (z_j - LSE ~ -90, so
     p_j ~ 8e-40, a bf16 subnormal in the oracle) next to elements just above it (z_j - LSE ~ -85):
