@@ -117,6 +117,25 @@ FEATS = {
 }
 
 
+@pytest.mark.parametrize("widths", [[4096], [1024, 1024, 2048], [512] * 8], ids=["tp1", "tp3", "tp8"])
+def test_split_large_magnitudes(widths):
+    """bf16 logits ~N(0, 1000^2) with +1e4 spikes (target on and off them), plain, smoothed and
+    softcapped: statistics that underflow across shards, a one-hot softmax, saturated tanh."""
+    V = sum(widths)
+    rng = np.random.default_rng([V, len(widths), 61])
+    n = 10
+    x = (rng.standard_normal((n, V)) * 1000.0).astype(np.float32)
+    y = rng.integers(0, V, n).astype(np.int64)
+    sp = rng.integers(0, V, n)
+    for i in range(5, n):
+        x[i, sp[i]] = 1.0e4
+    y[5:7] = sp[5:7]
+    xb = synth.f32_to_bf16_bits(x)
+    check_split(xb, y, V, widths)
+    check_split(xb, y, V, widths, eps=0.1, red="sum", grad_out=[0.5])
+    check_split(xb, y, V, widths, T=30.0)
+
+
 @pytest.mark.parametrize("n,V,dt,widths", CASES, ids=[f"{c[0]}x{c[1]}{c[2]}_tp{len(c[3])}" for c in CASES])
 @pytest.mark.parametrize("feat", list(FEATS))
 def test_split_matrix(n, V, dt, widths, feat):

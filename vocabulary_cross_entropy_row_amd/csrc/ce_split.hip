@@ -8,7 +8,7 @@
 //
 //   stats    one read of a shard [n, Vs] of the logits (global columns
 //            [v0, v0 + Vs)): per row m = max z, s = sum_{j != y} e^{z - m},
-//            e = sum_j e^{z - m} z, sum z, the target's z when it lies in the
+//            e = sum_{j != y} e^{z - m} z, sum z, the target's z when it lies in the
 //            shard, and the shard's first-index argmax of the raw logits.
 //   combine  per row over the shards (in ascending v0): lse, 1 - p_y, the loss,
 //            log p_y and the entropy (labs-molt PR "Enable Liger layers": the
@@ -40,7 +40,7 @@ using dev::u32x4;
 struct Part {
     float m = -FLT_MAX;   // running max of z (finite start: no inf - inf)
     float s = 0.0f;       // sum over j != target of e^{z - m}
-    float e = 0.0f;       // sum over j of e^{z - m} z
+    float e = 0.0f;       // sum over j != target of e^{z - m} z
     float zs = 0.0f;      // sum of z
     float amv = -INFINITY;
     int am = 0x7fffffff;  // shard-local index of the first maximum of the raw logits
@@ -140,16 +140,19 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
                 p.amv = xmax;
                 p.am = vi * E + first;
             }
+            // Every weight here carries the same rounding of mn * log2e (|mn| * 2^-24
+            // relative), which cancels between s and e; the target's weight is formed
+            // exactly in the combine, so the target stays out of both sums (inside e it would
+            // leave an entropy error of |z_y| times that rounding).
             const float mn = fmaxf(p.m, rmax), mnL = mn * kLog2e;
             const float f = dev::exp2_fast(fmaf(p.m, kLog2e, -mnL));
             float ex[E], pe = 0.0f, zsum = 0.0f;
 #pragma unroll
             for (int k = 0; k < E; ++k) {
                 ex[k] = dev::exp2_fast(fmaf(z[k], kLog2e, -mnL));
-                pe = fmaf(ex[k], z[k], pe);
                 zsum += z[k];
             }
-            if (vi == yv) {   // the target's vector: its element stays out of s
+            if (vi == yv) {   // the target's vector: its element stays out of s and e
 #pragma unroll
                 for (int k = 0; k < E; ++k)
                     if (k == ye) {
@@ -157,6 +160,8 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
                         ex[k] = 0.0f;
                     }
             }
+#pragma unroll
+            for (int k = 0; k < E; ++k) pe = fmaf(ex[k], z[k], pe);
             float ps = ex[0];
 #pragma unroll
             for (int k = 1; k < E; ++k) ps += ex[k];
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int
     if (q_out) q_out[i] = valid ? t.s / S : 0.0f;
     if (loss_tok) loss_tok[i] = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
     if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
-    if (ent_out) ent_out[i] = lse - t.e / S;   // -sum p log p = lse - sum p z
+    if (ent_out) ent_out[i] = lse - fmaf(ey, zy, t.e) / S;   // -sum p log p = lse - sum p z
     if (argmax_out) argmax_out[i] = am;
     if (valid && am == y) __hip_atomic_fetch_add(reinterpret_cast<unsigned long long *>(counts + 1), 1ull,
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(256) void ce_combine_wide_kernel(const float *stats
     if (q_out) q_out[i] = valid ? t.s / S : 0.0f;
     if (loss_tok) loss_tok[i] = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
     if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
-    if (ent_out) ent_out[i] = lse - t.e / S;
+    if (ent_out) ent_out[i] = lse - fmaf(ey, zy, t.e) / S;
     if (argmax_out) argmax_out[i] = am;
     if (valid && am == y) __hip_atomic_fetch_add(reinterpret_cast<unsigned long long *>(counts + 1), 1ull,
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -29,7 +29,7 @@
 // the fused linear cross-entropy; the Muse Glimmer page's Summary asks for the
 // loss without the [tokens, V] logits):
 //   OUT_STATS  reduces each row of the fp32 tile to one stats record (running
-//              max, sum of exponentials without the target, sum of e^{z-m} z,
+//              max, sums of e^{z-m} and of e^{z-m} z without the target,
 //              sum of z, first argmax of the raw logits, the target's z);
 //   OUT_GRAD   recomputes the same tile and stores the bf16 gradient
 //              s (p - (1 - eps)[j = y] - eps / V) dz/dx from the row's
@@ -222,14 +222,14 @@ __device__ __forceinline__ void stats_epilogue(const GemmArgs &g, f16v (&acc)[WI
                     if (!cv[j]) continue;
                     const float z = acc[i][j][rb + u];
                     float ex = dev::exp2_fast(fmaf(z, kL2e, -mL));
-                    se[u] = fmaf(ex, z, se[u]);
                     sz[u] += z;
-                    if (cbase + j * 32 == yr) {   // the target: its z, and out of the sum
+                    if (cbase + j * 32 == yr) {   // the target: its z, and out of both sums
                         rec_w[rl * 8 + 6] = z;
                         rec_w[rl * 8 + 7] = 1.0f;
                         ex = 0.0f;
                     }
                     sx[u] += ex;
+                    se[u] = fmaf(ex, z, se[u]);
                 }
             }
 #pragma unroll

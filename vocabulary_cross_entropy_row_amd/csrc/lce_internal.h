@@ -66,8 +66,8 @@ hipError_t launch_loss_fold(const float *loss_tok, int64_t n, const int64_t *cou
 
 // ---- split cross-entropy: shard statistics, combine, gradient ----------------
 
-// One stats record per row and shard: 8 floats (max z, sum of e^{z-max} without
-// the target, sum of e^{z-max} z, sum z, argmax value, global argmax index as
+// One stats record per row and shard: 8 floats (max z, sums of e^{z-max} and of
+// e^{z-max} z without the target, sum z, argmax value, global argmax index as
 // int bits, target z, target-present flag).
 constexpr int kStatsFloats = 8;
 hipError_t launch_ce_stats(const void *logits, int64_t ld, bool is_bf16, const int64_t *labels, int64_t n,
