@@ -36,55 +36,75 @@ using gemm::GemmArgs;
 
 // out[c][r] = in[r][c] for a [rows, cols] bf16 matrix (strides in elements);
 // output columns [rows, rows_pad) are written as zeros, so a GEMM may run its
-// K loop over whole 8-element chunks.  64 x 64 tiles through LDS; 16-byte
-// loads and stores where aligned.
+// K loop over whole 8-element chunks.  A workgroup moves a tile of kTrRows input
+// rows x 64 columns through LDS: each 16-byte chunk of an input row lands in LDS
+// with one 16-byte write, in slot (chunk ^ (row / 8) % 8) of its 128-byte LDS
+// row, so the writes of a wave cover 1 KB without conflicts and the 2-byte
+// reads of one output chunk (eight input rows, one column) from eight lanes
+// with different row groups fall in different banks.  16-byte global loads and
+// stores where aligned; each thread has four loads in flight.
+constexpr int kTrRows = 128;
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *in, int64_t ld_in, uint16_t *out,
                                                              int64_t ld_out, int rows, int rows_pad, int cols) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __shared__ uint16_t tile[64][64 + 8];
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    constexpr int kPer = kTrRows * 8 / 256;   // 16-byte chunks per thread, each way
+    __shared__ __align__(16) uint16_t tile[kTrRows * 64];
+    const int r0 = blockIdx.y * kTrRows, c0 = blockIdx.x * 64;
     const int t = threadIdx.x;
     const bool vin = ((ld_in & 7) == 0) && ((reinterpret_cast<uintptr_t>(in) & 15) == 0);
     const bool vout = ((ld_out & 7) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
-    // load: 64 rows x 8 chunks of 8 columns; 2 chunks per thread
+    u32x4 q[kPer];
+    if (vin && r0 + kTrRows <= rows && c0 + 64 <= cols) {   // interior tile: no checks, every load in flight
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int idx = t + h * 256;
-        const int r = idx >> 3, ch = idx & 7;
-        const int gr = r0 + r, gc = c0 + ch * 8;
-        if (vin && gr < rows && gc + 7 < cols) {
-            const u32x4 q = *reinterpret_cast<const u32x4 *>(in + static_cast<int64_t>(gr) * ld_in + gc);
+        for (int h = 0; h < kPer; ++h) {   // chunk ch of input row r
+            const int idx = t + h * 256, r = idx >> 3, ch = idx & 7;
+            q[h] = *reinterpret_cast<const u32x4 *>(in + static_cast<int64_t>(r0 + r) * ld_in + c0 + ch * 8);
+        }
+    } else {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                tile[r][ch * 8 + 2 * w] = static_cast<uint16_t>(q[w] & 0xffffu);
-                tile[r][ch * 8 + 2 * w + 1] = static_cast<uint16_t>(q[w] >> 16);
+        for (int h = 0; h < kPer; ++h) {
+            const int idx = t + h * 256, r = idx >> 3, ch = idx & 7;
+            const int gr = r0 + r, gc = c0 + ch * 8;
+            if (vin && gr < rows && gc + 7 < cols) {
+                q[h] = *reinterpret_cast<const u32x4 *>(in + static_cast<int64_t>(gr) * ld_in + gc);
+            } else {
+                uint16_t v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = (gr < rows && gc + e < cols) ? in[static_cast<int64_t>(gr) * ld_in + gc + e] : uint16_t(0);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) q[h][w] = v[2 * w] | (static_cast<uint32_t>(v[2 * w + 1]) << 16);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                tile[r][ch * 8 + e] =
-                    (gr < rows && gc + e < cols) ? in[static_cast<int64_t>(gr) * ld_in + gc + e] : uint16_t(0);
         }
     }
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int idx = t + h * 256, r = idx >> 3, ch = idx & 7;
+        *reinterpret_cast<u32x4 *>(tile + r * 64 + ((ch ^ (r >> 3)) & 7) * 8) = q[h];
+    }
     __syncthreads();
-    // store: output rows are input columns
+    // output row orow (= input column c0 + orow), chunk ch of eight input rows; a wave
+    // takes eight output rows and eight chunks of each (128 contiguous bytes per row)
+    const bool full_out = vout && r0 + kTrRows <= rows_pad && c0 + 64 <= cols;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kPer; ++h) {
         const int idx = t + h * 256;
-        const int orow = idx >> 3, ch = idx & 7;     // orow = input column, ch = chunk of input rows
+        const int orow = (idx >> 3) & 63, ch = (idx & 7) + 8 * (idx >> 9);
         const int gc = c0 + orow, gr = r0 + ch * 8;
-        if (gc >= cols) continue;
-        if (vout && gr + 7 < rows_pad) {
-            u32x4 q;
+        const uint16_t *src = tile + ch * 8 * 64 + (((orow >> 3) ^ ch) & 7) * 8 + (orow & 7);
+        uint16_t v[8];
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                q[w] = static_cast<uint32_t>(tile[ch * 8 + 2 * w][orow]) |
-                       (static_cast<uint32_t>(tile[ch * 8 + 2 * w + 1][orow]) << 16);
-            *reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(gc) * ld_out + gr) = q;
-        } else {
+        for (int e = 0; e < 8; ++e) v[e] = src[e * 64];
+        uint16_t *dst = out + static_cast<int64_t>(gc) * ld_out + gr;
+        if (full_out || (vout && gc < cols && gr + 7 < rows_pad)) {
+            u32x4 o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o[w] = v[2 * w] | (static_cast<uint32_t>(v[2 * w + 1]) << 16);
+            *reinterpret_cast<u32x4 *>(dst) = o;
+        } else if (gc < cols) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (gr + e < rows_pad) out[static_cast<int64_t>(gc) * ld_out + gr + e] = tile[ch * 8 + e][orow];
+                if (gr + e < rows_pad) dst[e] = v[e];
         }
     }
 }
@@ -151,7 +171,7 @@ int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, int rows, int rows_pad, int cols,
                      hipStream_t st) {
     if (rows_pad <= 0 || cols <= 0) return hipSuccess;
-    const dim3 grid(ceil_div(cols, 64), ceil_div(rows_pad, 64));
+    const dim3 grid(ceil_div(cols, 64), ceil_div(rows_pad, kTrRows));
     hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t *>(in), ld_in,
                        static_cast<uint16_t *>(out), ld_out, rows, rows_pad, cols);
     return hipGetLastError();
