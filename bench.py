@@ -713,17 +713,26 @@ def main() -> int:
         step(bufs[i])
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # the timed steps: back to back, nothing between the calls
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(bufs[args.warmup + i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-call durations (the roofline's): the same steps again on restored logits, HIP events
+    # around each call on the stream it runs on
+    for i in range(args.steps):
+        bufs[args.warmup + i].copy_(pristine)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
         ev[i][0].record(stream)
         step(bufs[args.warmup + i])
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_call_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
     call_ms = float(np.mean(per_call_ms))
     # context, after the timed region: a plain device copy of the same logits (one read + one write of
     # N V b bytes, the same traffic as one call), HIP events around each copy
