@@ -529,7 +529,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // sums are combined in wave order.  Eight loads go out before the first
     // is added, so the fold waits for one round trip per eight rows per thread.
     double acc = 0.0;
-    long long cor = 0;
+    // this thread's first n_correct partial goes out with the first batch of losses
+    // (clamped like them, masked when added)
+    long long cor = __hip_atomic_load(ws_correct(a.workspace) + (tid < G ? tid : 0), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
     constexpr int kFold = 8;
     for (int64_t r0 = 0; r0 < n; r0 += kFold * NT) {
         float lv[kFold];
@@ -545,7 +548,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         for (int u = 0; u < kFold; ++u)
             if (r0 + u * NT + tid < n) acc += static_cast<double>(lv[u]);
     }
-    for (int w = tid; w < G; w += NT)
+    if (tid >= G) cor = 0;
+    for (int w = tid + NT; w < G; w += NT)
         cor += __hip_atomic_load(ws_correct(a.workspace) + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     acc = wave_sum_d(acc);
     cor = wave_sum_ll(cor);
