@@ -146,6 +146,22 @@ def test_resident_shapes(n, H, V, chunk, eps, T, red):
     check_resident(hb, wb, y, eps=eps, T=T, red=red, grad_out=g, chunk=chunk)
 
 
+@pytest.mark.parametrize("eps,red", [(0.0, "mean"), (0.1, "sum")])
+def test_resident_large_magnitudes(eps, red):
+    """Logits of sigma ~1000 over four 256-column tiles, and rows 0-15 whose target logit is a 3e4 spike
+    (one-hot rows, entropy ~0).  Each tile's weights share the rounding of max * log2(e) (about 2^-9 at
+    these magnitudes); the target's weight is formed exactly when the records are merged, so the target
+    must stay out of both tile sums -- inside the e sum it would move the entropy by |z_y| * 2^-9."""
+    n, H, V = 64, 256, 1024
+    hb, wb, y = gen(n, H, V, seed=31, wsig=62.5)
+    w64 = bits_to_f64(wb)
+    for i in range(16):
+        if y[i] < 0:
+            y[i] = 5 + i
+        hb[i] = synth.f32_to_bf16_bits((w64[y[i]] * (3.0e4 / float(w64[y[i]] @ w64[y[i]]))).astype(np.float32))
+    check_resident(hb, wb, y, eps=eps, red=red, grad_out=[0.5], chunk=64)
+
+
 def test_resident_argmax_ties_and_accuracy():
     """Duplicate weight rows make exact logit ties: the first index wins; accuracy counts it."""
     hb, wb, y = gen(96, 128, 768, seed=5, wsig=0.2)
