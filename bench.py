@@ -502,20 +502,21 @@ def bench_split(args, w) -> int:
     ev = {k: [] for k in ("stats", "combine", "grad")}
 
     def step(buf, timed):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        e[0].record(stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else [None] * 4
+        mark = (lambda i: e[i].record(stream)) if timed else (lambda i: None)  # noqa: E731
+        mark(0)
         for k in range(tp):
             lce.lce_ce_stats(buf[:, k * ws:(k + 1) * ws], labels, v_offset=k * ws, softcap=w.softcap, stats=stats[k],
                              stream=stream)
-        e[1].record(stream)
+        mark(1)
         rows = lce.lce_ce_combine(stats, labels, w.V, label_smoothing=w.label_smoothing, reduction=w.reduction,
                                   stream=stream)
-        e[2].record(stream)
+        mark(2)
         for k in range(tp):
             lce.lce_ce_grad(buf[:, k * ws:(k + 1) * ws], labels, w.V, rows, v_offset=k * ws,
                             label_smoothing=w.label_smoothing, softcap=w.softcap, reduction=w.reduction,
                             grad_out=grad_out, stream=stream)
-        e[3].record(stream)
+        mark(3)
         if timed:
             ev["stats"].append((e[0], e[1]))
             ev["combine"].append((e[1], e[2]))
@@ -524,12 +525,20 @@ def bench_split(args, w) -> int:
 
     for i in range(args.warmup):
         step(bufs[i], False)
+    # the timed steps: back to back, nothing between the calls
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    whole = [step(bufs[args.warmup + i], True) for i in range(args.steps)]
+    for i in range(args.steps):
+        step(bufs[args.warmup + i], False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    # phase and call durations: the same steps again on restored logits, HIP events between the phases
+    for i in range(args.steps):
+        bufs[args.warmup + i].copy_(pristine)
+    torch.cuda.synchronize()
+    whole = [step(bufs[args.warmup + i], True) for i in range(args.steps)]
+    torch.cuda.synchronize()
     call_ms = float(np.mean([a[0].elapsed_time(a[3]) for a in whole]))
     phase = {k: round(float(np.mean([a.elapsed_time(b) for a, b in v])), 5) for k, v in ev.items()}
     nbytes = 3 * w.n * w.V * w.elem_bytes + w.n * (8 + tp * 32 * 2 + 4 * 6)

@@ -90,7 +90,7 @@ __device__ __forceinline__ void wave_part(Part &p) {
 
 constexpr int kStatsThreads = 256;                    // four waves per row: several rows per CU
 constexpr int kStatsWaves = kStatsThreads / 64;
-constexpr int kStatsAhead = 8;                        // 16-byte vectors each thread keeps in flight
+constexpr int kStatsAhead = 4;                        // 16-byte vectors per batch; two batches in flight
 
 template <bool BF16, bool SOFTCAP>
 __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *logits, int64_t ld, int64_t Vs,
@@ -114,11 +114,17 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
 
     Part p;
     float zy = 0.0f;
-    for (int base = 0; base < nvec; base += NTS * kStatsAhead) {
-        u32x4 v[kStatsAhead];
+    // two batches of loads in flight: the next batch goes out before this one is used
+    // (past the row, on the last pass too, the descriptor returns zeros without a memory access)
+    u32x4 v[kStatsAhead];
 #pragma unroll
-        for (int u = 0; u < kStatsAhead; ++u)   // past the row: the descriptor returns zeros
-            v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + u * NTS + tid) * 16, 0, 2);
+    for (int u = 0; u < kStatsAhead; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (u * NTS + tid) * 16, 0, 2);
+    for (int base = 0; base < nvec; base += NTS * kStatsAhead) {
+        u32x4 nx[kStatsAhead];
+#pragma unroll
+        for (int u = 0; u < kStatsAhead; ++u)
+            nx[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + (kStatsAhead + u) * NTS + tid) * 16, 0, 2);
 #pragma unroll
         for (int u = 0; u < kStatsAhead; ++u) {
             const int vi = base + u * NTS + tid;
@@ -170,6 +176,8 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
             p.e = fmaf(p.e, f, pe);
             p.m = mn;
         }
+#pragma unroll
+        for (int u = 0; u < kStatsAhead; ++u) v[u] = nx[u];
     }
     // wave (DPP exchanges, then the four 16-lane rows in a fixed order), then workgroup
     wave_part(p);
