@@ -192,6 +192,51 @@ def test_flce_clobbered_workspace():
         assert torch.equal(getattr(outs[0], name), getattr(outs[1], name)), name
 
 
+@pytest.mark.parametrize("group_chunks", [None, 2])
+def test_flce_graph_replay(group_chunks):
+    """The fused call captured in a HIP graph (torch's stream capture).  Its transposes run on a
+    second stream forked from and joined back to the caller's, so the graph holds both; every
+    replay, with eager work and host syncs in between, gives bitwise the eager result."""
+    hb, wb, y = gen(300, 256, 4096, seed=13)
+    n, H = hb.shape
+    V = wb.shape[0]
+    h, w, lab = bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV)
+    wsb = (lce.lce_flce_workspace_bytes(n, H, V, 64) if group_chunks is None
+           else lce.lce_flce_workspace_bytes_grouped(n, H, V, 64, group_chunks))
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    out = dict(loss_tok=torch.empty(n, dtype=torch.float32, device=DEV),
+               loss_out=torch.empty(1, dtype=torch.float32, device=DEV),
+               grad_hidden=torch.empty((n, H), dtype=torch.bfloat16, device=DEV),
+               grad_weight=torch.empty((V, H), dtype=torch.float32, device=DEV),
+               counts=torch.empty(3, dtype=torch.int64, device=DEV))
+    go = torch.full((1,), 0.5, dtype=torch.float32, device=DEV)
+
+    def call():
+        lce.lce_flce_fwd_bwd(h, w, lab, label_smoothing=0.1, softcap=30.0, grad_out=go, chunk_tokens=64,
+                             workspace=ws, stream=torch.cuda.current_stream(), **out)
+
+    call()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in out.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()   # warm-up on another stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        for v in out.values():
+            v.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            assert torch.equal(v, want[k]), k
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_flce_full_size_sampled():

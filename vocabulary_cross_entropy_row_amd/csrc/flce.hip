@@ -23,6 +23,7 @@
 // logits exists at a time.
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "ce_device.h"
@@ -303,6 +304,42 @@ bool flce_plan(int64_t n, int64_t H, int64_t V, int64_t chunk, size_t bytes, int
     return flce_layout(n, H, V, chunk, group, false).bytes <= bytes;
 }
 
+// A second stream per device for the bandwidth-bound transposes, which then run
+// beside the MFMA-bound GEMMs on the caller's stream: W^T beside the first chunk's
+// logits GEMM, each G_c^T beside its grad_hidden GEMM.  Default priority,
+// non-blocking; events fork it from and join it back to the caller's stream (so a
+// captured call captures both).  One mutex per process orders the enqueueing of
+// calls from several host threads, which share a device's side stream.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, wt = nullptr, gt = nullptr;
+};
+std::mutex g_side_mu;
+
+hipError_t side_stream(SideStream **out) {
+    static SideStream tab[64];
+    int d = 0;
+    hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess) return e;
+    if (d < 0 || d >= 64) return hipErrorInvalidDevice;
+    SideStream &t = tab[d];
+    if (!t.s) {
+        if ((e = hipEventCreateWithFlags(&t.fork, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&t.wt, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&t.gt, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking)) != hipSuccess)
+            return e;
+    }
+    *out = &t;
+    return hipSuccess;
+}
+
+// the side stream starts after everything enqueued on st so far
+hipError_t fork_to(const SideStream &S, hipStream_t st) {
+    hipError_t e = hipEventRecord(S.fork, st);
+    return e != hipSuccess ? e : hipStreamWaitEvent(S.s, S.fork, 0);
+}
+
 hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     hipError_t e;
     const FlceLayout L = flce_layout(f.n, f.H, f.V, f.chunk, f.group_chunks, f.with_wt);
@@ -325,11 +362,19 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
         hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(2048), dim3(256), 0, st, f.grad_weight, tot);
         return hipGetLastError();
     }
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *S = nullptr;
+    if ((e = side_stream(&S)) != hipSuccess) return e;
     uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
-    if (f.with_wt &&
-        (e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), st)) !=
-            hipSuccess)   // W^T [H, V]
-        return e;
+    bool wt_pending = false, gt_pending = false;
+    if (f.with_wt) {   // W^T [H, V], on the side stream
+        if ((e = fork_to(*S, st)) != hipSuccess ||
+            (e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), S->s)) !=
+                hipSuccess ||
+            (e = hipEventRecord(S->wt, S->s)) != hipSuccess)
+            return e;
+        wt_pending = true;
+    }
     const int tiles_dh = static_cast<int>(((C + gemm::BM - 1) / gemm::BM) * ((H + gemm::BN - 1) / gemm::BN));
     const int splits = choose_splits(tiles_dh, V);
 
@@ -344,6 +389,9 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             // H_c^T into columns [c0 - g0, ...) of the group's [H, ldg] buffer
             if ((e = transpose(hc, H, ht + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(H), st)) != hipSuccess)
                 return e;
+            // the previous chunk's G^T transpose still reads z
+            if (gt_pending && (e = hipStreamWaitEvent(st, S->gt, 0)) != hipSuccess) return e;
+            gt_pending = false;
             if (resident) {
                 // G_c straight from the GEMM's epilogue: Z_c stays in registers
                 gemm::CeEpi ce{};
@@ -385,6 +433,14 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
                 a.workspace = ce_ws;
                 if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
             }
+            // G_c^T into columns [c0 - g0, ...) of the group's [V, ldg] buffer, on the side stream
+            if ((e = fork_to(*S, st)) != hipSuccess ||
+                (e = transpose(z, V, gt + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(V), S->s)) != hipSuccess ||
+                (e = hipEventRecord(S->gt, S->s)) != hipSuccess)
+                return e;
+            gt_pending = true;
+            if (wt_pending && (e = hipStreamWaitEvent(st, S->wt, 0)) != hipSuccess) return e;
+            wt_pending = false;
             // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
             // (W^T K-contiguous when the workspace holds it, else W itself, k-major)
             if ((e = f.with_wt ? gemm_nt(gemm::OUT_F32, z, V, wt, V, part, H, cn, static_cast<int>(H),
@@ -400,10 +456,10 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
                                    static_cast<uint16_t *>(f.grad_hidden) + c0 * H, H, cn, static_cast<int>(H));
             }
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            // G_c^T into columns [c0 - g0, ...) of the group's [V, ldg] buffer
-            if ((e = transpose(z, V, gt + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(V), st)) != hipSuccess)
-                return e;
         }
+        // the group's G^T is complete (this also joins the side stream back to st)
+        if (gt_pending && (e = hipStreamWaitEvent(st, S->gt, 0)) != hipSuccess) return e;
+        gt_pending = false;
         // dW (+)= G_g^T H_g over the group's tokens (K padded to a whole 8-element chunk)
         if ((e = gemm_nt(g0 == 0 ? gemm::OUT_F32 : gemm::OUT_F32_ACC, gt, L.ldg, ht, L.ldg, f.grad_weight, H,
                          static_cast<int>(V), static_cast<int>(H), static_cast<int>(round8(gn)), 1, 0, st)) !=
