@@ -464,6 +464,13 @@ def test_full_size_workload(w):
         o = oracle.ce(x, y, V=w.V, label_smoothing=w.label_smoothing, softcap=w.softcap, want_grad=False)
         assert np.array_equal(res.argmax.cpu().numpy(), o["argmax"])
         assert int(res.counts.cpu()[1]) == int(o["counts"][1])
+        # the read-only entry point on the same logits, at the same size
+        buf = to_dev(x)
+        am, counts = lce.lce_ce_argmax(buf, torch.from_numpy(y).to(DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(am.cpu().numpy(), o["argmax"])
+        assert counts.cpu().tolist() == o["counts"].tolist()
+        del buf
     if w.softcap == 0:
         # property at any size: every valid row's gradient sums to ~0 (no cap)
         g = torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).to(DEV).float()
