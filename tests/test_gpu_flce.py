@@ -237,6 +237,44 @@ def test_flce_graph_replay(group_chunks):
             assert torch.equal(v, want[k]), k
 
 
+def test_flce_two_host_threads():
+    """Two host threads call the fused entry point at once, each on its own stream with its own
+    workspace and outputs; both share the device's second stream for the transposes.  Every
+    call gives bitwise the result of the same call made alone."""
+    import threading
+    cases = []
+    for seed in (21, 22):
+        hb, wb, y = gen(200, 256, 2048, seed=seed)
+        h, w, lab = bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV)
+        ws = torch.zeros(lce.lce_flce_workspace_bytes(200, 256, 2048, 64), dtype=torch.uint8, device=DEV)
+        alone = lce.lce_flce_fwd_bwd(h, w, lab, softcap=30.0, chunk_tokens=64, workspace=ws)
+        torch.cuda.synchronize()
+        cases.append((h, w, lab, ws, alone))
+    errors = []
+
+    def worker(k):
+        try:
+            h, w, lab, ws, alone = cases[k]
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(4):
+                    res = lce.lce_flce_fwd_bwd(h, w, lab, softcap=30.0, chunk_tokens=64, workspace=ws, stream=st)
+                    st.synchronize()
+                    for name in ("loss_tok", "loss_out", "grad_hidden", "grad_weight", "counts"):
+                        if not torch.equal(getattr(res, name), getattr(alone, name)):
+                            errors.append(f"thread {k}: {name}")
+        except Exception as exc:  # noqa: BLE001
+            errors.append(f"thread {k}: {exc!r}")
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_flce_full_size_sampled():
