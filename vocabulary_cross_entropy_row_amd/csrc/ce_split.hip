@@ -236,18 +236,26 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int
     float zy = 0.0f;
     bool has = false;
     int64_t am = -1;
+    // the next shard's record is loaded before this one is merged (the last pass
+    // reloads its own record: an unconditional load of a valid address)
+    const float4 *rec = reinterpret_cast<const float4 *>(stats + i * row_stride * 8);
+    const int64_t step = shard_stride * 2;   // float4s per shard
+    float4 a = rec[0], b = rec[1];
     for (int64_t k = 0; k < shards; ++k) {
-        const float *r = stats + (k * shard_stride + i * row_stride) * 8;
-        combine(t, r[0], r[1], r[2]);
-        t.zs += r[3];
-        if (r[4] > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
-            t.amv = r[4];
-            am = __float_as_int(r[5]);
+        const int64_t kn = k + 1 < shards ? k + 1 : k;
+        const float4 na = rec[kn * step], nb = rec[kn * step + 1];
+        combine(t, a.x, a.y, a.z);
+        t.zs += a.w;
+        if (b.x > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
+            t.amv = b.x;
+            am = __float_as_int(b.y);
         }
-        if (r[7] != 0.0f) {
-            zy = r[6];
+        if (b.w != 0.0f) {
+            zy = b.z;
             has = true;
         }
+        a = na;
+        b = nb;
     }
     const int64_t y = labels[i];
     const bool valid = y != ignore_index && y >= 0 && y < V;
