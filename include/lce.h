@@ -2,11 +2,15 @@
  * lce.h -- C ABI of the MI355X (gfx950) vocabulary cross-entropy library.
  *
  * Every entry point takes plain pointers and sizes.  "device" pointers are
- * HIP device memory owned by the caller; the library allocates nothing, keeps
- * no state between calls apart from the thread-local error text, and never
- * synchronises the host: work is enqueued on `stream` and its outputs are
- * valid once that stream has been synchronised.  Calls on different streams
- * are independent as long as their buffers do not overlap.
+ * HIP device memory owned by the caller; the library allocates no memory and
+ * never synchronises the host: work is enqueued on `stream` and its outputs
+ * are valid once that stream has been synchronised.  Calls on different
+ * streams are independent as long as their buffers do not overlap.  State
+ * kept between calls: the thread-local error text, and, for the fused linear
+ * calls, one extra HIP stream (default priority) with three events per device,
+ * created on that device's first call and kept until the process ends.  The
+ * fused calls fork that stream from `stream` and join it back before they
+ * return, so a captured call captures both.
  *
  * Errors: arguments are checked before any HIP call.  A bad argument returns
  * LCE_ERR_INVALID_ARG, a valid but unsupported combination returns

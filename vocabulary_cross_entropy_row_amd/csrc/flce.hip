@@ -316,19 +316,29 @@ struct SideStream {
 };
 std::mutex g_side_mu;
 
-hipError_t side_stream(SideStream **out) {
+// the side stream of the device that `st` belongs to, created there on first use
+hipError_t side_stream(hipStream_t st, SideStream **out) {
     static SideStream tab[64];
-    int d = 0;
-    hipError_t e = hipGetDevice(&d);
+    hipDevice_t d = 0;
+    hipError_t e = hipStreamGetDevice(st, &d);
     if (e != hipSuccess) return e;
     if (d < 0 || d >= 64) return hipErrorInvalidDevice;
     SideStream &t = tab[d];
     if (!t.s) {
-        if ((e = hipEventCreateWithFlags(&t.fork, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&t.wt, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&t.gt, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking)) != hipSuccess)
-            return e;
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != d && (e = hipSetDevice(d)) != hipSuccess) return e;
+        SideStream n;
+        if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) == hipSuccess &&
+            (e = hipEventCreateWithFlags(&n.wt, hipEventDisableTiming)) == hipSuccess &&
+            (e = hipEventCreateWithFlags(&n.gt, hipEventDisableTiming)) == hipSuccess)
+            e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+        if (cur != d) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        t = n;   // published only once complete
     }
     *out = &t;
     return hipSuccess;
@@ -364,7 +374,7 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     }
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream *S = nullptr;
-    if ((e = side_stream(&S)) != hipSuccess) return e;
+    if ((e = side_stream(st, &S)) != hipSuccess) return e;
     uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
     bool wt_pending = false, gt_pending = false;
     if (f.with_wt) {   // W^T [H, V], on the side stream
