@@ -5,12 +5,9 @@
  * HIP device memory owned by the caller; the library allocates no memory and
  * never synchronises the host: work is enqueued on `stream` and its outputs
  * are valid once that stream has been synchronised.  Calls on different
- * streams are independent as long as their buffers do not overlap.  State
- * kept between calls: the thread-local error text, and, for the fused linear
- * calls, one extra HIP stream (default priority) with three events per device,
- * created on that device's first call and kept until the process ends.  The
- * fused calls fork that stream from `stream` and join it back before they
- * return, so a captured call captures both.
+ * streams are independent as long as their buffers do not overlap.  The only
+ * state kept between calls is the thread-local error text; the functions are
+ * re-entrant.
  *
  * Errors: arguments are checked before any HIP call.  A bad argument returns
  * LCE_ERR_INVALID_ARG, a valid but unsupported combination returns
@@ -59,7 +56,11 @@ typedef enum { LCE_RED_NONE = 0, LCE_RED_MEAN = 1, LCE_RED_SUM = 2 } lce_reducti
  * Bytes of device workspace lce_ce_fwd_bwd needs for n rows of V columns
  * (256 + 16 * min(n, 4096); always > 0).  The workspace holds the completion
  * counter of the final reduction, the counters the workgroups draw rows and
- * ignored-row chunks from, and per-workgroup partial counts.
+ * ignored-row chunks from, and per-workgroup partial counts.  Each counter
+ * carries the tag of the launch that set it (its dispatch id), and a launch
+ * that finds another tag starts the counter afresh, so the workspace needs no
+ * initialisation and a call that never completed leaves nothing the next call
+ * would trip over.
  */
 size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
 
@@ -93,11 +94,11 @@ size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
  *                 n_correct = #{valid i : argmax_i == y_i} (0 when argmax_out
  *                 is NULL).  Token accuracy = n_correct / n_valid.
  *   workspace     device scratch of at least lce_ce_workspace_bytes(n, V)
- *                 bytes, 16-byte aligned.  Its first 16 bytes (counters)
- *                 must be zero before the first call (zero-fill it once at
- *                 allocation); every call leaves them zero again.  Calls
- *                 that share a
- *                 workspace must not run concurrently.
+ *                 bytes, 16-byte aligned, required (NULL is
+ *                 LCE_ERR_INVALID_ARG: the rows are handed out dynamically
+ *                 from a counter in it).  Its contents before the call do not
+ *                 matter.  Calls that share a workspace must not run
+ *                 concurrently.
  * loss_tok, argmax_out, counts, workspace and loss_out must not overlap the
  * logits or each other.  n == 0 is valid (counts and loss_out become 0).
  */
@@ -227,14 +228,26 @@ size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t
  *   grad_weight  device fp32 [V, H]: dL/dweight, overwritten (not accumulated
  *                across calls), accumulated in fp32 over the chunks [P5 Memory].
  *   counts       device int64 [3] {n_valid, 0, n_bad}.
- *   workspace    device, 256-byte aligned, clobbered; at least
+ *   workspace    device, 256-byte aligned, clobbered (its prior contents do
+ *                not matter); at least
  *                lce_flce_workspace_bytes_grouped(n, H, V, chunk_tokens, 1)
  *                bytes (LCE_ERR_INVALID_ARG otherwise).  The call uses the
  *                largest grad_weight group, up to the default one, whose
  *                layout fits workspace_bytes without W^T, and adds the W^T
  *                copy when the rest of the workspace holds it too; without
  *                it the grad_hidden GEMM reads W in place (about 15% slower
- *                for that GEMM, 2 H V bytes less workspace).
+ *                for that GEMM, 2 H V bytes less workspace), which needs
+ *                V * H * 2 < 4 GiB (LCE_ERR_UNSUPPORTED otherwise).
+ *   stream       the stream the call is ordered on.
+ *   aux_stream   NULL, or a second stream of the same device (default
+ *                priority) that the bandwidth-bound transposes may run on
+ *                beside the GEMMs.  The call forks it from `stream` and joins
+ *                it back before returning, with three events it creates and
+ *                destroys itself, so nothing it enqueues there outlives the
+ *                call's work on `stream` and a captured call captures both.
+ *                NULL, or a stream being captured into another graph than
+ *                `stream`, runs everything on `stream`.  Calls sharing an
+ *                aux_stream are ordered on it but stay correct.
  * Logits are formed in fp32 by bf16 MFMA and stored as bf16 for the row
  * kernel.  H and V must be multiples of 8 (LCE_ERR_UNSUPPORTED otherwise).
  */
@@ -242,7 +255,7 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
                             int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
                             lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, float *loss_tok,
                             float *loss_out, void *grad_hidden, float *grad_weight, int64_t *counts,
-                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+                            void *workspace, size_t workspace_bytes, hipStream_t stream, hipStream_t aux_stream);
 
 /*
  * Tile-resident fused linear cross-entropy [P5 Summary; Details/Softcap;
@@ -286,14 +299,15 @@ lce_status lce_flce_forward(const void *hidden, const void *weight, const int64_
  * from lse, one_minus_py and counts of lce_flce_forward on the same inputs and
  * options, with the upstream gradient grad_out (as for lce_ce_fwd_bwd).  Tokens
  * go in chunks of chunk_tokens; the workspace is that of lce_flce_fwd_bwd
- * (lce_flce_workspace_bytes[_grouped], the same group rule).  Nothing of the
+ * (lce_flce_workspace_bytes[_grouped], the same group rule and the same 4 GiB
+ * limit without W^T) and aux_stream as for lce_flce_fwd_bwd.  Nothing of the
  * forward's outputs is modified.
  */
 lce_status lce_flce_backward(const void *hidden, const void *weight, const int64_t *labels, int64_t n, int64_t H,
                              int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
                              lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, const float *lse,
                              const float *one_minus_py, const int64_t *counts, void *grad_hidden, float *grad_weight,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+                             void *workspace, size_t workspace_bytes, hipStream_t stream, hipStream_t aux_stream);
 
 /*
  * Text of the most recent error on the calling thread ("" if none).  Valid

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_workspace():
-    assert lce.lib().lce_abi_version() == lce.ABI_VERSION == 2
+    assert lce.lib().lce_abi_version() == lce.ABI_VERSION == 3
     assert lce.lce_ce_workspace_bytes(2048, 131072) > 0
 
 
@@ -107,13 +107,13 @@ def call_flce(**over):
     wsb_default = lce.lce_flce_workspace_bytes(64, 64, 512, 32)
     args = dict(hidden=FAKE, weight=FAKE, labels=FAKE, n=64, H=64, V=512, ignore_index=-100, eps=0.0, softcap=0.0,
                 red=lce.LCE_RED_MEAN, grad_out=None, chunk=32, loss_tok=FAKE, loss_out=None, grad_hidden=FAKE,
-                grad_weight=FAKE, counts=FAKE, ws=ALIGNED_WS, wsb=wsb_default, stream=None)
+                grad_weight=FAKE, counts=FAKE, ws=ALIGNED_WS, wsb=wsb_default, stream=None, aux=None)
     args.update(over)
     a = args
     st = lce.lib().lce_flce_fwd_bwd(a["hidden"], a["weight"], a["labels"], a["n"], a["H"], a["V"], a["ignore_index"],
                                     a["eps"], a["softcap"], a["red"], a["grad_out"], a["chunk"], a["loss_tok"],
                                     a["loss_out"], a["grad_hidden"], a["grad_weight"], a["counts"], a["ws"], a["wsb"],
-                                    a["stream"])
+                                    a["stream"], a["aux"])
     return st, lce.lce_last_error()
 
 
@@ -138,6 +138,31 @@ def test_flce_rejects_bad_arguments(over, needle, status):
     st, msg = call_flce(**over)
     assert st == status, msg
     assert needle in msg
+    # with a second stream named, the same rejection comes before any HIP call touches it
+    st2, msg2 = call_flce(aux=FAKE + 0x100, **over)
+    assert (st2, msg2) == (st, msg)
+
+
+@pytest.mark.parametrize("fn", ["fwd_bwd", "backward"])
+def test_flce_weight_in_place_limit(fn):
+    """Without room for W^T the grad_hidden GEMM reads the weight in place, which needs
+    V * H * 2 < 4 GiB: a one-chunk-group workspace at V = 202048, H = 16384 is refused up front
+    (the default workspace, which holds W^T, is not limited by it)."""
+    n, H, V, C = 2048, 16384, 202048, 1024
+    one = lce.lce_flce_workspace_bytes_grouped(n, H, V, C, 1)
+    if fn == "fwd_bwd":
+        st, msg = call_flce(n=n, H=H, V=V, chunk=C, wsb=one, aux=FAKE + 0x100)
+    else:
+        st, msg = call_flce_backward(n=n, H=H, V=V, chunk=C, wsb=one, aux=FAKE + 0x100)
+    assert st == lce.LCE_ERR_UNSUPPORTED and "4 GiB" in msg and "W^T" in msg, msg
+
+
+def test_header_documents_the_second_stream():
+    src = open(HEADER).read()
+    for fn in ("lce_flce_fwd_bwd", "lce_flce_backward"):
+        decl = re.search(fn + r"\(([^;]*)\);", src).group(1)
+        assert decl.rstrip().endswith("hipStream_t stream, hipStream_t aux_stream"), fn
+    assert "The only\n * state kept between calls is the thread-local error text" in src
 
 
 def test_flce_workspace_groups():
@@ -222,11 +247,12 @@ def call_flce_forward(**over):
 def call_flce_backward(**over):
     a = dict(hidden=FAKE, weight=FAKE, labels=FAKE, n=4, H=8, V=16, ignore_index=-100, eps=0.0, softcap=0.0,
              red=lce.LCE_RED_MEAN, grad_out=None, chunk=4, lse=FAKE, q=FAKE, counts=FAKE, gh=FAKE, gw=FAKE,
-             ws=ALIGNED_WS, wsb=1 << 30, stream=None)
+             ws=ALIGNED_WS, wsb=1 << 30, stream=None, aux=None)
     a.update(over)
     st = lce.lib().lce_flce_backward(a["hidden"], a["weight"], a["labels"], a["n"], a["H"], a["V"],
                                      a["ignore_index"], a["eps"], a["softcap"], a["red"], a["grad_out"], a["chunk"],
-                                     a["lse"], a["q"], a["counts"], a["gh"], a["gw"], a["ws"], a["wsb"], a["stream"])
+                                     a["lse"], a["q"], a["counts"], a["gh"], a["gw"], a["ws"], a["wsb"], a["stream"],
+                                     a["aux"])
     return st, lce.lce_last_error()
 
 

@@ -1,11 +1,16 @@
 """GPU parity of the fused linear cross-entropy (lce_flce_fwd_bwd) against the fp64 oracle.
 
-The kernel forms the logits in fp32 with bf16 MFMA and stores them as bf16 for the row
-kernel, so the per-token loss differs from the exact-logit oracle by at most
-sum_j |p_j - t_j| * |dz_j| <= 2 * 2^-9 * max_j |z_ij| (RNE half-ulp 2^-9 relative on each
-logit); that bound (+ the fp32 loss tolerance) is the per-token tolerance and its mean
-bounds the reduced loss.  Gradients: relative L2 <= 1e-2 (grad_hidden, grad_weight).
-Counts: exact.
+The call forms the logits in fp32 with bf16 MFMA and stores them as bf16 for the row kernel, so
+its losses are those of the bf16-rounded logits.  The reference for them is the oracle's row
+routine on RNE_bf16 of the exact logits (two oracle functions, composed here): per-token and
+reduced loss within 1e-4 max(1, |loss|).  Both sides round the same exact value, except where the
+fp32 accumulation error carries a logit across a bf16 rounding boundary (for the target logit,
+about one token in 10^4); such a token's loss may move by one bf16 step of its target logit, so
+at most one token in 200 (at least one) may instead meet the worst-case bound of bf16 logits
+against the exact-logit oracle, 2 2^-9 max_j |z_ij| + 1e-4 max(1, |loss|).  At full size the
+reduced loss is also held to 1e-4 max(1, |loss|) of the exact-logit oracle (the bf16 rounding of
+single logits averages out over ~3.9K tokens).  Gradients: relative L2 <= 1e-2 (grad_hidden,
+grad_weight).  Counts: exact.
 """
 from __future__ import annotations
 
@@ -53,21 +58,42 @@ def run_flce(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64, 
     return res
 
 
+def bf16_logit_reference(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None):
+    """The oracle's losses of the bf16-rounded exact logits, and each token's worst-case bound of
+    bf16 logits against the exact-logit losses (2 2^-9 max_j |z_ij|)."""
+    orc = oracle.default()
+    V = wb.shape[0]
+    Z = bits_to_f64(hb) @ bits_to_f64(wb).T          # exact: bf16 products, fp64 sums
+    ob = orc.ce(orc.round_bf16(Z), y, V=V, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out,
+                want_grad=False)
+    zc = T * np.tanh(Z / T) if T > 0 else Z
+    return ob, 2.0 * 2.0 ** -9 * np.abs(zc).max(axis=1)
+
+
+def check_loss_tok(lt, ob_loss, exact_loss, worst):
+    """Per-token loss within 1e-4 max(1, |loss|) of the bf16-logit reference; at most one token in
+    200 (at least one) may instead be within the worst-case bf16 bound of the exact-logit loss."""
+    lt = np.asarray(lt, dtype=np.float64)
+    err = np.abs(lt - ob_loss)
+    off = err > 1e-4 * np.maximum(1.0, np.abs(ob_loss))
+    assert np.count_nonzero(off) <= max(1, lt.size // 200), \
+        f"{np.count_nonzero(off)} tokens beyond 1e-4 max(1, |loss|), first {np.flatnonzero(off)[:5]}: {err[off][:5]}"
+    far = off & (np.abs(lt - exact_loss) > worst + 1e-4 * np.maximum(1.0, np.abs(exact_loss)))
+    assert not far.any(), f"loss_tok beyond the bf16-logit bound at {np.flatnonzero(far)[:5]}"
+    return float(err.max()) if err.size else 0.0, int(np.count_nonzero(off))
+
+
 def check_flce(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64, group_chunks=None):
     res = run_flce(hb, wb, y, eps=eps, T=T, red=red, grad_out=grad_out, chunk=chunk, group_chunks=group_chunks)
     o = oracle.flce(hb, wb, y, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out)
-    n = y.size
     assert res.counts.cpu().tolist() == [int(o["counts"][0]), 0, int(o["counts"][2])]
-    Z = bits_to_f64(hb) @ bits_to_f64(wb).T
-    zc = T * np.tanh(Z / T) if T > 0 else Z
-    bound = 2.0 * 2.0 ** -9 * np.abs(zc).max(axis=1) + 1e-4 * np.maximum(1.0, np.abs(o["loss_tok"]))
-    lt = res.loss_tok.cpu().numpy().astype(np.float64)
-    bad = np.abs(lt - o["loss_tok"]) > bound
-    assert not bad.any(), f"loss_tok beyond the bf16-logit bound at {np.flatnonzero(bad)[:5]}"
+    ob, worst = bf16_logit_reference(hb, wb, y, eps=eps, T=T, red=red, grad_out=grad_out)
+    e_max, n_off = check_loss_tok(res.loss_tok.cpu().numpy(), ob["loss_tok"], o["loss_tok"], worst)
     if red != "none":
-        valid = (y != -100) & (y >= 0) & (y < wb.shape[0])
-        lo_bound = bound[valid].mean() if red == "mean" and valid.any() else bound[valid].sum()
-        assert abs(float(res.loss_out.cpu()[0]) - o["loss_out"]) <= lo_bound + 1e-6
+        got = float(res.loss_out.cpu()[0])
+        assert abs(got - ob["loss_out"]) <= 1e-4 * max(1.0, abs(ob["loss_out"])), \
+            f"loss_out {got!r} vs {ob['loss_out']!r}"
+    print(f"  loss_tok max err {e_max:.2e} ({n_off} tokens on the worst-case bound)")
     dh = res.grad_hidden.view(torch.int16).cpu().numpy().view(np.uint16)
     e_h = rel_l2(bits_to_f64(dh), o["grad_hidden"])
     e_w = rel_l2(res.grad_weight.cpu().numpy().astype(np.float64), o["grad_weight"])
@@ -239,8 +265,8 @@ def test_flce_graph_replay(group_chunks):
 
 def test_flce_two_host_threads():
     """Two host threads call the fused entry point at once, each on its own stream with its own
-    workspace and outputs; both share the device's second stream for the transposes.  Every
-    call gives bitwise the result of the same call made alone."""
+    workspace and outputs (and the binding's second stream of its own thread).  Every call gives
+    bitwise the result of the same call made alone."""
     import threading
     cases = []
     for seed in (21, 22):
@@ -275,13 +301,121 @@ def test_flce_two_host_threads():
     assert not errors, errors
 
 
+def test_flce_second_stream_choices():
+    """The transposes on this thread's second stream (the default), on a stream the caller names,
+    or on the caller's stream alone, and the call on a stream other than the current one (which is
+    kept busy meanwhile): bitwise the same results."""
+    hb, wb, y = gen(300, 256, 4096, seed=17)
+    h, w, lab = bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV)
+    names = ("loss_tok", "loss_out", "grad_hidden", "grad_weight", "counts")
+    ref = lce.lce_flce_fwd_bwd(h, w, lab, label_smoothing=0.1, softcap=30.0, chunk_tokens=64)
+    torch.cuda.synchronize()
+    mine = torch.cuda.Stream()
+    for aux in (None, mine):
+        res = lce.lce_flce_fwd_bwd(h, w, lab, label_smoothing=0.1, softcap=30.0, chunk_tokens=64, aux_stream=aux)
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(getattr(res, k), getattr(ref, k)), (aux, k)
+    big = torch.randn(4096, 4096, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for _ in range(8):
+        big = big @ big.T / 64.0
+    res = lce.lce_flce_fwd_bwd(h, w, lab, label_smoothing=0.1, softcap=30.0, grad_out=1.0, chunk_tokens=64, stream=s)
+    s.synchronize()
+    for k in names:
+        assert torch.equal(getattr(res, k), getattr(ref, k)), ("other stream", k)
+    torch.cuda.synchronize()
+
+
+def test_flce_capture_beside_an_eager_call():
+    """One thread captures the fused call into a graph with a second stream it names; before the
+    capture ends, another thread makes an eager call naming the same second stream.  That stream
+    is then being captured into the first thread's graph, so the eager call runs on its own
+    stream alone and stays out of the graph.  The eager result and every replay of the graph are
+    bitwise the results of the call made alone."""
+    import threading
+    hb, wb, y = gen(200, 256, 2048, seed=23)
+    n, H = hb.shape
+    V = wb.shape[0]
+    h, w, lab = bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV)
+    names = ("loss_tok", "loss_out", "grad_hidden", "grad_weight", "counts")
+
+    def outputs():
+        return dict(loss_tok=torch.empty(n, dtype=torch.float32, device=DEV),
+                    loss_out=torch.empty(1, dtype=torch.float32, device=DEV),
+                    grad_hidden=torch.empty((n, H), dtype=torch.bfloat16, device=DEV),
+                    grad_weight=torch.empty((V, H), dtype=torch.float32, device=DEV),
+                    counts=torch.empty(3, dtype=torch.int64, device=DEV))
+
+    alone = lce.lce_flce_fwd_bwd(h, w, lab, softcap=30.0, chunk_tokens=64, aux_stream=None)
+    torch.cuda.synchronize()
+    shared_aux = torch.cuda.Stream()
+    cap_out, eager_out = outputs(), outputs()
+    cap_ws = torch.empty(lce.lce_flce_workspace_bytes(n, H, V, 64), dtype=torch.uint8, device=DEV)
+    eager_ws = torch.empty_like(cap_ws)
+    cap_stream, eager_stream = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    inside, eager_done = threading.Event(), threading.Event()
+    errors = []
+    graph = torch.cuda.CUDAGraph()
+
+    def capturer():
+        try:
+            with torch.cuda.stream(cap_stream):
+                lce.lce_flce_fwd_bwd(h, w, lab, softcap=30.0, chunk_tokens=64, workspace=cap_ws,
+                                     aux_stream=shared_aux, **cap_out)   # warm-up
+            cap_stream.synchronize()
+            with torch.cuda.graph(graph, stream=cap_stream, capture_error_mode="thread_local"):
+                lce.lce_flce_fwd_bwd(h, w, lab, softcap=30.0, chunk_tokens=64, workspace=cap_ws,
+                                     aux_stream=shared_aux, **cap_out)
+                inside.set()
+                if not eager_done.wait(120):
+                    errors.append("the eager call did not finish")
+        except Exception as exc:  # noqa: BLE001
+            errors.append(f"capture: {exc!r}")
+            inside.set()
+
+    def eager():
+        try:
+            if not inside.wait(120):
+                errors.append("the capture did not start")
+                return
+            lce.lce_flce_fwd_bwd(h, w, lab, softcap=30.0, chunk_tokens=64, workspace=eager_ws,
+                                 aux_stream=shared_aux, stream=eager_stream, **eager_out)
+            eager_stream.synchronize()
+        except Exception as exc:  # noqa: BLE001
+            errors.append(f"eager: {exc!r}")
+        finally:
+            eager_done.set()
+
+    threads = [threading.Thread(target=capturer), threading.Thread(target=eager)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=180)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+    for k in names:
+        assert torch.equal(eager_out[k], getattr(alone, k)), ("eager", k)
+    for _ in range(2):
+        for v in cap_out.values():
+            v.fill_(7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(cap_out[k], getattr(alone, k)), ("replay", k)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_flce_full_size_sampled():
     """The fused-linear workload at full size (hidden 4096 x 6656, weight 202048 x 6656, T = 30) in the
-    bench's launch configuration (chunks of 1024, default workspace): exact counts, every token's loss
-    within the bf16-logit bound, the mean loss, and sampled grad_hidden rows and grad_weight rows (the
-    sampled tokens' labels included) within 1e-2 relative L2, against the fp64 oracle."""
+    bench's launch configuration (chunks of 1024, default workspace): exact counts, the mean loss within
+    1e-4 max(1, |loss|) of the exact-logit oracle, 48 sampled tokens' losses against the oracle on
+    their bf16-rounded logits, and sampled grad_hidden rows and grad_weight rows (the sampled tokens'
+    labels included) within 1e-2 relative L2, against the fp64 oracle."""
     w = synth.C5
     y = synth.labels(w)
     hb = synth.flce_hidden_rows(w, np.arange(w.n))
@@ -295,12 +429,15 @@ def test_flce_full_size_sampled():
     o = oracle.flce_sampled(oracle.default(), hb, wb, y, tok, voc, softcap=w.softcap)
     print("  oracle done", flush=True)
     assert res.counts.cpu().tolist() == [int(o["counts"][0]), 0, int(o["counts"][2])]
-    bound = 2.0 * 2.0 ** -9 * o["zmax"] + 1e-4 * np.maximum(1.0, np.abs(o["loss_tok"]))
-    lt = res.loss_tok.cpu().numpy().astype(np.float64)
-    bad = np.abs(lt - o["loss_tok"]) > bound
-    assert not bad.any(), f"loss_tok beyond the bf16-logit bound at {np.flatnonzero(bad)[:5]}"
-    valid = (y != -100)
-    assert abs(float(res.loss_out.cpu()[0]) - o["loss_out"]) <= bound[valid].mean() + 1e-6
+    # the reduced loss against the exact logits: the bf16 rounding of single logits averages out
+    got = float(res.loss_out.cpu()[0])
+    assert abs(got - o["loss_out"]) <= 1e-4 * max(1.0, abs(o["loss_out"])), f"loss_out {got!r} vs {o['loss_out']!r}"
+    # sampled tokens' losses against the oracle on their bf16-rounded logits
+    sel = np.sort(rng.choice(w.n, 48, replace=False))
+    ob, worst = bf16_logit_reference(hb[sel], wb, y[sel], T=w.softcap, red="sum")
+    e_max, n_off = check_loss_tok(res.loss_tok.cpu().numpy()[sel], ob["loss_tok"], o["loss_tok"][sel], worst)
+    print(f"  loss_out err {abs(got - o['loss_out']):.2e}, sampled loss_tok max err {e_max:.2e} "
+          f"({n_off} on the worst-case bound)", flush=True)
     dh = res.grad_hidden[torch.from_numpy(tok).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
     e_h = rel_l2(bits_to_f64(dh), o["grad_hidden"])
     e_w = rel_l2(res.grad_weight[torch.from_numpy(voc).to(DEV)].cpu().numpy().astype(np.float64), o["grad_weight"])

@@ -1,13 +1,16 @@
 """GPU parity of the tile-resident fused linear cross-entropy (lce_flce_forward / lce_flce_backward)
 against the fp64 oracle, through the C ABI.
 
-The logits are fp32 sums of exact bf16 products, never rounded to bf16, so each logit differs from the
-exact one by at most delta_i = H * 2^-24 * max_j sum_k |h_ik w_jk| (the summation bound for H terms in
-any order).  The per-token loss, log-sum-exp and log p_y therefore lie within 2 delta_i (+ the fp32 loss
-tolerance) of the oracle's; entropy within 4 delta_i (+ the same).  The argmax, a decision taken on these
-logits, must equal the oracle's where the oracle's top-2 gap exceeds 2 delta_i, and elsewhere be a
-column whose exact logit is within 2 delta_i of the maximum; n_correct must count the kernel's own
-argmax.  Gradients: relative L2 <= 1e-2, as for the chunked call.
+The logits are fp32 sums of exact bf16 products, never rounded to bf16.  Their accumulation error is
+far below the loss tolerance at the workloads' magnitudes, so the per-token loss, log-sum-exp,
+log p_y and entropy, and the reduced loss, are held to 1e-4 max(1, |value|) of the oracle on the
+exact logits.  The argmax is a decision taken on these logits: each logit differs from the exact one
+by at most delta_i = H 2^-24 max_j sum_k |h_ik w_jk| (the summation bound for H terms in any order),
+so the argmax must equal the oracle's where the oracle's top-2 gap exceeds 2 delta_i, and elsewhere
+be a column whose exact logit is within 2 delta_i of the maximum; n_correct must count the kernel's
+own argmax.  One stress test (logits of magnitude ~1e3 to 3e4, where the fp32 accumulation error
+itself exceeds 1e-4 of a near-zero loss) is held to that summation bound instead: 2 delta_i for
+loss, LSE and log p_y, 4 delta_i for entropy.  Gradients: relative L2 <= 1e-2.
 """
 from __future__ import annotations
 
@@ -67,26 +70,25 @@ def run_resident(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=
     return rows, gh, gw
 
 
-def check_rows(rows, hb, wb, y, *, eps=0.0, T=0.0, red="mean"):
-    """Forward outputs against the oracle; returns the per-token logit bound."""
+def check_rows(rows, hb, wb, y, *, eps=0.0, T=0.0, red="mean", summation_bound=False):
+    """Forward outputs against the oracle; returns the per-token logit bound delta_i.  With
+    summation_bound the real-valued outputs are held to multiples of delta_i instead of
+    1e-4 max(1, |value|) (the large-magnitude stress test)."""
     orc = oracle.default()
     V = wb.shape[0]
     ro = oracle.flce_rows(orc, hb, wb, y, softcap=T)
-    o = orc.flce(hb, wb, y, label_smoothing=eps, softcap=T, reduction=red, grad_out=None) if hb.shape[0] <= 600 \
-        else None
+    o = orc.flce(hb, wb, y, label_smoothing=eps, softcap=T, reduction=red, grad_out=None)
     d = logit_bound(hb, wb)
     tol = lambda ref: 1e-4 * np.maximum(1.0, np.abs(ref))  # noqa: E731
-    lse = rows.lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(lse - ro["lse"]) <= 2 * d + tol(ro["lse"])), "lse beyond its bound"
-    logp = rows.logprob.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(logp - ro["logp"]) <= 2 * d + tol(ro["lse"])), "log p_y beyond its bound"
-    ent = rows.entropy.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(ent - ro["entropy"]) <= 4 * d + tol(ro["lse"])), "entropy beyond its bound"
-    lt = rows.loss_tok.cpu().numpy().astype(np.float64)
-    want = o["loss_tok"] if o is not None else ro["loss_tok"]
-    if o is not None or eps == 0.0:
-        assert np.all(np.abs(lt - want) <= 2 * d + tol(want)), \
-            f"loss_tok beyond its bound at {np.flatnonzero(np.abs(lt - want) > 2 * d + tol(want))[:5]}"
+    errs = {}
+    for name, got_t, ref, mult in (("lse", rows.lse, ro["lse"], 2), ("log p_y", rows.logprob, ro["logp"], 2),
+                                   ("entropy", rows.entropy, ro["entropy"], 4),
+                                   ("loss_tok", rows.loss_tok, o["loss_tok"], 2)):
+        got = got_t.cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        lim = mult * d + tol(ro["lse"]) if summation_bound else tol(ref)
+        assert np.all(err <= lim), f"{name} beyond its tolerance at {np.flatnonzero(err > lim)[:5]}: {err[err > lim][:5]}"
+        errs[name] = float(err.max()) if err.size else 0.0
     am = rows.argmax.cpu().numpy()
     firm = ro["gap"] > 2 * d
     assert np.array_equal(am[firm], ro["argmax"][firm]), "argmax differs where the top-2 gap is clear"
@@ -98,16 +100,21 @@ def check_rows(rows, hb, wb, y, *, eps=0.0, T=0.0, red="mean"):
     nv, nb = orc.count(y, V)
     assert counts[0] == nv and counts[2] == nb
     assert counts[1] == int(np.sum(valid & (am == y))), "n_correct does not count the argmax"
-    if o is not None and red != "none":
-        lo_bound = (2 * d + tol(o["loss_tok"]))[valid]
-        lo_bound = lo_bound.mean() if red == "mean" and valid.any() else lo_bound.sum()
-        assert abs(float(rows.loss_out.cpu()[0]) - o["loss_out"]) <= lo_bound + 1e-6
+    if red != "none":
+        got = float(rows.loss_out.cpu()[0])
+        if summation_bound:
+            lim = (2 * d + tol(o["loss_tok"]))[valid]
+            lim = lim.mean() if red == "mean" and valid.any() else lim.sum()
+        else:
+            lim = 1e-4 * max(1.0, abs(o["loss_out"]))
+        assert abs(got - o["loss_out"]) <= lim, f"loss_out {got!r} vs {o['loss_out']!r}"
+    print("  max errors: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     return d
 
 
-def check_resident(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64):
+def check_resident(hb, wb, y, *, eps=0.0, T=0.0, red="mean", grad_out=None, chunk=64, summation_bound=False):
     rows, gh, gw = run_resident(hb, wb, y, eps=eps, T=T, red=red, grad_out=grad_out, chunk=chunk)
-    check_rows(rows, hb, wb, y, eps=eps, T=T, red=red)
+    check_rows(rows, hb, wb, y, eps=eps, T=T, red=red, summation_bound=summation_bound)
     o = oracle.flce(hb, wb, y, label_smoothing=eps, softcap=T, reduction=red, grad_out=grad_out)
     e_h = rel_l2(bits_to_f64(gh.view(torch.int16).cpu().numpy().view(np.uint16)), o["grad_hidden"])
     e_w = rel_l2(gw.cpu().numpy().astype(np.float64), o["grad_weight"])
@@ -159,7 +166,7 @@ def test_resident_large_magnitudes(eps, red):
         if y[i] < 0:
             y[i] = 5 + i
         hb[i] = synth.f32_to_bf16_bits((w64[y[i]] * (3.0e4 / float(w64[y[i]] @ w64[y[i]]))).astype(np.float32))
-    check_resident(hb, wb, y, eps=eps, red=red, grad_out=[0.5], chunk=64)
+    check_resident(hb, wb, y, eps=eps, red=red, grad_out=[0.5], chunk=64, summation_bound=True)
 
 
 def test_resident_argmax_ties_and_accuracy():
@@ -253,10 +260,11 @@ def test_linear_cross_entropy_autograd(red):
 @pytest.mark.timeout(900)
 def test_resident_full_size_sampled():
     """The fused-linear workload at full size (hidden 4096 x 6656, weight 202048 x 6656, T = 30) in the
-    bench's launch configuration (backward in chunks of 1024, default workspace).  Sampled tokens
-    against the fp64 oracle one by one: loss, lse, log p_y, entropy, argmax (gap-aware) and
-    grad_hidden rows; over every token: counts and n_correct from the kernel's own argmax.  grad_weight
-    rows against the chunked call (checked against the oracle at this size by its own test)."""
+    bench's launch configuration (backward in chunks of 1024, default workspace), against the fp64
+    oracle: every token's loss and the mean loss within 1e-4 max(1, |loss|); on sampled tokens, one
+    by one, lse, log p_y and entropy within 1e-4 max(1, |value|), argmax (gap-aware) and grad_hidden
+    rows; sampled grad_weight rows (the sampled tokens' labels included); over every token, counts
+    and n_correct from the kernel's own argmax."""
     w = synth.C5
     y = synth.labels(w)
     hb = synth.flce_hidden_rows(w, np.arange(w.n))
@@ -268,14 +276,19 @@ def test_resident_full_size_sampled():
     rng = np.random.default_rng(98)
     tok = np.unique(np.concatenate([rng.choice(w.n, 30, replace=False), np.flatnonzero(y == -100)[:2],
                                     [0, w.n - 1]]))
-    ro = oracle.flce_rows(orc, hb, wb, y, tokens=tok, softcap=w.softcap, grad_scale=1.0 / nv, block=64)
+    voc = np.unique(np.concatenate([rng.choice(w.V, 64, replace=False), y[tok][y[tok] >= 0]]))
+    ro = oracle.flce_rows(orc, hb, wb, y, tokens=tok, softcap=w.softcap, block=64)
+    o = oracle.flce_sampled(orc, hb, wb, y, tok, voc, softcap=w.softcap)
     print("  oracle done", flush=True)
+    lt = rows.loss_tok.cpu().numpy().astype(np.float64)
+    err = np.abs(lt - o["loss_tok"])
+    assert np.all(err <= 1e-4 * np.maximum(1.0, np.abs(o["loss_tok"]))), f"loss_tok beyond 1e-4: {err.max():.3e}"
+    got = float(rows.loss_out.cpu()[0])
+    assert abs(got - o["loss_out"]) <= 1e-4 * max(1.0, abs(o["loss_out"])), f"loss_out {got!r} vs {o['loss_out']!r}"
+    for name, k in (("lse", "lse"), ("logprob", "logp"), ("entropy", "entropy")):
+        g = getattr(rows, name).cpu().numpy()[tok].astype(np.float64)
+        assert np.all(np.abs(g - ro[k]) <= 1e-4 * np.maximum(1.0, np.abs(ro[k]))), f"{name} beyond 1e-4"
     d = w.H * 2.0 ** -24 * (np.abs(bits_to_f64(hb[tok])) @ np.abs(bits_to_f64(wb)).T).max(axis=1)
-    tol = 1e-4 * np.maximum(1.0, np.abs(ro["lse"]))
-    for name, k, mult in (("loss_tok", "loss_tok", 2), ("lse", "lse", 2), ("logprob", "logp", 2),
-                          ("entropy", "entropy", 4)):
-        got = getattr(rows, name).cpu().numpy()[tok].astype(np.float64)
-        assert np.all(np.abs(got - ro[k]) <= mult * d + tol), f"{name} beyond its bound"
     am = rows.argmax.cpu().numpy()
     firm = ro["gap"] > 2 * d
     assert np.array_equal(am[tok][firm], ro["argmax"][firm])
@@ -283,11 +296,8 @@ def test_resident_full_size_sampled():
     valid = (y != -100) & (y >= 0) & (y < w.V)
     assert counts[0] == nv and counts[2] == nb and counts[1] == int(np.sum(valid & (am == y)))
     e_h = rel_l2(bits_to_f64(gh[torch.from_numpy(tok).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)),
-                 ro["grad_hidden"])
-    res = lce.lce_flce_fwd_bwd(bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV), softcap=w.softcap,
-                               chunk_tokens=w.chunk)
-    torch.cuda.synchronize()
-    voc = torch.from_numpy(np.unique(np.concatenate([rng.choice(w.V, 64, replace=False), y[tok][y[tok] >= 0]]))).to(DEV)
-    e_w = rel_l2(gw[voc].cpu().numpy().astype(np.float64), res.grad_weight[voc].cpu().numpy().astype(np.float64))
-    print(f"  rel L2 dH {e_h:.2e} (oracle)  dW {e_w:.2e} (chunked call)", flush=True)
+                 o["grad_hidden"])
+    e_w = rel_l2(gw[torch.from_numpy(voc).to(DEV)].cpu().numpy().astype(np.float64), o["grad_weight"])
+    print(f"  loss_tok max err {err.max():.2e}, loss_out err {abs(got - o['loss_out']):.2e}, "
+          f"rel L2 dH {e_h:.2e} dW {e_w:.2e} (oracle)", flush=True)
     assert e_h <= REL_L2 and e_w <= REL_L2

@@ -2,7 +2,9 @@
 
 The functions carry the names of the C entry points in include/lce.h and only
 marshal arguments: every step of the computation runs in the HIP kernels of
-liblce.so.  PyTorch supplies device memory and the current HIP stream.  There
+liblce.so.  PyTorch supplies device memory and streams: every function runs
+on ``stream`` (default: the current stream) and allocates its temporaries and
+default outputs with that stream current.  There
 is no CPU fallback: if the library is missing this module raises on import of
 the function table (``lib()``), and every call goes to the GPU.
 """
@@ -19,7 +21,7 @@ LCE_OK, LCE_ERR_INVALID_ARG, LCE_ERR_UNSUPPORTED, LCE_ERR_HIP = 0, 1, 2, 3
 LCE_F32, LCE_BF16 = 0, 1
 LCE_RED_NONE, LCE_RED_MEAN, LCE_RED_SUM = 0, 1, 2
 REDUCTIONS = {"none": LCE_RED_NONE, "mean": LCE_RED_MEAN, "sum": LCE_RED_SUM}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
     L.lce_flce_workspace_bytes_grouped.argtypes = [i64, i64, i64, i64, i64]
     L.lce_flce_fwd_bwd.restype = ctypes.c_int
     L.lce_flce_fwd_bwd.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, i64, p, p, p, p, p, p,
-                                   ctypes.c_size_t, p]
+                                   ctypes.c_size_t, p, p]
     L.lce_flce_stats_bytes.restype = ctypes.c_size_t
     L.lce_flce_stats_bytes.argtypes = [i64, i64]
     L.lce_flce_forward.restype = ctypes.c_int
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_size_t, p]
     L.lce_flce_backward.restype = ctypes.c_int
     L.lce_flce_backward.argtypes = [p, p, p, i64, i64, i64, i64, f32, f32, ctypes.c_int, p, i64, p, p, p, p, p, p,
-                                    ctypes.c_size_t, p]
+                                    ctypes.c_size_t, p, p]
     if L.lce_abi_version() != ABI_VERSION:
         raise ImportError("liblce.so ABI version mismatch; rebuild it")
     _lib = L
@@ -100,11 +102,63 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int | None:
+def _torch_stream(stream, device):
+    """The stream a call runs on, as a torch stream: ``stream`` (a torch stream or a raw HIP stream
+    handle) or the current stream of ``device``.  Each function allocates its temporaries and
+    default outputs with this stream current, so they are ordered before the launch and go back to
+    the caching allocator against the stream that uses them."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _on_call_stream(fn):
+    """Runs a binding function with its call stream current (see _torch_stream): the function
+    receives that stream as ``stream``."""
+    import functools
+
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        import torch
+        first = args[0] if args else None
+        if not (torch.is_tensor(first) and first.device.type == "cuda"):
+            return fn(*args, stream=stream, **kw)   # the function's own checks raise
+        st = _torch_stream(stream, first.device)
+        with torch.cuda.stream(st):
+            return fn(*args, stream=st, **kw)
+    return wrapper
+
+
+def _stream(stream) -> int:
+    return stream.cuda_stream
+
+
+_aux_streams = None   # per host thread: device index -> second stream of the fused linear calls
+
+
+def _aux_stream(aux_stream, device):
+    """The fused linear calls' second stream: "auto" gives this host thread's own stream on
+    ``device`` (created on first use, default priority), None gives none (one stream), anything
+    else is taken as given."""
+    import threading
+    import torch
+    global _aux_streams
+    if aux_stream is None:
+        return None
+    if not (isinstance(aux_stream, str) and aux_stream == "auto"):
+        return aux_stream.cuda_stream if hasattr(aux_stream, "cuda_stream") else int(aux_stream)
+    if _aux_streams is None:
+        _aux_streams = threading.local()
+    table = getattr(_aux_streams, "by_device", None)
+    if table is None:
+        table = _aux_streams.by_device = {}
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in table:
+        table[idx] = torch.cuda.Stream(device=idx)
+    return table[idx].cuda_stream
 
 
 def _dtype_code(t) -> int:
@@ -176,6 +230,7 @@ class CEResult:
     counts: object        # int64 [3] {n_valid, n_correct, n_bad}
 
 
+@_on_call_stream
 def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
                    softcap: float = 0.0, reduction: str = "mean", grad_out=None, want_argmax: bool = False,
                    loss_tok=None, loss_out=None, argmax_out=None, counts=None, workspace=None,
@@ -199,8 +254,8 @@ def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing:
     if counts is None:
         counts = torch.empty(3, dtype=torch.int64, device=dev)
     wsb = lce_ce_workspace_bytes(n, V)
-    if workspace is None:
-        workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    if workspace is None:   # needs no initialisation (tagged counters)
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     _buf(loss_tok, "loss_tok", torch.float32, n, dev)
     _buf(loss_out, "loss_out", torch.float32, 1, dev)
     _buf(argmax_out, "argmax_out", torch.int64, n, dev)
@@ -214,6 +269,7 @@ def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing:
     return CEResult(loss_tok, loss_out, argmax_out, counts)
 
 
+@_on_call_stream
 def lce_ce_argmax(logits, labels=None, *, ignore_index: int = -100, argmax_out=None, counts=None,
                   stream=None):
     """Read-only argmax sweep.  Returns (argmax int64 [n], counts int64 [3])."""
@@ -248,6 +304,7 @@ def _shard_view(shard):
     return n, Vs, (shard.stride(0) if n > 1 else Vs)
 
 
+@_on_call_stream
 def lce_ce_stats(shard, labels, *, v_offset: int = 0, ignore_index: int = -100, softcap: float = 0.0,
                  stats=None, stream=None):
     """One read-only sweep of a vocabulary shard (global columns [v_offset, v_offset + width));
@@ -276,6 +333,7 @@ class SplitRows:
     counts: object         # int64 [3]
 
 
+@_on_call_stream
 def lce_ce_combine(stats, labels, V: int, *, ignore_index: int = -100, label_smoothing: float = 0.0,
                    reduction: str = "mean", stream=None) -> SplitRows:
     """Row results from the stats of all shards: ``stats`` is fp32 [shards, n, 8] (or [n, 8] for one),
@@ -298,6 +356,7 @@ def lce_ce_combine(stats, labels, V: int, *, ignore_index: int = -100, label_smo
     return out
 
 
+@_on_call_stream
 def lce_ce_grad(shard, labels, V: int, rows: SplitRows, *, v_offset: int = 0, ignore_index: int = -100,
                 label_smoothing: float = 0.0, softcap: float = 0.0, reduction: str = "mean", grad_out=None,
                 stream=None) -> None:
@@ -400,12 +459,14 @@ class FLCEResult:
     counts: object        # int64 [3]
 
 
+@_on_call_stream
 def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
                      softcap: float = 0.0, reduction: str = "mean", grad_out=None, chunk_tokens: int = 1024,
                      loss_tok=None, loss_out=None, grad_hidden=None, grad_weight=None, counts=None, workspace=None,
-                     stream=None) -> FLCEResult:
+                     stream=None, aux_stream="auto") -> FLCEResult:
     """Fused linear cross-entropy of hidden [n, H] (bf16) and weight [V, H] (bf16), chunked over
-    tokens.  Outputs not passed in are allocated."""
+    tokens.  Outputs not passed in are allocated.  ``aux_stream``: the second stream the transposes
+    may run on ("auto": this host thread's own stream on the device; None: one stream)."""
     import torch
     dev = _check_flce_operands(hidden, weight)
     n, H = hidden.shape
@@ -423,8 +484,8 @@ def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_
     if counts is None:
         counts = torch.empty(3, dtype=torch.int64, device=dev)
     wsb = lce_flce_workspace_bytes(n, H, V, chunk_tokens)
-    if workspace is None:
-        workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    if workspace is None:   # clobbered by the call; its contents do not matter
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     _buf(loss_tok, "loss_tok", torch.float32, n, dev)
     _buf(loss_out, "loss_out", torch.float32, 1, dev)
     _buf(grad_hidden, "grad_hidden", torch.bfloat16, n * H, dev)
@@ -435,7 +496,8 @@ def lce_flce_fwd_bwd(hidden, weight, labels, *, ignore_index: int = -100, label_
                                 float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                                 int(chunk_tokens), _ptr(loss_tok), _ptr(loss_out), _ptr(grad_hidden),
                                 _ptr(grad_weight), _ptr(counts), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream))
+                                workspace.numel() * workspace.element_size(), _stream(stream),
+                                _aux_stream(aux_stream, dev))
     _check(st)
     return FLCEResult(loss_tok, loss_out, grad_hidden, grad_weight, counts)
 
@@ -460,6 +522,7 @@ def _check_flce_operands(hidden, weight):
     return dev
 
 
+@_on_call_stream
 def lce_flce_forward(hidden, weight, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
                      softcap: float = 0.0, reduction: str = "mean", workspace=None, out: SplitRows | None = None,
                      stream=None) -> SplitRows:
@@ -490,10 +553,13 @@ def lce_flce_forward(hidden, weight, labels, *, ignore_index: int = -100, label_
     return out
 
 
+@_on_call_stream
 def lce_flce_backward(hidden, weight, labels, rows: SplitRows, *, ignore_index: int = -100,
                       label_smoothing: float = 0.0, softcap: float = 0.0, reduction: str = "mean", grad_out=None,
-                      chunk_tokens: int = 1024, grad_hidden=None, grad_weight=None, workspace=None, stream=None):
-    """grad_hidden (bf16 [n, H]) and grad_weight (fp32 [V, H]) from the forward's rows."""
+                      chunk_tokens: int = 1024, grad_hidden=None, grad_weight=None, workspace=None, stream=None,
+                      aux_stream="auto"):
+    """grad_hidden (bf16 [n, H]) and grad_weight (fp32 [V, H]) from the forward's rows; ``aux_stream`` as
+    for lce_flce_fwd_bwd."""
     import torch
     dev = _check_flce_operands(hidden, weight)
     n, H = hidden.shape
@@ -516,7 +582,8 @@ def lce_flce_backward(hidden, weight, labels, rows: SplitRows, *, ignore_index: 
                                    float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                                    int(chunk_tokens), _ptr(rows.lse), _ptr(rows.one_minus_py), _ptr(rows.counts),
                                    _ptr(grad_hidden), _ptr(grad_weight), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+                                   workspace.numel() * workspace.element_size(), _stream(stream),
+                                   _aux_stream(aux_stream, dev)))
     return grad_hidden, grad_weight
 
 

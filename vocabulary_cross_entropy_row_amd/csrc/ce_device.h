@@ -56,6 +56,74 @@ struct Cap {
     __device__ __forceinline__ static float chain(float r, float q) { return 4.0f * r * q; }
 };
 
+// ---- tagged counters -----------------------------------------------------
+// Every counter is a 64-bit word: a 32-bit tag above a 32-bit count.  The tag
+// of a launch is its dispatch id (the packet's index in its hardware queue,
+// which every workgroup of the launch reads from the same SGPRs and every
+// launch or graph replay on a queue gets anew) with the top bit set, so no
+// launch uses tag 0.  A finished call leaves its words at 0.  At its start,
+// each workgroup of a launch claims the words: a compare-and-swap from 0 to
+// (tag, 0), issued without waiting for it; the first claim to reach a word
+// succeeds and the rest find the tag installed.  Each workgroup's claim is
+// ordered before its own draws on the same word (same address, same thread),
+// so when the call finds clean words every draw -- a plain increment -- sees
+// the launch's tag.  A draw that finds another tag -- a word left by a call
+// that never finished, or whatever the workspace held before its first use --
+// installs (tag, 1) with a compare-and-swap and takes count 0, or, if another
+// workgroup of the launch got there first, draws again.  So the counters never
+// need clearing before a call.
+}  // namespace dev
+extern "C" __device__ unsigned long long lce_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+namespace dev {
+__device__ __forceinline__ unsigned launch_tag() {
+    return static_cast<unsigned>(lce_dispatch_id()) | 0x80000000u;
+}
+// install (tag, 0) in a clean word; the result is not waited for
+__device__ __forceinline__ void tagged_claim(unsigned long long *w, unsigned tag) {
+    unsigned long long clean = 0ull;
+    (void)__hip_atomic_compare_exchange_strong(w, &clean, static_cast<unsigned long long>(tag) << 32,
+                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+// The increment, issued now and resolved later (tagged_count).  A wrapping
+// increment (never reaching its bound) rather than an add: the compiler rewrites
+// a one-lane add into a wave-level form that consumes the result at once, i.e.
+// waits right there for every memory operation issued before it, the row
+// loads included.
+__device__ __forceinline__ unsigned long long tagged_inc(unsigned long long *w) {
+    return __builtin_amdgcn_atomic_inc64(reinterpret_cast<unsigned long *>(w), ~0ul, __ATOMIC_RELAXED, "");
+}
+// the count of a draw whose increment returned `seen`
+__device__ __forceinline__ unsigned tagged_count(unsigned long long *w, unsigned long long seen, unsigned tag) {
+    if (static_cast<unsigned>(seen >> 32) == tag) return static_cast<unsigned>(seen);
+    unsigned long long cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    for (;;) {
+        if (static_cast<unsigned>(cur >> 32) == tag) {   // installed by another workgroup: draw again
+            cur = tagged_inc(w);
+            if (static_cast<unsigned>(cur >> 32) == tag) return static_cast<unsigned>(cur);
+            continue;
+        }
+        if (__hip_atomic_compare_exchange_strong(w, &cur, (static_cast<unsigned long long>(tag) << 32) | 1ull,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+            return 0u;
+    }
+}
+__device__ __forceinline__ unsigned tagged_draw(unsigned long long *w, unsigned tag) {
+    return tagged_count(w, tagged_inc(w), tag);
+}
+
+// Row-kernel workspace: the completion counter at byte 0, the row counter at
+// byte 64, the counter of the ignored-row chunks at byte 128 (tagged words, one
+// per 64-byte line), int64 n_correct partials of the workgroups from byte 256.
+constexpr size_t kWsPartials = 256;
+__device__ __forceinline__ unsigned long long *ws_ticket(void *ws) { return static_cast<unsigned long long *>(ws); }
+__device__ __forceinline__ unsigned long long *ws_rows(void *ws) { return static_cast<unsigned long long *>(ws) + 8; }
+__device__ __forceinline__ unsigned long long *ws_zero_chunks(void *ws) {
+    return static_cast<unsigned long long *>(ws) + 16;
+}
+__device__ __forceinline__ long long *ws_correct(void *ws) {
+    return reinterpret_cast<long long *>(static_cast<char *>(ws) + kWsPartials);
+}
+
 // ---- element access ---------------------------------------------------------
 
 template <bool BF16> struct Elt;

@@ -56,8 +56,8 @@ __device__ __forceinline__ RowInfo row_info(const CEArgs &a, int64_t row) {
 __device__ void finish_call(const CEArgs &a, int *sh_flag, double *sh_d) {
     if (threadIdx.x == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const unsigned t = __hip_atomic_fetch_add(static_cast<unsigned *>(a.workspace), 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
+        // the tagged completion counter (see tagged_draw)
+        const unsigned t = tagged_draw(ws_ticket(a.workspace), launch_tag());
         const int last = t == gridDim.x - 1;
         if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         *sh_flag = last;
@@ -83,7 +83,7 @@ __device__ void finish_call(const CEArgs &a, int *sh_flag, double *sh_d) {
             }
             *a.loss_out = out;
         }
-        *static_cast<unsigned *>(a.workspace) = 0u;
+        *ws_ticket(a.workspace) = 0ull;
     }
 }
 
@@ -97,7 +97,7 @@ __device__ __forceinline__ void record_argmax(const CEArgs &a, int64_t row, cons
 
 __global__ __launch_bounds__(1024) void ce_count_kernel(const int64_t *labels, int64_t n, int64_t V,
                                                         int64_t ignore_index, int64_t *counts,
-                                                        unsigned *ticket, float *loss_out) {
+                                                        unsigned long long *ticket, float *loss_out) {
     __shared__ long long sh[2][16];
     long long nv = 0, nb = 0;
     for (int64_t i = threadIdx.x; i < n; i += 1024) {
@@ -124,11 +124,11 @@ __global__ __launch_bounds__(1024) void ce_count_kernel(const int64_t *labels, i
         counts[1] = 0;
         counts[2] = b;
         if (ticket) {
-            // the row kernel's completion, row and zeroing-chunk counters: a
-            // caller-clobbered workspace (the fused linear call's) starts from zero
-            ticket[0] = 0u;
-            ticket[1] = 0u;
-            ticket[2] = 0u;
+            // the row kernel's completion, row and zeroing-chunk counters (tagged,
+            // so not required; a clobbered workspace then starts from clean words)
+            *ws_ticket(ticket) = 0ull;
+            *ws_rows(ticket) = 0ull;
+            *ws_zero_chunks(ticket) = 0ull;
         }
         if (loss_out) *loss_out = 0.0f;
     }
@@ -149,6 +149,7 @@ __global__ __launch_bounds__(NT) void ce_row_generic(CEArgs a) {
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int V = static_cast<int>(a.V);
+    if (tid == 0) tagged_claim(ws_ticket(a.workspace), launch_tag());
     const RowInfo ri = row_info(a, row);
     const int64_t base = row * a.ld;
     const bool smooth = a.eps != 0.0f;
@@ -185,19 +186,20 @@ __global__ __launch_bounds__(NT) void ce_row_generic(CEArgs a) {
     const float xy = EL::load_one(a.logits, base + ri.y);
     const float Mz = SOFTCAP ? cap.z_of_r(cap.r_of(m)) : m;
     const float zy = SOFTCAP ? cap.z_of_r(cap.r_of(xy)) : xy;
-    const float MzL = Mz * kLog2e;
+    // every weight relative to the row max itself (z - M is exact where the
+    // weight matters), not to an fp32 rounding of M log2 e
     float s = 0.0f, zs = 0.0f;
     for (int j = tid; j < V; j += NT) {
         const float x = EL::load_one(a.logits, base + j);
         const float z = SOFTCAP ? cap.z_of_r(cap.r_of(x)) : x;
-        if (j != ri.y) s += exp2_fast(fmaf(z, kLog2e, -MzL));
+        if (j != ri.y) s += exp2_fast((z - Mz) * kLog2e);
         zs += z;
     }
     s = block_sum(s, sh_s);
     zs = block_sum(zs, sh_z);
     const float eps = a.eps;
     const float invV = 1.0f / static_cast<float>(a.V);
-    const float S = s + exp2_fast(fmaf(zy, kLog2e, -MzL));
+    const float S = s + exp2_fast((zy - Mz) * kLog2e);
     const float lse = Mz + logf(S);
     if (tid == 0) {
         float loss = lse - (1.0f - eps) * zy;
@@ -207,7 +209,8 @@ __global__ __launch_bounds__(NT) void ce_row_generic(CEArgs a) {
     __syncthreads();   // every thread has read x_y before any gradient overwrites it
     const float scale = ri.scale;
     const float epsV = eps * invV;
-    const float lseL = lse * kLog2e;
+    // exponent (z - M) log2 e - log2 S, consistent with the weights above
+    const float l2S = log2f(S);
     for (int j = tid; j < V; j += NT) {
         const float x = EL::load_one(a.logits, base + j);
         float g;
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(NT) void ce_row_generic(CEArgs a) {
             chain = Cap::chain(r, q);
         }
         if (j == ri.y) g = scale * (eps - s / S - epsV) * chain;
-        else g = scale * (exp2_fast(fmaf(z, kLog2e, -lseL)) - epsV) * chain;
+        else g = scale * (exp2_fast(fmaf(z - Mz, kLog2e, -l2S)) - epsV) * chain;
         EL::store_one(a.logits, base + j, g);
     }
     finish_call(a, &sh_flag, sh_d);
@@ -348,14 +351,14 @@ hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream) 
         return launch_resident(a, is_bf16, kr, kl, stream);
     }
     hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, a.count_labels, a.count_n, a.V,
-                       a.ignore_index, a.counts, static_cast<unsigned *>(a.workspace), a.loss_out);
+                       a.ignore_index, a.counts, static_cast<unsigned long long *>(a.workspace), a.loss_out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.n == 0) return err;
     return is_bf16 ? launch_generic<true>(a, stream) : launch_generic<false>(a, stream);
 }
 
 hipError_t launch_ce_count(const int64_t *labels, int64_t n, int64_t V, int64_t ignore_index, int64_t *counts,
-                           unsigned *ticket, float *loss_out, hipStream_t stream) {
+                           unsigned long long *ticket, float *loss_out, hipStream_t stream) {
     hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, labels, n, V, ignore_index, counts, ticket,
                        loss_out);
     return hipGetLastError();
@@ -366,10 +369,10 @@ hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const 
                             hipStream_t stream) {
     if (labels) {
         hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, labels, n, V, ignore_index, counts,
-                           static_cast<unsigned *>(nullptr), static_cast<float *>(nullptr));
+                           static_cast<unsigned long long *>(nullptr), static_cast<float *>(nullptr));
     } else {
         hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, labels, int64_t(0), V, ignore_index,
-                           counts, static_cast<unsigned *>(nullptr), static_cast<float *>(nullptr));
+                           counts, static_cast<unsigned long long *>(nullptr), static_cast<float *>(nullptr));
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0) return err;

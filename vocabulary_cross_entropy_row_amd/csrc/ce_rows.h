@@ -41,10 +41,6 @@
 namespace lce {
 namespace dev {
 
-// Workspace layout: [0,4) completion counter, [4,8) row counter, [8,12) counter
-// of the ignored-row chunks (all zero between calls), [256, 256 + 8G) int64
-// n_correct partials.
-constexpr size_t kWsPartials = 256;
 // Ignored rows one draw may step over; past that the ignored row is processed
 // (with scale 0) instead of drawing again.
 constexpr int kSkipMax = 16;
@@ -56,26 +52,11 @@ constexpr int kBufferWord3 = 0x00020000;
 // Cache-policy bit of buffer loads/stores: non-temporal (streamed once).
 constexpr int kNonTemporal = 2;
 
-__device__ __forceinline__ unsigned *ws_ticket(void *ws) { return static_cast<unsigned *>(ws); }
-__device__ __forceinline__ unsigned *ws_rows(void *ws) { return static_cast<unsigned *>(ws) + 1; }
-__device__ __forceinline__ unsigned *ws_zero_chunks(void *ws) { return static_cast<unsigned *>(ws) + 2; }
-__device__ __forceinline__ long long *ws_correct(void *ws) {
-    return reinterpret_cast<long long *>(static_cast<char *>(ws) + kWsPartials);
-}
 // Row draws and the final fold's operands go through system-scope atomics:
 // they are performed at, or written through to, memory, so workgroups on
 // different XCDs (each with its own L2) see each other's values without a
 // cache-wide writeback or invalidate.
-// The draw is a wrapping increment (never reaching its 2^32 - 1 bound) rather
-// than an add: the compiler rewrites a one-lane add into a wave-level form
-// that consumes the result at once, i.e. waits right there for every memory
-// operation issued before it, the row loads included.
-__device__ __forceinline__ unsigned draw_row(void *ws) {
-    return __builtin_amdgcn_atomic_inc32(ws_rows(ws), 0xffffffffu, __ATOMIC_RELAXED, "");
-}
-__device__ __forceinline__ unsigned draw_zero_chunk(void *ws) {
-    return __builtin_amdgcn_atomic_inc32(ws_zero_chunks(ws), 0xffffffffu, __ATOMIC_RELAXED, "");
-}
+
 __device__ __forceinline__ void store_through(float *p, float v) {
     __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_SYSTEM);
@@ -187,13 +168,19 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // ignored one is carried through with scale 0
     int64_t row = blockIdx.x;
     // thread 0's draw of the row after the next one: requested behind the LDS
-    // rounds of a row, so it has landed when they have
-    unsigned draw = 0;
+    // rounds of a row, so it has landed when they have (resolved when used)
+    const unsigned tag = launch_tag();
+    unsigned long long draw = 0;
+    bool drawn = false;
     {
         const __amdgpu_buffer_rsrc_t src = row_rsrc(row, row < n);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (k == KL && tid == 0 && G < n) draw = draw_row(a.workspace);
+            if (k == KL && tid == 0 && G < n) {
+                tagged_claim(ws_rows(a.workspace), tag);
+                draw = tagged_inc(ws_rows(a.workspace));
+                drawn = true;
+            }
             issue_round(k, src);
             __builtin_amdgcn_sched_barrier(0);   // issue in the order pass A consumes
         }
@@ -252,7 +239,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         // thread 0: the drawn row and its label, requested now so both have
         // landed by the combine barrier (the draw was issued before the row's
         // register rounds, so it is complete once they are)
-        int64_t nx = static_cast<int64_t>(G) + static_cast<int64_t>(draw);
+        int64_t nx = n;
+        if (tid == 0 && drawn) nx = static_cast<int64_t>(G) + tagged_count(ws_rows(a.workspace), draw, tag);
         int64_t ynx = 0;
         if constexpr (!ARGMAX)
             if (tid == 0 && nx < n) ynx = a.labels[nx];
@@ -309,9 +297,15 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                     const float b = fmaf(a.softcap, kLog2e, -mnL);
 #pragma unroll
                     for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], capk, b));
-                } else {
+                } else if constexpr (BF16) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], kLog2e, -mnL));
+                } else {
+                    // fp32 rows: every weight relative to the running max itself
+                    // (z - m is exact where the weight matters), not to an fp32
+                    // rounding of m log2 e
+#pragma unroll
+                    for (int e = 0; e < E; ++e) ex[e] = exp2_fast((z[e] - mn) * kLog2e);
                 }
                 if (k == ky) {
                     // the target's round (uniform branch, taken once per row); the
@@ -331,7 +325,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 part = ex[0];
 #pragma unroll
                 for (int e = 1; e < E; ++e) part += ex[e];
-                s = fmaf(s, exp2_fast(fmaf(m, kLog2e, -mnL)), part);
+                s = fmaf(s, exp2_fast(BF16 || SOFTCAP ? fmaf(m, kLog2e, -mnL) : (m - mn) * kLog2e), part);
                 m = mn;
             }
         }
@@ -361,7 +355,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 // workgroups that have run out of rows
                 if constexpr (!ARGMAX) {
                     for (int skips = 0; nx < n && !valid_label(ynx) && skips < kSkipMax; ++skips) {
-                        nx = static_cast<int64_t>(G) + static_cast<int64_t>(draw_row(a.workspace));
+                        nx = static_cast<int64_t>(G) + tagged_draw(ws_rows(a.workspace), tag);
                         if (nx < n) ynx = a.labels[nx];
                     }
                 }
@@ -393,7 +387,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const float xy = sh_xy[pb];
         const float Mz = m;
         const float zy = SOFTCAP ? cap.z_of_r(cap.r_of(xy)) : xy;
-        const float e_y = exp2_fast(fmaf(zy, kLog2e, -Mz * kLog2e));
+        const float e_y = exp2_fast((zy - Mz) * kLog2e);
         const float S = s + e_y;
         const float lse = Mz + logf(S);
         // thread 0's row outputs are stored only after the next row's loads
@@ -412,6 +406,12 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         const float l2s = log2f(ascale);                  // -inf when the scale is 0
         const float epsV = SMOOTH ? eps * invV * ascale : 0.0f;
         const float lseL = lse * kLog2e - l2s;
+        // fp32 rows: the exponent is (x - M) log2 e + (log2|s_i| - log2 S), like
+        // pass A's weights, so the row max never passes through an fp32 rounding
+        // of LSE or of M log2 e (at |x| ~ 4e3 their ulp, 5e-4, would be a relative
+        // error in every p_j).  bf16 rows keep the one-fma form: that rounding is
+        // far below half a bf16 ulp.
+        const float l2rel = l2s - log2f(S);
         const float capb2 = (a.softcap - lse) * kLog2e + l2s;
         float gy = scale * (eps - s / S - (SMOOTH ? eps * invV : 0.0f));   // s_i (p_y - (1 - eps) - eps/V)
         if constexpr (SOFTCAP) {
@@ -436,7 +436,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                     const float p4 = exp2_fast(fmaf(r, capk, capb2 + 2.0f));   // 4 |s_i| p_j
                     g[e] = (SMOOTH ? p4 - 4.0f * epsV : p4) * (r * q);
                 } else {
-                    const float p = exp2_fast(fmaf(x, kLog2e, -lseL));      // |s_i| p_j
+                    const float p = BF16 ? exp2_fast(fmaf(x, kLog2e, -lseL))          // |s_i| p_j
+                                         : exp2_fast(fmaf(x - Mz, kLog2e, l2rel));
                     g[e] = SMOOTH ? p - epsV : p;
                 }
             }
@@ -466,7 +467,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         }
         // the row after the next (none to draw once the schedule has run out: a
         // draw still in flight would delay this workgroup's final publish)
-        if (tid == 0 && nxt < n) draw = draw_row(a.workspace);
+        if (tid == 0) {
+            drawn = nxt < n;
+            if (drawn) draw = tagged_inc(ws_rows(a.workspace));
+        }
         __builtin_amdgcn_sched_barrier(0);
         // the register rounds, then the next row's register rounds
 #pragma unroll
@@ -493,8 +497,9 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // ignored row that was also carried through the row loop (past kSkipMax
     // skips) gets zeros twice: the same bytes.
     if constexpr (!ARGMAX) {
+        if (tid == 0 && G < n) tagged_claim(ws_zero_chunks(a.workspace), tag);
         for (int q = 0; G < n; q ^= 1) {
-            if (tid == 0) sh_chunk[q] = draw_zero_chunk(a.workspace);
+            if (tid == 0) sh_chunk[q] = tagged_draw(ws_zero_chunks(a.workspace), tag);
             __syncthreads();
             const int64_t c0 = static_cast<int64_t>(G) + static_cast<int64_t>(sh_chunk[q]) * kZeroChunk;
             if (c0 >= n) break;
@@ -517,8 +522,8 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         __hip_atomic_store(ws_correct(a.workspace) + blockIdx.x, correct, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const unsigned t = __hip_atomic_fetch_add(ws_ticket(a.workspace), 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_SYSTEM);
+        tagged_claim(ws_ticket(a.workspace), tag);
+        const unsigned t = tagged_draw(ws_ticket(a.workspace), tag);
         sh_flag = t == static_cast<unsigned>(G) - 1u;
     }
     __syncthreads();
@@ -574,9 +579,9 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         a.counts[0] = n_valid;
         a.counts[1] = c;
         a.counts[2] = n_bad;
-        *ws_ticket(a.workspace) = 0u;
-        *ws_rows(a.workspace) = 0u;
-        *ws_zero_chunks(a.workspace) = 0u;
+        *ws_ticket(a.workspace) = 0ull;
+        *ws_rows(a.workspace) = 0ull;
+        *ws_zero_chunks(a.workspace) = 0ull;
     }
 }
 

@@ -23,7 +23,6 @@
 // logits exists at a time.
 #include <hip/hip_runtime.h>
 #include <algorithm>
-#include <mutex>
 #include <stdint.h>
 
 #include "ce_device.h"
@@ -304,50 +303,46 @@ bool flce_plan(int64_t n, int64_t H, int64_t V, int64_t chunk, size_t bytes, int
     return flce_layout(n, H, V, chunk, group, false).bytes <= bytes;
 }
 
-// A second stream per device for the bandwidth-bound transposes, which then run
-// beside the MFMA-bound GEMMs on the caller's stream: W^T beside the first chunk's
-// logits GEMM, each G_c^T beside its grad_hidden GEMM.  Default priority,
-// non-blocking; events fork it from and join it back to the caller's stream (so a
-// captured call captures both).  One mutex per process orders the enqueueing of
-// calls from several host threads, which share a device's side stream.
-struct SideStream {
-    hipStream_t s = nullptr;
+// The caller's optional second stream for the bandwidth-bound transposes, which
+// then run beside the MFMA-bound GEMMs on the caller's stream: W^T beside the
+// first chunk's logits GEMM, each G_c^T beside its grad_hidden GEMM.  Three
+// events, created by the call and destroyed when it has enqueued everything,
+// fork it from and join it back to the caller's stream, so a captured call
+// captures both and nothing is kept between calls.  A second stream that is
+// being captured while the caller's stream is not (or into another graph) is
+// left alone: everything then runs on the caller's stream.
+struct Aux {
+    hipStream_t s = nullptr;   // null: no second stream
     hipEvent_t fork = nullptr, wt = nullptr, gt = nullptr;
-};
-std::mutex g_side_mu;
-
-// the side stream of the device that `st` belongs to, created there on first use
-hipError_t side_stream(hipStream_t st, SideStream **out) {
-    static SideStream tab[64];
-    hipDevice_t d = 0;
-    hipError_t e = hipStreamGetDevice(st, &d);
-    if (e != hipSuccess) return e;
-    if (d < 0 || d >= 64) return hipErrorInvalidDevice;
-    SideStream &t = tab[d];
-    if (!t.s) {
-        int cur = 0;
-        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
-        if (cur != d && (e = hipSetDevice(d)) != hipSuccess) return e;
-        SideStream n;
-        if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) == hipSuccess &&
-            (e = hipEventCreateWithFlags(&n.wt, hipEventDisableTiming)) == hipSuccess &&
-            (e = hipEventCreateWithFlags(&n.gt, hipEventDisableTiming)) == hipSuccess)
-            e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
-        if (cur != d) {
-            const hipError_t e2 = hipSetDevice(cur);
-            if (e == hipSuccess) e = e2;
-        }
-        if (e != hipSuccess) return e;
-        t = n;   // published only once complete
+    Aux() = default;
+    Aux(const Aux &) = delete;
+    Aux &operator=(const Aux &) = delete;
+    ~Aux() {
+        for (hipEvent_t e : {fork, wt, gt})
+            if (e) (void)hipEventDestroy(e);   // released once the recorded work has run
     }
-    *out = &t;
+};
+
+hipError_t aux_open(hipStream_t st, hipStream_t aux, Aux *A) {
+    if (!aux || aux == st) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone, ca = hipStreamCaptureStatusNone;
+    unsigned long long ids = 0, ida = 0;
+    hipError_t e;
+    if ((e = hipStreamGetCaptureInfo(st, &cs, &ids)) != hipSuccess) return e;
+    if ((e = hipStreamGetCaptureInfo(aux, &ca, &ida)) != hipSuccess) return e;
+    if (ca == hipStreamCaptureStatusActive && (cs != hipStreamCaptureStatusActive || ida != ids)) return hipSuccess;
+    if ((e = hipEventCreateWithFlags(&A->fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&A->wt, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&A->gt, hipEventDisableTiming)) != hipSuccess)
+        return e;
+    A->s = aux;
     return hipSuccess;
 }
 
-// the side stream starts after everything enqueued on st so far
-hipError_t fork_to(const SideStream &S, hipStream_t st) {
-    hipError_t e = hipEventRecord(S.fork, st);
-    return e != hipSuccess ? e : hipStreamWaitEvent(S.s, S.fork, 0);
+// the second stream starts after everything enqueued on st so far
+hipError_t fork_to(const Aux &A, hipStream_t st) {
+    hipError_t e = hipEventRecord(A.fork, st);
+    return e != hipSuccess ? e : hipStreamWaitEvent(A.s, A.fork, 0);
 }
 
 hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
@@ -364,7 +359,7 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
     const bool resident = f.lse != nullptr;
     // counts (and a zeroed completion counter for the chunk CE calls); the
     // resident backward takes them from its stats pass
-    if (!resident && (e = launch_ce_count(f.labels, f.n, V, f.ignore_index, f.counts, static_cast<unsigned *>(ce_ws),
+    if (!resident && (e = launch_ce_count(f.labels, f.n, V, f.ignore_index, f.counts, static_cast<unsigned long long *>(ce_ws),
                                           f.loss_out, st)) != hipSuccess)
         return e;
     if (f.n == 0) {
@@ -372,18 +367,20 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
         hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(2048), dim3(256), 0, st, f.grad_weight, tot);
         return hipGetLastError();
     }
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *S = nullptr;
-    if ((e = side_stream(st, &S)) != hipSuccess) return e;
+    Aux A;
+    if ((e = aux_open(st, f.aux, &A)) != hipSuccess) return e;
+    const bool two = A.s != nullptr;
+    // where the transposes of W and G_c go
+    const hipStream_t ts = two ? A.s : st;
     uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.off_wt);
     bool wt_pending = false, gt_pending = false;
-    if (f.with_wt) {   // W^T [H, V], on the side stream
-        if ((e = fork_to(*S, st)) != hipSuccess ||
-            (e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), S->s)) !=
+    if (f.with_wt) {   // W^T [H, V], on the second stream
+        if ((two && (e = fork_to(A, st)) != hipSuccess) ||
+            (e = transpose(f.weight, H, wt, V, static_cast<int>(V), static_cast<int>(V), static_cast<int>(H), ts)) !=
                 hipSuccess ||
-            (e = hipEventRecord(S->wt, S->s)) != hipSuccess)
+            (two && (e = hipEventRecord(A.wt, A.s)) != hipSuccess))
             return e;
-        wt_pending = true;
+        wt_pending = two;
     }
     const int tiles_dh = static_cast<int>(((C + gemm::BM - 1) / gemm::BM) * ((H + gemm::BN - 1) / gemm::BN));
     const int splits = choose_splits(tiles_dh, V);
@@ -400,7 +397,7 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             if ((e = transpose(hc, H, ht + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(H), st)) != hipSuccess)
                 return e;
             // the previous chunk's G^T transpose still reads z
-            if (gt_pending && (e = hipStreamWaitEvent(st, S->gt, 0)) != hipSuccess) return e;
+            if (gt_pending && (e = hipStreamWaitEvent(st, A.gt, 0)) != hipSuccess) return e;
             gt_pending = false;
             if (resident) {
                 // G_c straight from the GEMM's epilogue: Z_c stays in registers
@@ -443,13 +440,13 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
                 a.workspace = ce_ws;
                 if ((e = launch_ce_fwd_bwd(a, true, st)) != hipSuccess) return e;
             }
-            // G_c^T into columns [c0 - g0, ...) of the group's [V, ldg] buffer, on the side stream
-            if ((e = fork_to(*S, st)) != hipSuccess ||
-                (e = transpose(z, V, gt + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(V), S->s)) != hipSuccess ||
-                (e = hipEventRecord(S->gt, S->s)) != hipSuccess)
+            // G_c^T into columns [c0 - g0, ...) of the group's [V, ldg] buffer, on the second stream
+            if ((two && (e = fork_to(A, st)) != hipSuccess) ||
+                (e = transpose(z, V, gt + (c0 - g0), L.ldg, cn, cpad, static_cast<int>(V), ts)) != hipSuccess ||
+                (two && (e = hipEventRecord(A.gt, A.s)) != hipSuccess))
                 return e;
-            gt_pending = true;
-            if (wt_pending && (e = hipStreamWaitEvent(st, S->wt, 0)) != hipSuccess) return e;
+            gt_pending = two;
+            if (wt_pending && (e = hipStreamWaitEvent(st, A.wt, 0)) != hipSuccess) return e;
             wt_pending = false;
             // dH_c = G_c W: split-K partials [splits, cn, H] fp32, folded to bf16
             // (W^T K-contiguous when the workspace holds it, else W itself, k-major)
@@ -467,8 +464,8 @@ hipError_t launch_flce(const FlceArgs &f, hipStream_t st) {
             }
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        // the group's G^T is complete (this also joins the side stream back to st)
-        if (gt_pending && (e = hipStreamWaitEvent(st, S->gt, 0)) != hipSuccess) return e;
+        // the group's G^T is complete (this also joins the second stream back to st)
+        if (gt_pending && (e = hipStreamWaitEvent(st, A.gt, 0)) != hipSuccess) return e;
         gt_pending = false;
         // dW (+)= G_g^T H_g over the group's tokens (K padded to a whole 8-element chunk)
         if ((e = gemm_nt(g0 == 0 ? gemm::OUT_F32 : gemm::OUT_F32_ACC, gt, L.ldg, ht, L.ldg, f.grad_weight, H,

@@ -64,7 +64,7 @@ lce_status check_flce_resident(const char *fn, const void *hidden, const void *w
 
 extern "C" {
 
-int lce_abi_version(void) { return 2; }
+int lce_abi_version(void) { return 3; }
 
 const char *lce_last_error(void) { return g_err; }
 
@@ -252,7 +252,7 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
                             int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
                             lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, float *loss_tok,
                             float *loss_out, void *grad_hidden, float *grad_weight, int64_t *counts, void *workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            size_t workspace_bytes, hipStream_t stream, hipStream_t aux_stream) {
     const char *fn = "lce_flce_fwd_bwd";
     if (n < 0) return fail(LCE_ERR_INVALID_ARG, "%s: n must be >= 0 (got %lld)", fn, (long long)n);
     if (H < 1) return fail(LCE_ERR_INVALID_ARG, "%s: H must be >= 1 (got %lld)", fn, (long long)H);
@@ -287,6 +287,11 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
         static_cast<unsigned long long>(C) * V * 2 >= (1ull << 32) || 256ull * V * 2 >= (1ull << 32) ||
         256ull * H * 2 >= (1ull << 32))
         return fail(LCE_ERR_UNSUPPORTED, "%s: a chunk of logits or a 256-row operand tile exceeds 4 GiB", fn);
+    if (!with_wt && n > 0 && static_cast<unsigned long long>(V) * H * 2 >= (1ull << 32))
+        return fail(LCE_ERR_UNSUPPORTED,
+                    "%s: without room for W^T in the workspace the grad_hidden GEMM reads the weight in place, "
+                    "which needs V * H * 2 < 4 GiB (V=%lld H=%lld); pass lce_flce_workspace_bytes() bytes", fn,
+                    (long long)V, (long long)H);
     lce::FlceArgs f;
     f.hidden = hidden;
     f.weight = weight;
@@ -308,6 +313,7 @@ lce_status lce_flce_fwd_bwd(const void *hidden, const void *weight, const int64_
     f.workspace = workspace;
     f.group_chunks = group;
     f.with_wt = with_wt;
+    f.aux = aux_stream;
     return hip_status(lce::launch_flce(f, stream), "lce_flce_fwd_bwd launch");
 }
 
@@ -359,7 +365,7 @@ lce_status lce_flce_backward(const void *hidden, const void *weight, const int64
                              int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
                              lce_reduction reduction, const float *grad_out, int64_t chunk_tokens, const float *lse,
                              const float *one_minus_py, const int64_t *counts, void *grad_hidden, float *grad_weight,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                             void *workspace, size_t workspace_bytes, hipStream_t stream, hipStream_t aux_stream) {
     const char *fn = "lce_flce_backward";
     lce_status st = check_flce_resident(fn, hidden, weight, labels, n, H, V, label_smoothing, softcap, reduction);
     if (st != LCE_OK) return st;
@@ -380,6 +386,11 @@ lce_status lce_flce_backward(const void *hidden, const void *weight, const int64
     const int64_t C = chunk_tokens < n ? chunk_tokens : n;
     if (C > 0x7fffffffLL / 16 || static_cast<unsigned long long>(C) * V * 2 >= (1ull << 32))
         return fail(LCE_ERR_UNSUPPORTED, "%s: a chunk of gradients exceeds 4 GiB", fn);
+    if (!with_wt && n > 0 && static_cast<unsigned long long>(V) * H * 2 >= (1ull << 32))
+        return fail(LCE_ERR_UNSUPPORTED,
+                    "%s: without room for W^T in the workspace the grad_hidden GEMM reads the weight in place, "
+                    "which needs V * H * 2 < 4 GiB (V=%lld H=%lld); pass lce_flce_workspace_bytes() bytes", fn,
+                    (long long)V, (long long)H);
     lce::FlceArgs f;
     f.hidden = hidden;
     f.weight = weight;
@@ -403,6 +414,7 @@ lce_status lce_flce_backward(const void *hidden, const void *weight, const int64
     f.with_wt = with_wt;
     f.lse = lse;
     f.q = one_minus_py;
+    f.aux = aux_stream;
     return hip_status(lce::launch_flce(f, stream), "lce_flce_backward launch");
 }
 

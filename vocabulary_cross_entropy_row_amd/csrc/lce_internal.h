@@ -27,7 +27,7 @@ struct CEArgs {
     float *loss_out;         // scalar or NULL
     int64_t *argmax_out;     // [n] or NULL
     int64_t *counts;         // [3]
-    void *workspace;         // completion counter + per-workgroup partials
+    void *workspace;         // tagged counters + per-workgroup partials (any prior contents)
 };
 
 // Threads per row workgroup of the register-resident path.
@@ -55,9 +55,10 @@ hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const 
 // false for the generic streaming kernel.
 bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl);
 
-// counts = {n_valid, 0, n_bad} over labels[0, n); zeroes *ticket and *loss_out when given.
+// counts = {n_valid, 0, n_bad} over labels[0, n); clears the three counter words at
+// ticket and *loss_out when given.
 hipError_t launch_ce_count(const int64_t *labels, int64_t n, int64_t V, int64_t ignore_index, int64_t *counts,
-                           unsigned *ticket, float *loss_out, hipStream_t stream);
+                           unsigned long long *ticket, float *loss_out, hipStream_t stream);
 
 // loss_out = mean (over counts[0]) or sum of loss_tok[0, n), 0 for 'none'; one
 // workgroup, fixed-order fp64 sum.
@@ -120,6 +121,8 @@ struct FlceArgs {
     // (no logits stored, no losses written, counts read as given).
     const float *lse = nullptr;
     const float *q = nullptr;
+    // The caller's second stream for the transposes, or null (everything on the call's stream).
+    hipStream_t aux = nullptr;
 };
 
 // Stats pass of the tile-resident fused linear cross-entropy: one record per
