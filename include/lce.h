@@ -6,8 +6,9 @@
  * never synchronises the host: work is enqueued on `stream` and its outputs
  * are valid once that stream has been synchronised.  Calls on different
  * streams are independent as long as their buffers do not overlap.  The only
- * state kept between calls is the thread-local error text; the functions are
- * re-entrant.
+ * state kept between calls is the thread-local error text, and for
+ * lce_ce_fwd_bwd_noalloc (callers that cannot allocate) one scratch array per
+ * device; the other functions are re-entrant.
  *
  * Errors: arguments are checked before any HIP call.  A bad argument returns
  * LCE_ERR_INVALID_ARG, a valid but unsupported combination returns
@@ -107,6 +108,26 @@ lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const
                           float softcap, lce_reduction reduction, const float *grad_out,
                           float *loss_tok, float *loss_out, int64_t *argmax_out, int64_t *counts,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lce_ce_fwd_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture that may not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation).  Every
+ * argument, output and result is that of lce_ce_fwd_bwd; the call allocates
+ * nothing.  Its workspace is a file-scope device array of 65,792 bytes (room
+ * for any n: lce_ce_workspace_bytes stops growing at n = 4096), one copy per
+ * device, held until the process ends; the first call on a device looks up
+ * that copy's address with the device current (hipGetSymbolAddress) and keeps
+ * it.  The array keeps the last call's contents; its counters carry the tag of
+ * the launch that set them, so nothing in it needs clearing between calls.
+ * Calls that overlap on one device share that array and race: order them
+ * (one stream, or events) or use lce_ce_fwd_bwd with workspaces of their own.
+ */
+lce_status lce_ce_fwd_bwd_noalloc(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels,
+                                  int64_t n, int64_t V, int64_t ignore_index, float label_smoothing,
+                                  float softcap, lce_reduction reduction, const float *grad_out,
+                                  float *loss_tok, float *loss_out, int64_t *argmax_out, int64_t *counts,
+                                  hipStream_t stream);
 
 /*
  * Read-only argmax sweep [P2 "What does this PR do?"; P5 Summary]: argmax_out[i]

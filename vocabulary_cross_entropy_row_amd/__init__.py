@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
     L.lce_ce_fwd_bwd.restype = ctypes.c_int
     L.lce_ce_fwd_bwd.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, f32, f32, ctypes.c_int, p, p, p, p, p,
                                  p, ctypes.c_size_t, p]
+    L.lce_ce_fwd_bwd_noalloc.restype = ctypes.c_int
+    L.lce_ce_fwd_bwd_noalloc.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, f32, f32, ctypes.c_int, p, p, p, p,
+                                         p, p]
     L.lce_ce_argmax.restype = ctypes.c_int
     L.lce_ce_argmax.argtypes = [p, i64, ctypes.c_int, p, i64, i64, i64, p, p, p]
     L.lce_flce_workspace_bytes.restype = ctypes.c_size_t
@@ -265,6 +268,38 @@ def lce_ce_fwd_bwd(logits, labels, *, ignore_index: int = -100, label_smoothing:
                               float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
                               _ptr(loss_tok), _ptr(loss_out), _ptr(argmax_out), _ptr(counts), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+    return CEResult(loss_tok, loss_out, argmax_out, counts)
+
+
+@_on_call_stream
+def lce_ce_fwd_bwd_noalloc(logits, labels, *, ignore_index: int = -100, label_smoothing: float = 0.0,
+                           softcap: float = 0.0, reduction: str = "mean", grad_out=None, loss_tok=None, loss_out=None,
+                           argmax_out=None, counts=None, stream=None) -> CEResult:
+    """lce_ce_fwd_bwd with the library's own per-device scratch instead of a workspace (for callers
+    that cannot allocate: pass every output, and grad_out as an fp32 device tensor or None, and
+    nothing is allocated here either).  Calls overlapping on one device race on that scratch."""
+    import torch
+    if logits.dim() != 2 or (logits.size(1) > 1 and logits.stride(1) != 1):
+        raise ValueError("logits must be a 2-D view with unit column stride")
+    n, V = logits.shape
+    ld = logits.stride(0) if n > 1 else V
+    dev = _on_gpu(logits, "logits")
+    _buf(labels, "labels", torch.int64, n, dev, required=True)
+    grad_out = _grad_out(grad_out, reduction, n, dev)
+    if loss_tok is None:
+        loss_tok = torch.empty(n, dtype=torch.float32, device=dev)
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(3, dtype=torch.int64, device=dev)
+    _buf(loss_tok, "loss_tok", torch.float32, n, dev)
+    _buf(loss_out, "loss_out", torch.float32, 1, dev)
+    _buf(argmax_out, "argmax_out", torch.int64, n, dev)
+    _buf(counts, "counts", torch.int64, 3, dev)
+    st = lib().lce_ce_fwd_bwd_noalloc(_ptr(logits), ld, _dtype_code(logits), _ptr(labels), n, V, int(ignore_index),
+                                      float(label_smoothing), float(softcap), REDUCTIONS[reduction], _ptr(grad_out),
+                                      _ptr(loss_tok), _ptr(loss_out), _ptr(argmax_out), _ptr(counts), _stream(stream))
     _check(st)
     return CEResult(loss_tok, loss_out, argmax_out, counts)
 

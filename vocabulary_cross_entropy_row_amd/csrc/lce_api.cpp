@@ -8,7 +8,18 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "lce_internal.h"
+
+// The workspace of lce_ce_fwd_bwd_noalloc: room for the row kernel's workspace
+// at any n (its per-workgroup part stops growing at kMaxRowGroups workgroups),
+// one copy per device, held until the process ends.  Host code never uses this
+// name as an address: it is a host-side stand-in for the device symbol, whose
+// address on each device comes from hipGetSymbolAddress (noalloc_scratch).
+constexpr size_t kNoAllocScratchBytes = lce::ce_workspace_bytes(lce::kMaxRowGroups);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -73,42 +84,43 @@ size_t lce_ce_workspace_bytes(int64_t n, int64_t V) {
     return lce::ce_workspace_bytes(n);
 }
 
-lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
-                          int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
-                          lce_reduction reduction, const float *grad_out, float *loss_tok, float *loss_out,
-                          int64_t *argmax_out, int64_t *counts, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
-    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: n must be >= 0 (got %lld)", (long long)n);
-    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: V must be >= 1 (got %lld)", (long long)V);
-    if (ld < V) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: ld (%lld) must be >= V (%lld)", (long long)ld,
-                            (long long)V);
-    if (dtype != LCE_F32 && dtype != LCE_BF16)
-        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: unknown dtype %d", (int)dtype);
+}  // extern "C"
+
+namespace {
+
+// Checks of lce_ce_fwd_bwd's arguments other than the workspace, in the order the
+// header lists them; the call's name prefixes every message.
+lce_status check_ce_args(const char *fn, const void *logits_inout, int64_t ld, lce_dtype dtype,
+                         const int64_t *labels, int64_t n, int64_t V, float label_smoothing, float softcap,
+                         lce_reduction reduction, const float *loss_tok, const int64_t *counts) {
+    if (n < 0) return fail(LCE_ERR_INVALID_ARG, "%s: n must be >= 0 (got %lld)", fn, (long long)n);
+    if (V < 1) return fail(LCE_ERR_INVALID_ARG, "%s: V must be >= 1 (got %lld)", fn, (long long)V);
+    if (ld < V) return fail(LCE_ERR_INVALID_ARG, "%s: ld (%lld) must be >= V (%lld)", fn, (long long)ld, (long long)V);
+    if (dtype != LCE_F32 && dtype != LCE_BF16) return fail(LCE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     if (reduction != LCE_RED_NONE && reduction != LCE_RED_MEAN && reduction != LCE_RED_SUM)
-        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: unknown reduction %d", (int)reduction);
+        return fail(LCE_ERR_INVALID_ARG, "%s: unknown reduction %d", fn, (int)reduction);
     if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
-        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: label_smoothing must be in [0, 1] (got %g)",
-                    (double)label_smoothing);
+        return fail(LCE_ERR_INVALID_ARG, "%s: label_smoothing must be in [0, 1] (got %g)", fn, (double)label_smoothing);
     if (!(softcap >= 0.0f) || isinf(softcap))
-        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: softcap must be finite and >= 0 (got %g)", (double)softcap);
-    if (!counts) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: counts is required");
-    if (!workspace) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: workspace is required");
-    if (workspace_bytes < lce_ce_workspace_bytes(n, V))
-        return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: workspace_bytes %zu < required %zu", workspace_bytes,
-                    lce_ce_workspace_bytes(n, V));
-    if (!is_aligned(workspace, 16)) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: workspace must be 16-byte aligned");
+        return fail(LCE_ERR_INVALID_ARG, "%s: softcap must be finite and >= 0 (got %g)", fn, (double)softcap);
+    if (!counts) return fail(LCE_ERR_INVALID_ARG, "%s: counts is required", fn);
     if (n > 0) {
-        if (!logits_inout) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: logits is required");
-        if (!labels) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: labels is required");
-        if (!loss_tok) return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: loss_tok is required");
+        if (!logits_inout) return fail(LCE_ERR_INVALID_ARG, "%s: logits is required", fn);
+        if (!labels) return fail(LCE_ERR_INVALID_ARG, "%s: labels is required", fn);
+        if (!loss_tok) return fail(LCE_ERR_INVALID_ARG, "%s: loss_tok is required", fn);
         const size_t esz = dtype == LCE_BF16 ? 2 : 4;
         if (!is_aligned(logits_inout, esz))
-            return fail(LCE_ERR_INVALID_ARG, "lce_ce_fwd_bwd: logits must be aligned to its element size");
+            return fail(LCE_ERR_INVALID_ARG, "%s: logits must be aligned to its element size", fn);
     }
-    if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "lce_ce_fwd_bwd: n > 2^31-1 rows is not supported");
-    if (V > 0x7fffffffLL / 16)
-        return fail(LCE_ERR_UNSUPPORTED, "lce_ce_fwd_bwd: V > 2^27 columns is not supported");
+    return LCE_OK;
+}
 
+lce_status launch_ce(const char *fn, void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                     int64_t V, int64_t ignore_index, float label_smoothing, float softcap, lce_reduction reduction,
+                     const float *grad_out, float *loss_tok, float *loss_out, int64_t *argmax_out, int64_t *counts,
+                     void *workspace, hipStream_t stream) {
+    if (n > 0x7fffffffLL) return fail(LCE_ERR_UNSUPPORTED, "%s: n > 2^31-1 rows is not supported", fn);
+    if (V > 0x7fffffffLL / 16) return fail(LCE_ERR_UNSUPPORTED, "%s: V > 2^27 columns is not supported", fn);
     lce::CEArgs a;
     a.logits = logits_inout;
     a.ld = ld;
@@ -127,7 +139,82 @@ lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const
     a.argmax_out = argmax_out;
     a.counts = counts;
     a.workspace = workspace;
-    return hip_status(lce::launch_ce_fwd_bwd(a, dtype == LCE_BF16, stream), "lce_ce_fwd_bwd launch");
+    char what[64];
+    snprintf(what, sizeof what, "%s launch", fn);
+    return hip_status(lce::launch_ce_fwd_bwd(a, dtype == LCE_BF16, stream), what);
+}
+
+// Device address of `scratch` on each device, looked up by the first
+// lce_ce_fwd_bwd_noalloc call on that device (with the device current).
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;   // taken only until a device's address is known
+
+lce_status noalloc_scratch(const char *fn, hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_status(e, "lce_ce_fwd_bwd_noalloc: hipStreamGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(LCE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices the scratch table holds", fn, dev,
+                    kMaxDevices);
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_acquire);
+        if (!p) {
+            int cur = -1;
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e, "lce_ce_fwd_bwd_noalloc: hipGetDevice");
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+                return hip_status(e, "lce_ce_fwd_bwd_noalloc: hipSetDevice");
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+            if (e != hipSuccess) return hip_status(e, "lce_ce_fwd_bwd_noalloc: hipGetSymbolAddress");
+            if (back != hipSuccess) return hip_status(back, "lce_ce_fwd_bwd_noalloc: hipSetDevice");
+            if (!p) return fail(LCE_ERR_HIP, "%s: hipGetSymbolAddress gave a null address", fn);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                          int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                          lce_reduction reduction, const float *grad_out, float *loss_tok, float *loss_out,
+                          int64_t *argmax_out, int64_t *counts, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    const char *fn = "lce_ce_fwd_bwd";
+    lce_status st = check_ce_args(fn, logits_inout, ld, dtype, labels, n, V, label_smoothing, softcap, reduction,
+                                  loss_tok, counts);
+    if (st != LCE_OK) return st;
+    if (!workspace) return fail(LCE_ERR_INVALID_ARG, "%s: workspace is required", fn);
+    if (workspace_bytes < lce_ce_workspace_bytes(n, V))
+        return fail(LCE_ERR_INVALID_ARG, "%s: workspace_bytes %zu < required %zu", fn, workspace_bytes,
+                    lce_ce_workspace_bytes(n, V));
+    if (!is_aligned(workspace, 16)) return fail(LCE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+    return launch_ce(fn, logits_inout, ld, dtype, labels, n, V, ignore_index, label_smoothing, softcap, reduction,
+                     grad_out, loss_tok, loss_out, argmax_out, counts, workspace, stream);
+}
+
+lce_status lce_ce_fwd_bwd_noalloc(void *logits_inout, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
+                                  int64_t V, int64_t ignore_index, float label_smoothing, float softcap,
+                                  lce_reduction reduction, const float *grad_out, float *loss_tok, float *loss_out,
+                                  int64_t *argmax_out, int64_t *counts, hipStream_t stream) {
+    const char *fn = "lce_ce_fwd_bwd_noalloc";
+    lce_status st = check_ce_args(fn, logits_inout, ld, dtype, labels, n, V, label_smoothing, softcap, reduction,
+                                  loss_tok, counts);
+    if (st != LCE_OK) return st;
+    if (lce_ce_workspace_bytes(n, V) > kNoAllocScratchBytes)
+        return fail(LCE_ERR_UNSUPPORTED, "%s: needs %zu bytes of scratch, more than the %zu it holds", fn,
+                    lce_ce_workspace_bytes(n, V), kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if ((st = noalloc_scratch(fn, stream, &ws)) != LCE_OK) return st;
+    return launch_ce(fn, logits_inout, ld, dtype, labels, n, V, ignore_index, label_smoothing, softcap, reduction,
+                     grad_out, loss_tok, loss_out, argmax_out, counts, ws, stream);
 }
 
 lce_status lce_ce_argmax(const void *logits, int64_t ld, lce_dtype dtype, const int64_t *labels, int64_t n,
