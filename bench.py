@@ -74,6 +74,11 @@ def parse():
                     help="split: stats / combine / gradient as separate calls over --tp vocabulary shards; "
                          "resident: the tile-resident fused linear forward + backward (fused-linear workloads)")
     ap.add_argument("--tp", type=int, default=1, help="vocabulary shards of the split path (one GPU)")
+    ap.add_argument("--flce-workspace", choices=["default", "wt", "lean"], default="default",
+                    help="fused linear workspace: the default layout (one grad_weight pass, grad_hidden reads W in "
+                         "place), wt (also room for W^T), or lean (one chunk per grad_weight group)")
+    ap.add_argument("--no-pages-protocol", action="store_true",
+                    help="skip the extra per-call timing in the pages' protocol (10 warmups, 3 x 50 samples)")
     return ap.parse_args()
 
 
@@ -134,12 +139,50 @@ def split_cpu_baseline(w, x, y, nbytes: int, nthreads: int, min_seconds: float =
                       f"log-sum-exp, log p_y and entropy, scaled to the step's algorithmic bytes"}
 
 
+# ---------------------------------------------------------------- the pages' timing protocol
+
+def pages_protocol(call, work, pristine, stream, dev, warmup: int = 10, reps: int = 3, samples: int = 50) -> dict:
+    """Per-call latency measured the way the pages measure their CE table (Megatron-LM PR "Add opt-in
+    Liger vocab-parallel cross entropy", Performance: 10 warmups, 3 x 50 samples, the median, fresh
+    input clones outside the timed region): before every sample the logits are restored from the
+    pristine copy and a 512 MB buffer is written, so the 256 MB Infinity Cache holds none of the
+    restored logits; both untimed.  Each call is timed with HIP events on its stream."""
+    import numpy as np
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def sample(ev=None):
+        work.copy_(pristine)
+        flush.fill_(1)
+        if ev:
+            ev[0].record(stream)
+        call(work)
+        if ev:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        sample()
+    rep_ms = []
+    for _ in range(reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+        for e in evs:
+            sample(e)
+        torch.cuda.synchronize()
+        rep_ms.append([a.elapsed_time(b) for a, b in evs])
+    flat = np.concatenate(rep_ms)
+    return {"warmups": warmup, "reps": reps, "samples_per_rep": samples,
+            "median_ms": round(float(np.median(flat)), 5), "p10_ms": round(float(np.percentile(flat, 10)), 5),
+            "p90_ms": round(float(np.percentile(flat, 90)), 5),
+            "rep_medians_ms": [round(float(np.median(r)), 5) for r in rep_ms]}
+
+
 # ---------------------------------------------------------------- counter summaries
 
 # the sources each measured kernel is compiled from: the persistent row kernel, and for the
 # fused variant also its GEMM, transposes and driver
-CE_SOURCES = ("ce_device.h", "ce_rows.h", "ce_rows_inst.hip", "lce_internal.h")
-FLCE_SOURCES = CE_SOURCES + ("ce_kernels.hip", "gemm_mfma.h", "flce.hip", "ce_split.hip")
+CE_SOURCES = ("ce_device.h", "ce_rows.h", "ce_rows_inst.hip", "ce_rows_mr.h", "ce_rows_mr.hip", "ce_kernels.hip",
+              "lce_internal.h")
+FLCE_SOURCES = CE_SOURCES + ("gemm_mfma.h", "flce.hip", "ce_split.hip")
 
 
 def kernel_source_hash(workload: str = "") -> str:
@@ -179,18 +222,33 @@ def _rocprof(args: list[str], outdir: str, bench_args: list[str], timeout: int) 
 
 
 def _ours(name: str) -> bool:
-    return "ce_rows_kernel" in name or "ce_row_generic" in name
+    return "ce_rows_kernel" in name or "ce_rows_mr_kernel" in name or "ce_row_generic" in name
+
+
+# VALU counters of the row kernel (one rocprofv3 pass: 3 SQ counters, one GRBM counter)
+VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "VALUBusy", "GRBM_GUI_ACTIVE")
+CUS, CLOCK_GHZ = 256, 2.4          # MI355X compute units and peak engine clock
+TRANS_SLOWDOWN = 2                 # transcendentals take two issue slots (measured: half rate)
+
+
+def valu_roofline(valu_insts: float, trans_insts: float, kernel_ns: float) -> dict:
+    """The time the kernel's VALU instructions need at the issue rate (one wave64 instruction per CU per
+    clock, transcendentals four times as long), and the kernel's fraction of that bound."""
+    cycles = (valu_insts - trans_insts) + TRANS_SLOWDOWN * trans_insts   # CU-clocks, summed over CUs
+    bound_ns = cycles / CUS / CLOCK_GHZ
+    return {"bound_ns": bound_ns, "frac": bound_ns / kernel_ns if kernel_ns > 0 else float("nan")}
 
 
 def collect_profiles(workload: str) -> int:
     import synth
-    w = synth.WORKLOADS[workload]
+    w = synth.ALL_CE_WORKLOADS[workload]
     raw = os.path.join(RAW_PROFILES, workload)
     os.makedirs(raw, exist_ok=True)
     base = ["--workload", workload, "--no-cpu-baseline"]
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
     _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "5", "--warmup", "2"], 180)
     _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "5", "--warmup", "2"], 180)
+    _rocprof(["--pmc", *VALU_COUNTERS], os.path.join(raw, "valu"), base + ["--steps", "5", "--warmup", "2"], 180)
 
     stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
     ours = [r for r in stats if _ours(r["Name"])]
@@ -208,6 +266,9 @@ def collect_profiles(workload: str) -> int:
     wk, wc, nwk, nwc = counter("write", "WRITE_SIZE")
     fscale, wscale = copy_kib / fc, copy_kib / wc
     traffic = (fk * fscale + wk * wscale) * 1024.0
+    valu = {c: counter("valu", c)[0] for c in VALU_COUNTERS}
+    kernel_ns = float(ours[0]["AverageNs"]) if ours else float("nan")
+    vr = valu_roofline(valu["SQ_INSTS_VALU"], valu["SQ_INSTS_VALU_TRANS_F32"], kernel_ns)
     b = " ".join(base)
     lines = [
         f"# rocprofv3 summary: persistent cross-entropy row kernel, workload {workload}",
@@ -217,8 +278,12 @@ def collect_profiles(workload: str) -> int:
         f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 10 --warmup 3",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <raw>/fetch -o run -- python bench.py {b} --steps 5 --warmup 2",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <raw>/write -o run -- python bench.py {b} --steps 5 --warmup 2",
+        f"#   rocprofv3 --pmc {' '.join(VALU_COUNTERS)} -f csv -d <raw>/valu -o run -- python bench.py {b} "
+        "--steps 5 --warmup 2",
         "# Counter scale: what each counter reads for the plain copy (__amd_rocclr_copyBuffer) of the",
         f"# pristine logits -- a known {copy_kib:.0f} KiB read + {copy_kib:.0f} KiB write -- divided into that size.",
+        "# VALU roofline: wave64 VALU instructions issue at one per CU per clock (4 SIMDs x 16 lanes),",
+        "# transcendentals (exp, rcp, log) at half of that (measured on the device); 256 CUs at 2.4 GHz.",
         "#",
         "# kernel trace (--stats), nanoseconds:",
     ]
@@ -236,6 +301,12 @@ def collect_profiles(workload: str) -> int:
         f"write_scale: {wscale:.4f}",
         f"traffic_bytes_per_dispatch: {traffic:.0f}",
         f"algorithmic_bytes_per_dispatch: {algorithmic_bytes(w)}",
+        f"valu_insts_per_dispatch: {valu['SQ_INSTS_VALU']:.0f}",
+        f"valu_trans_f32_insts_per_dispatch: {valu['SQ_INSTS_VALU_TRANS_F32']:.0f}",
+        f"valu_busy_pct: {valu['VALUBusy']:.1f}",
+        f"grbm_gui_active_per_dispatch: {valu['GRBM_GUI_ACTIVE']:.0f}",
+        f"valu_issue_bound_ns: {vr['bound_ns']:.1f}",
+        f"valu_roofline_frac: {vr['frac']:.4f}",
         f"kernel_source_sha256_16: {kernel_source_hash(workload)}",
     ]
     os.makedirs(PROFILES, exist_ok=True)
@@ -300,8 +371,12 @@ def bench_flce(args, w) -> int:
     grad_hidden = torch.empty((w.n, w.H), dtype=torch.bfloat16, device=dev)
     grad_weight = torch.empty((w.V, w.H), dtype=torch.float32, device=dev)
     counts = torch.empty(3, dtype=torch.int64, device=dev)
-    wsb = lce.lce_flce_workspace_bytes(w.n, w.H, w.V, w.chunk)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    nchunks = -(-w.n // w.chunk)
+    default_wsb = lce.lce_flce_workspace_bytes(w.n, w.H, w.V, w.chunk)
+    wsb = {"default": default_wsb, "wt": default_wsb + (2 * w.H * w.V + 255) // 256 * 256,
+           "lean": lce.lce_flce_workspace_bytes_grouped(w.n, w.H, w.V, w.chunk, 1)}[args.flce_workspace]
+    del nchunks
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     resident = args.path == "resident"
     if resident:
@@ -329,6 +404,13 @@ def bench_flce(args, w) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # device memory a step allocates beyond what the caller already holds (inputs, outputs, workspace):
+    # the binding allocates nothing when every buffer is passed, so this is expected to be 0
+    base_alloc = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    step()
+    torch.cuda.synchronize()
+    step_extra = torch.cuda.max_memory_allocated(dev) - base_alloc
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -364,7 +446,15 @@ def bench_flce(args, w) -> int:
         "config": {"workload": w.name, "n": w.n, "H": w.H, "V": w.V, "chunk_tokens": w.chunk,
                    "hidden_scale": w.hidden_scale, "w_sigma": w.w_sigma, "ignore_frac": w.ignore_frac,
                    "softcap": w.softcap, "label_smoothing": w.label_smoothing, "reduction": w.reduction,
-                   "workspace_bytes": wsb, "parallelism": "none (1 GPU)"},
+                   "workspace_layout": args.flce_workspace, "workspace_bytes": wsb, "parallelism": "none (1 GPU)"},
+        "memory": {"extra_device_bytes": wsb + (int(stats_ws.numel()) + 6 * 4 * w.n if resident else 0),
+                   "workspace_bytes": wsb,
+                   "forward_stats_bytes": int(stats_ws.numel()) if resident else 0,
+                   "allocated_by_the_step_bytes": int(step_extra),
+                   "bf16_logits_bytes_for_comparison": 2 * w.n * w.V,
+                   "grad_weight_fp32_bytes": 4 * w.V * w.H,
+                   "note": "extra device memory beyond the inputs (hidden, weight, labels) and the outputs "
+                           "(grad_hidden, fp32 grad_weight, losses, counts)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": ("lce_flce_forward + lce_flce_backward" if resident else "lce_flce_fwd_bwd call") +
@@ -397,6 +487,8 @@ def collect_profiles_flce(workload: str, resident: bool = False) -> int:
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "3", "--warmup", "1"], 600)
     _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "1", "--warmup", "1"], 600)
     _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "1", "--warmup", "1"], 600)
+    _rocprof(["--pmc", "TCC_HIT_sum", "TCC_MISS_sum"], os.path.join(raw, "l2"), base + ["--steps", "1", "--warmup", "1"],
+             600)
     stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
     calls = 4   # warmup + steps of the trace run
     ref_kib = (256 << 20) * 4 / 1024.0
@@ -415,6 +507,22 @@ def collect_profiles_flce(workload: str, resident: bool = False) -> int:
     wk, wc, nwk = counter("write", "WRITE_SIZE")
     fscale, wscale = ref_kib / fc, ref_kib / wc
     traffic = (fk * fscale + wk * wscale) * 1024.0
+
+    def per_gemm(sub: str, cname: str) -> dict:
+        """Counter per GEMM launch kind (the kernel's template arguments name its output mode), averaged
+        over that kind's launches."""
+        rows = [r for r in csv.DictReader(open(os.path.join(raw, sub, "run_counter_collection.csv")))
+                if r["Counter_Name"] == cname and "gemm_nt_kernel" in r["Kernel_Name"]]
+        acc = {}
+        for r in rows:
+            key = r["Kernel_Name"].split("(")[0].replace("void lce::gemm::", "")
+            tot, cnt = acc.get(key, (0.0, 0))
+            acc[key] = (tot + float(r["Counter_Value"]), cnt + 1)
+        return {k: (t / c, c) for k, (t, c) in acc.items()}
+
+    gemm_fetch = per_gemm("fetch", "FETCH_SIZE")
+    gemm_hit = per_gemm("l2", "TCC_HIT_sum")
+    gemm_miss = per_gemm("l2", "TCC_MISS_sum")
     b = " ".join(base)
     total_ns = sum(float(r["TotalDurationNs"]) for r in stats if any(o in r["Name"] for o in ours)) / calls
     what = ("tile-resident fused linear cross-entropy (lce_flce_forward + lce_flce_backward)" if resident
@@ -427,6 +535,8 @@ def collect_profiles_flce(workload: str, resident: bool = False) -> int:
         f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 3 --warmup 1",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <raw>/fetch -o run -- python bench.py {b} --steps 1 --warmup 1",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <raw>/write -o run -- python bench.py {b} --steps 1 --warmup 1",
+        f"#   rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum -f csv -d <raw>/l2 -o run -- python bench.py {b} --steps 1 "
+        "--warmup 1",
         "# Counter scale: what each counter reads for a plain 1 GiB device copy (__amd_rocclr_copyBuffer)",
         "# made once before timing, divided into its known size.  Traffic is per step (one call, or",
         "# forward + backward), summed over all of its kernels.",
@@ -459,8 +569,16 @@ def collect_profiles_flce(workload: str, resident: bool = False) -> int:
         f"write_scale: {wscale:.4f}",
         f"traffic_bytes_per_dispatch: {traffic:.0f}",
         f"algorithmic_flops_per_call: {flce_flops(w)}",
-        f"kernel_source_sha256_16: {kernel_source_hash(workload)}",
+        "# per GEMM launch kind (averaged over its launches): duration, FETCH_SIZE scaled to bytes, L2 hits / misses",
     ]
+    for r in gemm:
+        key = r["Name"].split("(")[0].replace("void lce::gemm::", "")
+        f_kib = gemm_fetch.get(key, (float("nan"), 0))[0]
+        hit, miss = gemm_hit.get(key, (float("nan"), 0))[0], gemm_miss.get(key, (float("nan"), 0))[0]
+        lines.append(f"gemm: {key}  avg_ns {float(r['AverageNs']):.0f}  calls {r['Calls']}  "
+                     f"fetch_bytes {f_kib * fscale * 1024.0:.4g}  l2_hit {hit:.4g}  l2_miss {miss:.4g}  "
+                     f"l2_hit_rate {hit / (hit + miss) if hit + miss > 0 else float('nan'):.3f}")
+    lines.append(f"kernel_source_sha256_16: {kernel_source_hash(workload)}")
     os.makedirs(PROFILES, exist_ok=True)
     with open(profile_path(workload, resident), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -610,7 +728,7 @@ def collect_profiles_split(workload: str, tp: int) -> int:
     """Kernel trace of the split path's three kernels (stats per shard, combine, gradient per shard),
     then FETCH_SIZE and WRITE_SIZE of every kernel a step launches, scaled like the fused path's."""
     import synth
-    w = synth.WORKLOADS[workload]
+    w = synth.ALL_CE_WORKLOADS[workload]
     raw = os.path.join(RAW_PROFILES, f"{workload}_split_tp{tp}")
     os.makedirs(raw, exist_ok=True)
     base = ["--workload", workload, "--no-cpu-baseline", "--path", "split", "--tp", str(tp)]
@@ -684,14 +802,14 @@ def main() -> int:
     if args.workload in synth.FLCE_WORKLOADS:
         return bench_flce(args, synth.FLCE_WORKLOADS[args.workload])
     if args.path == "split":
-        return bench_split(args, synth.WORKLOADS[args.workload])
+        return bench_split(args, synth.ALL_CE_WORKLOADS[args.workload])
 
     import numpy as np
     import torch
 
     import vocabulary_cross_entropy_row_amd as lce
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.ALL_CE_WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     y = synth.labels(w)
@@ -752,6 +870,7 @@ def main() -> int:
         b_.record(stream)
     torch.cuda.synchronize()
     copy_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in cev]))
+    pages = None if args.no_pages_protocol else pages_protocol(step, bufs[0], pristine, stream, dev)
 
     nbytes = algorithmic_bytes(w)
     prof = read_profile(w.name)
@@ -787,6 +906,15 @@ def main() -> int:
                      "workspace_bytes": int(ws.numel())},
         "cpu_baseline": None,
     }
+    if pages is not None:
+        pages["GBps_at_median"] = round(nbytes / (pages["median_ms"] * 1e-3) / 1e9, 1)
+        pages["frac_at_median"] = round(nbytes / (pages["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        out["pages_protocol"] = pages
+    if prof and traffic is not None and "valu_roofline_frac" in prof:
+        out["valu"] = {"bound": "alu", "issue_bound_ms": round(float(prof["valu_issue_bound_ns"]) * 1e-6, 5),
+                       "kernel_ms_rocprof": round(float(prof["kernel_avg_ns"]) * 1e-6, 5),
+                       "frac": float(prof["valu_roofline_frac"]), "valu_busy_pct": float(prof["valu_busy_pct"]),
+                       "source": os.path.relpath(profile_path(w.name), ROOT)}
     if w.n == 2048 and w.V == 131072 and w.dtype == "bf16":
         out["context_other_hardware"] = H100_CONTEXT
     if not args.no_cpu_baseline:

@@ -213,13 +213,16 @@ lce_status lce_ce_grad(void *logits_inout, int64_t ld, lce_dtype dtype, const in
 
 /*
  * Bytes of device workspace lce_flce_fwd_bwd uses by default (0 for invalid
- * sizes), the fastest layout.  It holds W^T [H, V] bf16 (so that the
- * grad_hidden GEMM reads W K-contiguous), one chunk of logits [C, V], split-K
- * partials [16, C, H] fp32, and the transposed gradients and hidden states of
- * one grad_weight group, [V + H, G] bf16: about 2 H V + 2 C V + 64 C H +
- * 2 (V + H) G bytes with C = min(chunk, n).  The default group G is as many chunks as
- * 2 GiB holds (at least one, at most all n tokens); grad_weight is written once
- * per group, so fewer groups mean less grad_weight traffic.
+ * sizes).  It holds one chunk of logits [C, V] bf16, split-K partials
+ * [16, C, H] fp32, and the transposed gradients and hidden states of one
+ * grad_weight group, [V + H, G] bf16: about 2 C V + 64 C H + 2 (V + H) G bytes
+ * with C = min(chunk, n).  The default group G is as many chunks as 2 GiB
+ * holds (at least one, at most all n tokens); grad_weight is written once per
+ * group, so fewer groups mean less grad_weight traffic.  A workspace larger by
+ * 2 H V bytes (rounded up to 256) also holds W^T [H, V], which the call then
+ * uses so that the grad_hidden GEMM reads W K-contiguous; at the fused-linear
+ * workload (4096 x 6656 x 202048) that measured no faster overall (the W^T
+ * transpose costs what the GEMM saves), so the default leaves it out.
  */
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens);
 

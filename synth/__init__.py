@@ -81,6 +81,17 @@ C5_SMALL = FLCEWorkload("flce_bf16_256x512x8192", 1005, 256, 512, 8192, 0.5, 0.0
 WORKLOADS = {w.name: w for w in (C1, C2, C3, C4)}
 FLCE_WORKLOADS = {w.name: w for w in (C5, C5_SMALL)}
 
+# The vocabulary sweep of the cross-entropy op (bench only): sequence 2048 x batch 4 tokens over
+# vocabularies from 4K to 128K (the Liger CE micro-bench's setup), one vocabulary-parallel rank's
+# shard of the 128K vocabulary at 8 ranks ([2048, 16384]), and an odd vocabulary (50257, the GPT-2
+# tokenizer's size) that only the generic kernel takes.  sigma 2, 5% ignored, mean reduction.
+SWEEP = {w.name: w for w in (
+    [CEWorkload(f"ce_bf16_8192x{v}", 1100 + i, 8192, v, "bf16", 2.0, 0.05)
+     for i, v in enumerate((4096, 16384, 32768, 65536, 131072))]
+    + [CEWorkload("ce_bf16_2048x16384", 1110, 2048, 16384, "bf16", 2.0, 0.05),
+       CEWorkload("ce_bf16_2048x50257", 1111, 2048, 50257, "bf16", 2.0, 0.05)])}
+ALL_CE_WORKLOADS = {**WORKLOADS, **SWEEP}
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""

@@ -141,6 +141,25 @@ def test_small_matrix(n, V, ld, dt, feat):
     run_and_check(x, y, V, **kw)
 
 
+# (n, V, dtype): the short-row kernel's families at their capacity and one vector past it, where the
+# next family (or the long-row kernel) takes over; 300 rows leave a partial last row set
+SHORT_ROWS = [
+    (300, 2048, "bf16"), (300, 4096, "bf16"), (300, 4104, "bf16"), (300, 8192, "bf16"), (300, 8200, "bf16"),
+    (300, 16384, "bf16"), (300, 16392, "bf16"), (300, 2048, "f32"), (300, 4096, "f32"), (300, 8192, "f32"),
+    (300, 8196, "f32"), (1000, 64, "bf16"), (37, 520, "f32"),
+]
+
+
+@pytest.mark.parametrize("n,V,dt", SHORT_ROWS, ids=[f"{s[0]}x{s[1]}{s[2]}" for s in SHORT_ROWS])
+@pytest.mark.parametrize("feat", ["plain", "all"])
+def test_short_row_families(n, V, dt, feat):
+    rng = np.random.default_rng([n, V, len(dt), len(feat)])
+    x = make_logits(rng, n, V, V, dt, sigma=4.0)
+    y = _labels(rng, n, V, bad=2 if feat == "all" else 0)
+    kw = dict(plain=dict(), all=dict(eps=0.2, T=30.0, red="none", grad_out=rng.normal(size=n), want_argmax=True))[feat]
+    run_and_check(x, y, V, **kw)
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 def test_c1_full():
@@ -355,13 +374,14 @@ STALE_WORD = (0xFEDCBA98 << 32) | 700
 
 
 @pytest.mark.parametrize("want_argmax", [False, True], ids=["plain", "argmax"])
-def test_workspace_contents_do_not_matter(want_argmax):
+@pytest.mark.parametrize("V", [32768, 4096], ids=["long-rows", "short-rows"])
+def test_workspace_contents_do_not_matter(want_argmax, V):
     """The workspace's counters carry the tag of the launch that set them, so a workspace full of
     0xFF bytes, of random bytes, or holding the counters of a call that never finished gives
-    bitwise the results of a zeroed one (1024 rows: every workgroup draws rows, and 10 % ignored
-    rows make the zeroing chunks run)."""
+    bitwise the results of a zeroed one (1024 rows: every workgroup of the long-row kernel draws
+    rows, and 10 % ignored rows make the zeroing chunks run; at V = 4096 the short-row kernel)."""
     rng = np.random.default_rng(12)
-    n, V = 1024, 32768
+    n = 1024
     x = make_logits(rng, n, V, V, "bf16")
     y = _labels(rng, n, V)
     wsb = lce.lce_ce_workspace_bytes(n, V)

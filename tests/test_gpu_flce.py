@@ -152,20 +152,27 @@ def test_flce_grad_weight_groups(group_chunks):
     assert torch.equal(grouped.grad_hidden, one_pass.grad_hidden)
 
 
+def wt_workspace_bytes(n, H, V, chunk):
+    """The default workspace plus room for W^T (2 H V bytes, rounded up to 256)."""
+    return lce.lce_flce_workspace_bytes(n, H, V, chunk) + (2 * H * V + 255) // 256 * 256
+
+
 @pytest.mark.parametrize("n,H,V", [(300, 520, 1000), (130, 136, 4104)])
 def test_flce_weight_read_in_place(n, H, V):
-    """A workspace without room for W^T makes the grad_hidden GEMM read W in place (k-major operand,
-    transposing LDS reads): the same eight k values reach every lane in the same order, so grad_hidden is
-    bitwise that of the W^T path, and everything matches the oracle."""
+    """The default workspace has no room for W^T, so the grad_hidden GEMM reads W in place (k-major
+    operand, transposing LDS reads); a workspace with room for W^T reads it K-contiguous instead.  The
+    same eight k values reach every lane in the same order, so the results are bitwise equal, and
+    match the oracle."""
     hb, wb, y = gen(n, H, V, seed=n + V)
-    chunks = -(-n // 64)
-    _, o, _, _ = check_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64, group_chunks=chunks)
-    in_place = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64, group_chunks=chunks)
-    with_wt = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64)
-    assert lce.lce_flce_workspace_bytes(n, H, V, 64) - lce.lce_flce_workspace_bytes_grouped(n, H, V, 64, chunks) \
-        >= H * V * 2
+    _, o, _, _ = check_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64)
+    in_place = run_flce(hb, wb, y, eps=0.1, T=30.0, chunk=64)
+    ws = torch.empty(wt_workspace_bytes(n, H, V, 64), dtype=torch.uint8, device=DEV)
+    with_wt = lce.lce_flce_fwd_bwd(bf16_tensor(hb), bf16_tensor(wb), torch.from_numpy(y).to(DEV), label_smoothing=0.1,
+                                   softcap=30.0, chunk_tokens=64, workspace=ws)
+    torch.cuda.synchronize()
     assert torch.equal(in_place.grad_hidden, with_wt.grad_hidden)
     assert torch.equal(in_place.grad_weight, with_wt.grad_weight)
+    assert torch.equal(in_place.loss_tok, with_wt.loss_tok)
 
 
 def test_flce_chunk_invariance():

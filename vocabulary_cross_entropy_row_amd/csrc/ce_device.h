@@ -111,6 +111,18 @@ __device__ __forceinline__ unsigned tagged_draw(unsigned long long *w, unsigned 
     return tagged_count(w, tagged_inc(w), tag);
 }
 
+// Word 3 of a gfx9-family buffer descriptor: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy bit of buffer loads/stores: non-temporal (streamed once).
+constexpr int kNonTemporal = 2;
+
+// A store performed at memory (system scope): another workgroup, on any XCD,
+// reads it past its own L2.
+__device__ __forceinline__ void store_through(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Row-kernel workspace: the completion counter at byte 0, the row counter at
 // byte 64, the counter of the ignored-row chunks at byte 128 (tagged words, one
 // per 64-byte line), int64 n_correct partials of the workgroups from byte 256.

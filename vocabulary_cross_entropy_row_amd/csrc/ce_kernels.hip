@@ -303,6 +303,35 @@ hipError_t launch_generic(const CEArgs &a, hipStream_t st) {
 LCE_FAMILIES(LCE_DECL)
 #undef LCE_DECL
 
+// Short-row families compiled from ce_rows_mr.hip: (waves per row, vectors per lane).
+#define LCE_MR_FAMILIES(X) X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 8) X(4, 8) X(4, 16)
+#define LCE_MR_DECL(p, kv)                                                          \
+    hipError_t launch_rows_mr_0_##p##_##kv(const CEArgs &, int, hipStream_t);      \
+    hipError_t launch_rows_mr_1_##p##_##kv(const CEArgs &, int, hipStream_t);
+LCE_MR_FAMILIES(LCE_MR_DECL)
+#undef LCE_MR_DECL
+
+// Rows of at most this many 16-byte vectors go to the short-row kernel.
+constexpr int64_t kMrMaxVectors = 2048;
+
+bool ce_short_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *p, int *kv) {
+    const int E = is_bf16 ? 8 : 4;
+    if (V % E != 0 || ld % E != 0) return false;
+    if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0) return false;
+    const int64_t nvec = V / E;
+    if (nvec > kMrMaxVectors) return false;
+#define LCE_MR_ENTRY(a, b) {a, b},
+    static const int fam[][2] = {LCE_MR_FAMILIES(LCE_MR_ENTRY)};   // in increasing capacity
+#undef LCE_MR_ENTRY
+    for (const auto &f : fam)
+        if (64 * f[0] * f[1] >= nvec) {
+            *p = f[0];
+            *kv = f[1];
+            return true;
+        }
+    return false;
+}
+
 bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl) {
     const int E = is_bf16 ? 8 : 4;
     if (V % E != 0 || ld % E != 0) return false;
@@ -344,8 +373,22 @@ hipError_t launch_resident(const CEArgs &a, bool bf16, int kr, int kl, hipStream
 }
 }  // namespace
 
+hipError_t launch_short(const CEArgs &a, bool bf16, int p, int kv, hipStream_t st) {
+    const int cus = device_cu_count();
+#define LCE_MR_CASE(pp, kk)                                                                                  \
+    if (p == pp && kv == kk)                                                                                 \
+        return bf16 ? launch_rows_mr_1_##pp##_##kk(a, cus, st) : launch_rows_mr_0_##pp##_##kk(a, cus, st);
+    LCE_MR_FAMILIES(LCE_MR_CASE)
+#undef LCE_MR_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream) {
-    int kr = 0, kl = 0;
+    int kr = 0, kl = 0, p = 0, kv = 0;
+    if (a.n > 0 && ce_short_plan(a.logits, a.ld, is_bf16, a.V, &p, &kv)) {
+        // one launch: the short-row kernel counts labels and reduces on its own
+        return launch_short(a, is_bf16, p, kv, stream);
+    }
     if (a.n > 0 && ce_resident_plan(a.logits, a.ld, is_bf16, a.V, &kr, &kl)) {
         // one launch: the persistent kernel counts labels and reduces on its own
         return launch_resident(a, is_bf16, kr, kl, stream);

@@ -47,20 +47,12 @@ constexpr int kSkipMax = 16;
 // Rows per chunk of the end-of-call pass that zeroes ignored rows.
 constexpr int kZeroChunk = 64;
 
-// Word 3 of a gfx9-family buffer descriptor: 32-bit data format, no swizzle.
-constexpr int kBufferWord3 = 0x00020000;
-// Cache-policy bit of buffer loads/stores: non-temporal (streamed once).
-constexpr int kNonTemporal = 2;
 
 // Row draws and the final fold's operands go through system-scope atomics:
 // they are performed at, or written through to, memory, so workgroups on
 // different XCDs (each with its own L2) see each other's values without a
 // cache-wide writeback or invalidate.
 
-__device__ __forceinline__ void store_through(float *p, float v) {
-    __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
-}
 
 template <bool BF16, int KR, int KL, bool SOFTCAP, bool ARGMAX, bool SMOOTH>
 __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {

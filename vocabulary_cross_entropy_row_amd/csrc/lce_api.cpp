@@ -327,7 +327,7 @@ lce_status lce_ce_grad(void *logits_inout, int64_t ld, lce_dtype dtype, const in
 
 size_t lce_flce_workspace_bytes(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens) {
     if (n < 0 || H < 1 || V < 1 || chunk_tokens < 1) return 0;
-    return lce::flce_layout(n, H, V, chunk_tokens, lce::flce_default_group_chunks(n, H, V, chunk_tokens), true).bytes;
+    return lce::flce_layout(n, H, V, chunk_tokens, lce::flce_default_group_chunks(n, H, V, chunk_tokens), false).bytes;
 }
 
 size_t lce_flce_workspace_bytes_grouped(int64_t n, int64_t H, int64_t V, int64_t chunk_tokens, int64_t group_chunks) {
