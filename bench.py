@@ -616,6 +616,9 @@ def bench_split(args, w) -> int:
     ws = w.V // tp
     stats = torch.empty((tp, w.n, 8), dtype=torch.float32, device=dev)
     grad_out = torch.full((1,), w.grad_out, dtype=torch.float32, device=dev)
+    fv = lambda: torch.empty(w.n, dtype=torch.float32, device=dev)  # noqa: E731
+    rows_out = lce.SplitRows(fv(), fv(), fv(), torch.empty(1, dtype=torch.float32, device=dev), fv(), fv(),
+                             torch.empty(w.n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
     stream = torch.cuda.current_stream()
     ev = {k: [] for k in ("stats", "combine", "grad")}
 
@@ -628,7 +631,7 @@ def bench_split(args, w) -> int:
                              stream=stream)
         mark(1)
         rows = lce.lce_ce_combine(stats, labels, w.V, label_smoothing=w.label_smoothing, reduction=w.reduction,
-                                  stream=stream)
+                                  out=rows_out, stream=stream)
         mark(2)
         for k in range(tp):
             lce.lce_ce_grad(buf[:, k * ws:(k + 1) * ws], labels, w.V, rows, v_offset=k * ws,

@@ -370,9 +370,9 @@ class SplitRows:
 
 @_on_call_stream
 def lce_ce_combine(stats, labels, V: int, *, ignore_index: int = -100, label_smoothing: float = 0.0,
-                   reduction: str = "mean", stream=None) -> SplitRows:
+                   reduction: str = "mean", out: SplitRows | None = None, stream=None) -> SplitRows:
     """Row results from the stats of all shards: ``stats`` is fp32 [shards, n, 8] (or [n, 8] for one),
-    shards in ascending vocabulary order."""
+    shards in ascending vocabulary order.  ``out`` (optional) supplies the output tensors."""
     import torch
     if stats.dim() == 2:
         stats = stats.unsqueeze(0)
@@ -381,9 +381,16 @@ def lce_ce_combine(stats, labels, V: int, *, ignore_index: int = -100, label_smo
     shards, n = stats.shape[0], stats.shape[1]
     dev = _on_gpu(stats, "stats")
     _buf(labels, "labels", torch.int64, n, dev, required=True)
-    f = lambda: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
-    out = SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=dev), f(), f(),
-                    torch.empty(n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
+    if out is None:
+        f = lambda: torch.empty(n, dtype=torch.float32, device=dev)  # noqa: E731
+        out = SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=dev), f(), f(),
+                        torch.empty(n, dtype=torch.int64, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
+    for name in ("lse", "one_minus_py", "loss_tok", "logprob", "entropy"):
+        _buf(getattr(out, name), f"out.{name}", torch.float32, n, dev)
+    _buf(out.lse, "out.lse", torch.float32, n, dev, required=True)
+    _buf(out.loss_out, "out.loss_out", torch.float32, 1, dev)
+    _buf(out.argmax, "out.argmax", torch.int64, n, dev)
+    _buf(out.counts, "out.counts", torch.int64, 3, dev, required=True)
     _check(lib().lce_ce_combine(_ptr(stats), shards, _ptr(labels), n, int(V), int(ignore_index),
                                 float(label_smoothing), REDUCTIONS[reduction], _ptr(out.lse), _ptr(out.one_minus_py),
                                 _ptr(out.loss_tok), _ptr(out.loss_out), _ptr(out.logprob), _ptr(out.entropy),

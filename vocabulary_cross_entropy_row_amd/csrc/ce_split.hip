@@ -272,6 +272,103 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The whole combine in one workgroup, for up to kCombineOneMaxRows rows of a
+// few shards: row outputs, label counts, n_correct and the reduced loss, with
+// no atomics and no second launch.  Thread t takes rows t, t + 1024, ...; the
+// counts and the fp64 loss sum fold over the threads in a fixed order.
+constexpr int kCombineOneThreads = 1024;
+constexpr int64_t kCombineOneMaxRows = 16384;
+__global__ __launch_bounds__(kCombineOneThreads) void ce_combine_one_kernel(
+    const float *stats, int64_t shards, int64_t shard_stride, int64_t row_stride, const int64_t *labels, int64_t n,
+    int64_t V, int64_t ignore_index, float eps, int reduction, float *lse_out, float *q_out, float *loss_tok,
+    float *loss_out, float *logp_out, float *ent_out, int64_t *argmax_out, int64_t *counts) {
+    constexpr int NW = kCombineOneThreads / 64;
+    __shared__ double sh_d[NW];
+    __shared__ long long sh_c[3][NW];
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    long long nv = 0, nc = 0, nb = 0;
+    for (int64_t i = tid; i < n; i += kCombineOneThreads) {
+        Part t;
+        float zy = 0.0f;
+        bool has = false;
+        int64_t am = -1;
+        const float4 *rec = reinterpret_cast<const float4 *>(stats + i * row_stride * 8);
+        const int64_t step = shard_stride * 2;   // float4s per shard
+        const int64_t y = labels[i];
+        // eight shards' records in flight at a time (clamped to the last shard), merged in order
+        constexpr int kBatch = 8;
+        for (int64_t k0 = 0; k0 < shards; k0 += kBatch) {
+            float4 ra[kBatch], rb[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t k = k0 + u < shards ? k0 + u : shards - 1;
+                ra[u] = rec[k * step];
+                rb[u] = rec[k * step + 1];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (k0 + u >= shards) break;
+                combine(t, ra[u].x, ra[u].y, ra[u].z);
+                t.zs += ra[u].w;
+                if (rb[u].x > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
+                    t.amv = rb[u].x;
+                    am = __float_as_int(rb[u].y);
+                }
+                if (rb[u].w != 0.0f) {
+                    zy = rb[u].z;
+                    has = true;
+                }
+            }
+        }
+        const bool valid = y != ignore_index && y >= 0 && y < V;
+        if (y != ignore_index) {
+            if (valid) ++nv;
+            else ++nb;
+        }
+        const float ey = has ? dev::exp2_fast((zy - t.m) * kLog2e) : 0.0f;
+        const float S = t.s + ey;
+        const float lse = t.m + logf(S);
+        const float loss = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
+        lse_out[i] = lse;
+        if (q_out) q_out[i] = valid ? t.s / S : 0.0f;
+        if (loss_tok) loss_tok[i] = loss;
+        if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
+        if (ent_out) ent_out[i] = lse - fmaf(ey, zy, t.e) / S;
+        if (argmax_out) argmax_out[i] = am;
+        if (valid && am == y) ++nc;
+        acc += static_cast<double>(loss);
+    }
+    acc = dev::wave_sum_d(acc);
+    nv = dev::wave_sum_ll(nv);
+    nc = dev::wave_sum_ll(nc);
+    nb = dev::wave_sum_ll(nb);
+    if ((tid & 63) == 0) {
+        sh_d[tid >> 6] = acc;
+        sh_c[0][tid >> 6] = nv;
+        sh_c[1][tid >> 6] = nc;
+        sh_c[2][tid >> 6] = nb;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        long long c[3] = {0, 0, 0};
+        for (int w = 0; w < NW; ++w) {
+            tot += sh_d[w];
+            for (int j = 0; j < 3; ++j) c[j] += sh_c[j][w];
+        }
+        counts[0] = c[0];
+        counts[1] = c[1];
+        counts[2] = c[2];
+        if (loss_out) {
+            float out = 0.0f;
+            if (reduction == 1) out = c[0] > 0 ? static_cast<float>(tot / static_cast<double>(c[0])) : 0.0f;
+            else if (reduction == 2) out = static_cast<float>(tot);
+            *loss_out = out;
+        }
+    }
+}
+
 // Many shards per row (one per 256 columns in the tile-resident fused linear
 // path): one wave per row, each lane merges every 64th shard in ascending
 // order, then a butterfly merges the lanes (argmax ties to the smaller index).
@@ -325,7 +422,7 @@ __global__ __launch_bounds__(256) void ce_combine_wide_kernel(const float *stats
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool BF16, bool SOFTCAP, bool SMOOTH>
+template <bool BF16, bool SOFTCAP, bool SMOOTH, int PER>   // PER: 16-byte vectors per thread
 __global__ __launch_bounds__(256) void ce_grad_kernel(void *logits, int64_t ld, int64_t Vs, int64_t v0, int64_t V,
                                                       const int64_t *labels, int64_t ignore_index, float eps,
                                                       float softcap, int reduction, const float *grad_out,
@@ -333,7 +430,6 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(void *logits, int64_t ld, 
                                                       int blocks_per_row) {
     using EL = Elt<BF16>;
     constexpr int E = EL::E;
-    constexpr int PER = 4;   // vectors per thread
     const int64_t row = blockIdx.x / blocks_per_row;
     const int part = blockIdx.x % blocks_per_row;
     const int nvec = static_cast<int>(Vs / E);
@@ -425,6 +521,13 @@ hipError_t launch_ce_combine(const float *stats, int64_t shards, int64_t shard_s
                              float *q, float *loss_tok, float *loss_out, float *logp, float *ent,
                              int64_t *argmax_out, int64_t *counts, hipStream_t st) {
     hipError_t e;
+    if (shards <= 16 && n <= kCombineOneMaxRows) {
+        // one launch does everything (n == 0 included: counts and loss_out become 0)
+        hipLaunchKernelGGL(ce_combine_one_kernel, dim3(1), dim3(kCombineOneThreads), 0, st, stats, shards,
+                           shard_stride, row_stride, labels, n, V, ignore_index, eps, reduction, lse, q, loss_tok,
+                           loss_out, logp, ent, argmax_out, counts);
+        return hipGetLastError();
+    }
     // counts {n_valid, 0, n_bad}; n_correct is added below
     if ((e = launch_ce_count(labels, n, V, ignore_index, counts, nullptr, loss_out, st)) != hipSuccess) return e;
     if (n > 0 && shards > 16) {
@@ -449,12 +552,22 @@ hipError_t launch_ce_grad(void *logits, int64_t ld, bool is_bf16, const int64_t 
     if (n == 0) return hipSuccess;
     const int E = is_bf16 ? 8 : 4;
     const int64_t nvec = Vs / E;
-    const int bpr = static_cast<int>((nvec + 256 * 4 - 1) / (256 * 4));
+    // eight vectors per thread on long shards (fewer, larger workgroups: measured faster at 16384
+    // vectors, slower at 2048), else four
+    const bool wide = nvec >= 8192;
+    const int per = wide ? 8 : 4;
+    const int bpr = static_cast<int>((nvec + 256 * per - 1) / (256 * per));
     const dim3 grid(static_cast<unsigned>(n * bpr)), block(256);
     const bool sc = softcap > 0.0f, sm = eps != 0.0f;
-#define LCE_GRAD(B, S, M)                                                                                        \
-    hipLaunchKernelGGL((ce_grad_kernel<B, S, M>), grid, block, 0, st, logits, ld, Vs, v0, V, labels, ignore_index, \
-                       eps, softcap, reduction, grad_out, lse, q, counts, bpr)
+#define LCE_GRAD(B, S, M)                                                                                          \
+    do {                                                                                                           \
+        if (wide)                                                                                                  \
+            hipLaunchKernelGGL((ce_grad_kernel<B, S, M, 8>), grid, block, 0, st, logits, ld, Vs, v0, V, labels,    \
+                               ignore_index, eps, softcap, reduction, grad_out, lse, q, counts, bpr);              \
+        else                                                                                                       \
+            hipLaunchKernelGGL((ce_grad_kernel<B, S, M, 4>), grid, block, 0, st, logits, ld, Vs, v0, V, labels,    \
+                               ignore_index, eps, softcap, reduction, grad_out, lse, q, counts, bpr);              \
+    } while (0)
     if (is_bf16) {
         if (sc) { if (sm) LCE_GRAD(true, true, true); else LCE_GRAD(true, true, false); }
         else { if (sm) LCE_GRAD(true, false, true); else LCE_GRAD(true, false, false); }
