@@ -65,7 +65,9 @@ def algorithmic_bytes(w) -> int:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: as many as 64 GB of pristine input copies hold, 20 to 100; "
+                         "20 for the fused-linear workloads)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ce_bf16_2048x131072")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -180,7 +182,8 @@ def pages_protocol(call, work, pristine, stream, dev, warmup: int = 10, reps: in
 
 # the sources each measured kernel is compiled from: the persistent row kernel, and for the
 # fused variant also its GEMM, transposes and driver
-CE_SOURCES = ("ce_device.h", "ce_rows.h", "ce_rows_inst.hip", "ce_rows_mr.h", "ce_rows_mr.hip", "ce_kernels.hip",
+CE_SOURCES = ("ce_device.h", "ce_rows.h", "ce_rows_inst.hip", "ce_rows_mr.h", "ce_rows_mr.hip", "ce_rows_half.h",
+              "ce_rows_half.hip", "ce_kernels.hip",
               "lce_internal.h")
 FLCE_SOURCES = CE_SOURCES + ("gemm_mfma.h", "flce.hip", "ce_split.hip")
 
@@ -803,8 +806,12 @@ def main() -> int:
         return 2
 
     if args.workload in synth.FLCE_WORKLOADS:
+        if args.steps is None:
+            args.steps = 20
         return bench_flce(args, synth.FLCE_WORKLOADS[args.workload])
     if args.path == "split":
+        if args.steps is None:
+            args.steps = 20
         return bench_split(args, synth.ALL_CE_WORKLOADS[args.workload])
 
     import numpy as np
@@ -822,6 +829,11 @@ def main() -> int:
     else:
         pristine = torch.from_numpy(x).to(dev)
     labels = torch.from_numpy(y).to(dev)
+    if args.steps is None:
+        # each timed step gets its own pristine copy; enough steps that the fixed cost of the
+        # first launch and the final synchronisation (~0.1 ms) is spread thin
+        per_buf = w.n * w.V * w.elem_bytes
+        args.steps = int(min(100, max(20, 64e9 // per_buf - args.warmup)))
     nbuf = args.warmup + args.steps
     bufs = [torch.empty_like(pristine) for _ in range(nbuf)]
     for b in bufs:

@@ -55,13 +55,17 @@ typedef enum { LCE_RED_NONE = 0, LCE_RED_MEAN = 1, LCE_RED_SUM = 2 } lce_reducti
 
 /*
  * Bytes of device workspace lce_ce_fwd_bwd needs for n rows of V columns
- * (256 + 16 * min(n, 4096); always > 0).  The workspace holds the completion
+ * (256 + 16 * min(n, 4096) rounded up to a multiple of 256, plus
+ * 128 * min(2 n, 512); always > 0).  The workspace holds the completion
  * counter of the final reduction, the counters the workgroups draw rows and
- * ignored-row chunks from, and per-workgroup partial counts.  Each counter
- * carries the tag of the launch that set it (its dispatch id), and a launch
- * that finds another tag starts the counter afresh, so the workspace needs no
- * initialisation and a call that never completed leaves nothing the next call
- * would trip over.
+ * ignored-row chunks from, per-workgroup partial counts, and the records
+ * through which the two workgroups of a pair exchange their half rows'
+ * statistics (16-byte aligned rows of 122,888 to 153,600 bf16 or 61,444 to
+ * 76,800 fp32 columns are reduced half a row per workgroup).  Each counter carries the
+ * tag of the launch that set it (its dispatch id), each record word a key of
+ * the launch and the step, and a reader clears a record it has taken, so the
+ * workspace needs no initialisation and a call that never completed leaves
+ * nothing the next call would trip over.
  */
 size_t lce_ce_workspace_bytes(int64_t n, int64_t V);
 
@@ -114,7 +118,7 @@ lce_status lce_ce_fwd_bwd(void *logits_inout, int64_t ld, lce_dtype dtype, const
  * allocate device memory (code under stream capture that may not call
  * hipMalloc, tight serving loops, harnesses that forbid allocation).  Every
  * argument, output and result is that of lce_ce_fwd_bwd; the call allocates
- * nothing.  Its workspace is a file-scope device array of 65,792 bytes (room
+ * nothing.  Its workspace is a file-scope device array of 131,328 bytes (room
  * for any n: lce_ce_workspace_bytes stops growing at n = 4096), one copy per
  * device, held until the process ends; the first call on a device looks up
  * that copy's address with the device current (hipGetSymbolAddress) and keeps

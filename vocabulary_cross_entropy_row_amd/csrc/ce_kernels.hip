@@ -311,6 +311,14 @@ LCE_FAMILIES(LCE_DECL)
 LCE_MR_FAMILIES(LCE_MR_DECL)
 #undef LCE_MR_DECL
 
+// Half-row families compiled from ce_rows_half.hip: rounds of 960 vectors per half row.
+#define LCE_HALF_FAMILIES(X) X(9) X(10)
+#define LCE_HALF_DECL(kh)                                                       \
+    hipError_t launch_rows_half_0_##kh(const CEArgs &, int, hipStream_t);      \
+    hipError_t launch_rows_half_1_##kh(const CEArgs &, int, hipStream_t);
+LCE_HALF_FAMILIES(LCE_HALF_DECL)
+#undef LCE_HALF_DECL
+
 // Rows of at most this many 16-byte vectors go to the short-row kernel.
 constexpr int64_t kMrMaxVectors = 2048;
 
@@ -349,6 +357,23 @@ bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, i
     return false;
 }
 
+bool ce_half_plan(const void *logits, int64_t ld, bool is_bf16, int64_t n, int64_t V, int *kh) {
+    const int E = is_bf16 ? 8 : 4;
+    if (V % E != 0 || ld % E != 0 || n < 1 || n > 0x7fffffffLL) return false;
+    if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0) return false;
+    const int64_t hv0 = (V / E + 1) / 2;
+    const int64_t need = (hv0 + 959) / 960;   // rounds of 960 vectors per half row
+#define LCE_HALF_ENTRY(k) k,
+    static const int fam[] = {LCE_HALF_FAMILIES(LCE_HALF_ENTRY)};
+#undef LCE_HALF_ENTRY
+    for (int f : fam)
+        if (f == need) {
+            *kh = f;
+            return true;
+        }
+    return false;
+}
+
 int device_cu_count() {
     static int cus[64] = {0};
     int d = 0;
@@ -373,6 +398,21 @@ hipError_t launch_resident(const CEArgs &a, bool bf16, int kr, int kl, hipStream
 }
 }  // namespace
 
+// The half-row kernel's grid: one 1024-thread workgroup per CU (its LDS slot
+// takes most of a CU's LDS), an even count, at most two per row.
+hipError_t launch_half(const CEArgs &a, bool bf16, int kh, hipStream_t st) {
+    int64_t g = device_cu_count() & ~1;
+    if (g > kHalfMaxGroups) g = kHalfMaxGroups;
+    if (g > 2 * a.n) g = 2 * a.n;
+    if (g < 2) g = 2;
+    const int groups = static_cast<int>(g);
+#define LCE_HALF_CASE(k) \
+    if (kh == k) return bf16 ? launch_rows_half_1_##k(a, groups, st) : launch_rows_half_0_##k(a, groups, st);
+    LCE_HALF_FAMILIES(LCE_HALF_CASE)
+#undef LCE_HALF_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_short(const CEArgs &a, bool bf16, int p, int kv, hipStream_t st) {
     const int cus = device_cu_count();
 #define LCE_MR_CASE(pp, kk)                                                                                  \
@@ -388,6 +428,11 @@ hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream) 
     if (a.n > 0 && ce_short_plan(a.logits, a.ld, is_bf16, a.V, &p, &kv)) {
         // one launch: the short-row kernel counts labels and reduces on its own
         return launch_short(a, is_bf16, p, kv, stream);
+    }
+    int kh = 0;
+    if (a.n > 0 && ce_half_plan(a.logits, a.ld, is_bf16, a.n, a.V, &kh)) {
+        // one launch: pairs of workgroups, one half row each
+        return launch_half(a, is_bf16, kh, stream);
     }
     if (a.n > 0 && ce_resident_plan(a.logits, a.ld, is_bf16, a.V, &kr, &kl)) {
         // one launch: the persistent kernel counts labels and reduces on its own

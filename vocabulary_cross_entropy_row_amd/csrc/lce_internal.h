@@ -38,9 +38,17 @@ constexpr int kMaxRegRounds = 16;
 constexpr int kMaxLdsRounds = 9;
 // Upper bound on persistent workgroups (sizes the workspace partials).
 constexpr int kMaxRowGroups = 4096;
-// Workspace: 256-byte header (completion counter) + 16 bytes per workgroup.
+// Upper bound on the half-row kernel's workgroups (two per row in flight).
+constexpr int kHalfMaxGroups = 512;
+// Workspace: 256-byte header (tagged counters) + 16 bytes per workgroup, then,
+// 256-byte aligned, two 64-byte exchange records per half-row workgroup.
+constexpr size_t ce_records_offset(int64_t n) {
+    return (256 + 16 * static_cast<size_t>(n < kMaxRowGroups ? (n > 0 ? n : 1) : kMaxRowGroups) + 255) &
+           ~static_cast<size_t>(255);
+}
 constexpr size_t ce_workspace_bytes(int64_t n) {
-    return 256 + 16 * static_cast<size_t>(n < kMaxRowGroups ? (n > 0 ? n : 1) : kMaxRowGroups);
+    return ce_records_offset(n) + 128 * static_cast<size_t>(n < kHalfMaxGroups / 2 ? 2 * (n > 0 ? n : 1)
+                                                                                      : kHalfMaxGroups);
 }
 
 // Enqueue count + row kernels.  is_bf16 selects the element type.
@@ -50,6 +58,9 @@ hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream);
 hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const int64_t *labels,
                             int64_t n, int64_t V, int64_t ignore_index, int64_t *argmax_out,
                             int64_t *counts, hipStream_t stream);
+
+// Whether a shape takes the half-row kernel, and its rounds of 960 vectors per half.
+bool ce_half_plan(const void *logits, int64_t ld, bool is_bf16, int64_t n, int64_t V, int *kh);
 
 // Which row kernel a shape takes: rounds in VGPRs (*kr) and LDS (*kl), or
 // false for the generic streaming kernel.
