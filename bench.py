@@ -225,7 +225,8 @@ def _rocprof(args: list[str], outdir: str, bench_args: list[str], timeout: int) 
 
 
 def _ours(name: str) -> bool:
-    return "ce_rows_kernel" in name or "ce_rows_mr_kernel" in name or "ce_row_generic" in name
+    return ("ce_rows_kernel" in name or "ce_rows_mr_kernel" in name or "ce_half_kernel" in name
+            or "ce_row_generic" in name)
 
 
 # VALU counters of the row kernel (one rocprofv3 pass: 3 SQ counters, one GRBM counter)
@@ -236,7 +237,7 @@ TRANS_SLOWDOWN = 2                 # transcendentals take two issue slots (measu
 
 def valu_roofline(valu_insts: float, trans_insts: float, kernel_ns: float) -> dict:
     """The time the kernel's VALU instructions need at the issue rate (one wave64 instruction per CU per
-    clock, transcendentals four times as long), and the kernel's fraction of that bound."""
+    clock, transcendentals twice as long), and the kernel's fraction of that bound."""
     cycles = (valu_insts - trans_insts) + TRANS_SLOWDOWN * trans_insts   # CU-clocks, summed over CUs
     bound_ns = cycles / CUS / CLOCK_GHZ
     return {"bound_ns": bound_ns, "frac": bound_ns / kernel_ns if kernel_ns > 0 else float("nan")}
@@ -274,7 +275,7 @@ def collect_profiles(workload: str) -> int:
     vr = valu_roofline(valu["SQ_INSTS_VALU"], valu["SQ_INSTS_VALU_TRANS_F32"], kernel_ns)
     b = " ".join(base)
     lines = [
-        f"# rocprofv3 summary: persistent cross-entropy row kernel, workload {workload}",
+        f"# rocprofv3 summary: the cross-entropy kernel of lce_ce_fwd_bwd, workload {workload}",
         f"# ({w.n} x {w.V} {w.dtype}, eps {w.label_smoothing}, softcap {w.softcap}, argmax {w.want_argmax})",
         f"# made by: python bench.py --collect-profiles --workload {workload}",
         "# which runs, from /tmp with TMPDIR=/tmp:",

@@ -21,13 +21,17 @@ ARCH = "gfx950"
 # (source, extra flags, object name).  ce_rows_inst.hip is compiled once per
 # (dtype, rounds in VGPRs, rounds in LDS) family of the resident row kernel.
 FAMILIES = [(1, 0), (2, 0), (4, 0), (8, 0), (4, 8), (8, 8), (10, 9), (13, 9), (16, 9)]
+# The families also built for rows that need not start on a 16-byte boundary.
+UA_FAMILIES = [(1, 0), (2, 0), (4, 0), (8, 0), (4, 8), (8, 8)]
 # Short-row kernel families (waves per row, 16-byte vectors per lane), ce_rows_mr.hip.
 MR_FAMILIES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 8), (4, 8), (4, 16)]
 # Half-row kernel families (rounds of 960 vectors per half row), ce_rows_half.hip.
 HALF_FAMILIES = [9, 10]
 UNITS = [("ce_kernels.hip", [], "ce_kernels"), ("flce.hip", [], "flce"), ("ce_split.hip", [], "ce_split"), ("lce_api.cpp", ["-x", "hip"], "lce_api")] + [
-    ("ce_rows_inst.hip", [f"-DLCE_BF16={b}", f"-DLCE_KR={kr}", f"-DLCE_KL={kl}"], f"ce_rows_{b}_{kr}_{kl}")
+    ("ce_rows_inst.hip", [f"-DLCE_BF16={b}", f"-DLCE_KR={kr}", f"-DLCE_KL={kl}", "-DLCE_UA=0"], f"ce_rows_{b}_{kr}_{kl}")
     for b in (1, 0) for kr, kl in FAMILIES] + [
+    ("ce_rows_inst.hip", [f"-DLCE_BF16={b}", f"-DLCE_KR={kr}", f"-DLCE_KL={kl}", "-DLCE_UA=1"], f"ce_rows_ua_{b}_{kr}_{kl}")
+    for b in (1, 0) for kr, kl in UA_FAMILIES] + [
     ("ce_rows_mr.hip", [f"-DLCE_BF16={b}", f"-DLCE_P={p}", f"-DLCE_KV={kv}"], f"ce_rows_mr_{b}_{p}_{kv}")
     for b in (1, 0) for p, kv in MR_FAMILIES] + [
     ("ce_rows_half.hip", [f"-DLCE_BF16={b}", f"-DLCE_KH={kh}"], f"ce_rows_half_{b}_{kh}")

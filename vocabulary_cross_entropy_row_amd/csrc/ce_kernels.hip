@@ -297,11 +297,19 @@ hipError_t launch_generic(const CEArgs &a, hipStream_t st) {
 
 // Resident-path families compiled from ce_rows_inst.hip: (register rounds, LDS rounds).
 #define LCE_FAMILIES(X) X(1, 0) X(2, 0) X(4, 0) X(8, 0) X(4, 8) X(8, 8) X(10, 9) X(13, 9) X(16, 9)
-#define LCE_DECL(kr, kl)                                                         \
-    hipError_t launch_rows_0_##kr##_##kl(const CEArgs &, int, hipStream_t);     \
-    hipError_t launch_rows_1_##kr##_##kl(const CEArgs &, int, hipStream_t);
+// The families also built for rows that need not start on a 16-byte boundary
+// (rows of up to 16 rounds; wider unaligned rows take the generic kernel).
+#define LCE_UA_FAMILIES(X) X(1, 0) X(2, 0) X(4, 0) X(8, 0) X(4, 8) X(8, 8)
+#define LCE_DECL(kr, kl)                                                           \
+    hipError_t launch_rows_0_0_##kr##_##kl(const CEArgs &, int, hipStream_t);     \
+    hipError_t launch_rows_0_1_##kr##_##kl(const CEArgs &, int, hipStream_t);
 LCE_FAMILIES(LCE_DECL)
 #undef LCE_DECL
+#define LCE_UA_DECL(kr, kl)                                                        \
+    hipError_t launch_rows_1_0_##kr##_##kl(const CEArgs &, int, hipStream_t);     \
+    hipError_t launch_rows_1_1_##kr##_##kl(const CEArgs &, int, hipStream_t);
+LCE_UA_FAMILIES(LCE_UA_DECL)
+#undef LCE_UA_DECL
 
 // Short-row families compiled from ce_rows_mr.hip: (waves per row, vectors per lane).
 #define LCE_MR_FAMILIES(X) X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 8) X(4, 8) X(4, 16)
@@ -340,14 +348,26 @@ bool ce_short_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int 
     return false;
 }
 
-bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl) {
+bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl, bool *ua) {
     const int E = is_bf16 ? 8 : 4;
-    if (V % E != 0 || ld % E != 0) return false;
-    if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0) return false;
-    const int64_t need = (V / E + NT - 1) / NT;   // rounds of 1024 vectors
+    // rows on 16-byte boundaries, or else read through aligned windows of up to
+    // one more vector
+    *ua = V % E != 0 || ld % E != 0 || (reinterpret_cast<uintptr_t>(logits) & 15u) != 0;
+    const int64_t nv = *ua ? (V + 2 * E - 2) / E : V / E;
+    const int64_t need = (nv + NT - 1) / NT;   // rounds of 1024 vectors
 #define LCE_FAM_ENTRY(r, l) {r, l},
-    static const int fam[][2] = {LCE_FAMILIES(LCE_FAM_ENTRY)};   // in increasing K = KR + KL
+    static const int fam[][2] = {LCE_FAMILIES(LCE_FAM_ENTRY)};        // in increasing K = KR + KL
+    static const int fam_ua[][2] = {LCE_UA_FAMILIES(LCE_FAM_ENTRY)};
 #undef LCE_FAM_ENTRY
+    if (*ua) {
+        for (const auto &f : fam_ua)
+            if (f[0] + f[1] >= need) {
+                *kr = f[0];
+                *kl = f[1];
+                return true;
+            }
+        return false;
+    }
     for (const auto &f : fam)
         if (f[0] + f[1] >= need) {
             *kr = f[0];
@@ -388,10 +408,17 @@ int device_cu_count() {
 
 namespace {
 
-hipError_t launch_resident(const CEArgs &a, bool bf16, int kr, int kl, hipStream_t st) {
+hipError_t launch_resident(const CEArgs &a, bool bf16, int kr, int kl, bool ua, hipStream_t st) {
     const int cus = device_cu_count();
-#define LCE_CASE(r, l)                                                                            \
-    if (kr == r && kl == l) return bf16 ? launch_rows_1_##r##_##l(a, cus, st) : launch_rows_0_##r##_##l(a, cus, st);
+    if (ua) {
+#define LCE_UA_CASE(r, l)                                                                                    \
+    if (kr == r && kl == l) return bf16 ? launch_rows_1_1_##r##_##l(a, cus, st) : launch_rows_1_0_##r##_##l(a, cus, st);
+        LCE_UA_FAMILIES(LCE_UA_CASE)
+#undef LCE_UA_CASE
+        return hipErrorInvalidValue;
+    }
+#define LCE_CASE(r, l)                                                                                       \
+    if (kr == r && kl == l) return bf16 ? launch_rows_0_1_##r##_##l(a, cus, st) : launch_rows_0_0_##r##_##l(a, cus, st);
     LCE_FAMILIES(LCE_CASE)
 #undef LCE_CASE
     return hipErrorInvalidValue;
@@ -434,9 +461,10 @@ hipError_t launch_ce_fwd_bwd(const CEArgs &a, bool is_bf16, hipStream_t stream) 
         // one launch: pairs of workgroups, one half row each
         return launch_half(a, is_bf16, kh, stream);
     }
-    if (a.n > 0 && ce_resident_plan(a.logits, a.ld, is_bf16, a.V, &kr, &kl)) {
+    bool ua = false;
+    if (a.n > 0 && ce_resident_plan(a.logits, a.ld, is_bf16, a.V, &kr, &kl, &ua)) {
         // one launch: the persistent kernel counts labels and reduces on its own
-        return launch_resident(a, is_bf16, kr, kl, stream);
+        return launch_resident(a, is_bf16, kr, kl, ua, stream);
     }
     hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, a.count_labels, a.count_n, a.V,
                        a.ignore_index, a.counts, static_cast<unsigned long long *>(a.workspace), a.loss_out);

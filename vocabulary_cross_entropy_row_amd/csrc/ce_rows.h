@@ -36,6 +36,8 @@
 // every reduction is deterministic whichever workgroup took which row.
 #pragma once
 
+#include <type_traits>
+
 #include "ce_device.h"
 
 namespace lce {
@@ -54,7 +56,15 @@ constexpr int kZeroChunk = 64;
 // cache-wide writeback or invalidate.
 
 
-template <bool BF16, int KR, int KL, bool SOFTCAP, bool ARGMAX, bool SMOOTH>
+// UA (unaligned rows): a row need not start on a 16-byte boundary (odd V, ld not
+// a multiple of the vector, or an unaligned base).  The row is then read
+// through the 16-byte aligned window that holds it: its first vector may start
+// with elements of the row before and its last may end with elements of the
+// row after.  Those elements are masked in pass A, and the lane holding such a
+// boundary vector stores only the row's own elements of it, one at a time
+// (its 16-byte store is dropped by an out-of-range offset), so the rows around
+// are never written.
+template <bool BF16, int KR, int KL, bool SOFTCAP, bool ARGMAX, bool SMOOTH, bool UA>
 __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     using EL = Elt<BF16>;
     constexpr int E = EL::E;
@@ -106,9 +116,31 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // return zeros without touching memory.  Reloading unconditionally lets
     // each register round die right after its last use.
     const uint32_t row_bytes = static_cast<uint32_t>(nvec) * 16u;
+    const int Vi = static_cast<int>(a.V);
+    // unaligned rows: the elements of the row before in row r's first vector,
+    // and the number of vectors of its window
+    auto row_off = [&](int64_t r) -> int {
+        if constexpr (!UA) return 0;
+        else
+            return static_cast<int>((reinterpret_cast<uintptr_t>(a.logits) +
+                                     static_cast<uintptr_t>(r * a.ld * EL::bytes)) & 15u) / EL::bytes;
+    };
+    auto row_nv = [&](int off) -> int { return UA ? (off + Vi + E - 1) / E : nvec; };
     auto row_rsrc = [&](int64_t r, bool live) {
-        return __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.logits) + (live ? r : 0) * a.ld * EL::bytes,
-                                                 0, live ? row_bytes : 0u, kBufferWord3);
+        if constexpr (UA) {
+            const int off = live ? row_off(r) : 0;
+            return __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<char *>(a.logits) + (live ? r * a.ld * EL::bytes - off * EL::bytes : 0), 0,
+                live ? static_cast<uint32_t>(row_nv(off)) * 16u : 0u, kBufferWord3);
+        } else {
+            return __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.logits) + (live ? r : 0) * a.ld * EL::bytes,
+                                                     0, live ? row_bytes : 0u, kBufferWord3);
+        }
+    };
+    // the boundary vector of an unaligned row's window that holds elements of
+    // another row (idx: its vector index, off / nv: the window's geometry)
+    auto boundary = [&](int idx, int off, int nv) {
+        return (idx == 0 && off > 0) || (idx == nv - 1 && (off + Vi) % E != 0);
     };
     const int voff = tid * 16;
 
@@ -134,10 +166,31 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // 12-15 of each 16-lane group have stored what the next instruction wrote.
     // (The add is formed at each store: hoisted, every round would hold its
     // own offset register.)
-    auto store_round = [&](int k, __amdgpu_buffer_rsrc_t dst, u32x4 val) {
-        int vo = voff;
+    auto store_round = [&](int k, __amdgpu_buffer_rsrc_t dst, u32x4 val, bool drop = false) {
+        int vo = drop ? 0x40000000 : voff;   // past any descriptor's range: the store is dropped
         asm volatile("" : "+v"(vo));
         __builtin_amdgcn_raw_buffer_store_b128(val, dst, vo + k * NT * 16, 0, kNonTemporal);
+    };
+    // a boundary vector's own elements, one store each, taken from the packed
+    // vector (element offsets within the window; positions outside the row are
+    // skipped)
+    // (the first element's offset is formed here, opaque to the optimiser:
+    // hoisted, every round would keep its own offsets in registers)
+    auto store_elems = [&](__amdgpu_buffer_rsrc_t dst, int idx, int off, const u32x4 &pk) {
+        int p0 = idx * E - off;   // row position of element 0
+        asm volatile("" : "+v"(p0));
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (p0 + e >= 0 && p0 + e < Vi) {
+                const uint32_t w = e * EL::bytes / 4 == 0 ? pk.x : e * EL::bytes / 4 == 1 ? pk.y
+                                 : e * EL::bytes / 4 == 2 ? pk.z : pk.w;
+                if constexpr (BF16)
+                    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w >> (16 * (e & 1))), dst,
+                                                          (p0 + off + e) * 2, 0, kNonTemporal);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(w, dst, (p0 + off + e) * 4, 0, kNonTemporal);
+            }
+        }
     };
     // a round of the resident row as a 16-byte vector
     auto round_vec = [&](int k) -> u32x4 { return k >= KL ? v[k >= KL ? k - KL : 0] : lds_rows[k * NT + tid]; };
@@ -145,8 +198,15 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
     // zero gradient and loss of an ignored row: stores only
     auto zero_row = [&](int64_t r) {
         const __amdgpu_buffer_rsrc_t rz = row_rsrc(r, true);
+        const int off = row_off(r), nv = row_nv(off);
 #pragma unroll
-        for (int k = 0; k < K; ++k) store_round(k, rz, zero4);
+        for (int k = 0; k < K; ++k) {
+            const bool bnd = UA && boundary(k * NT + tid, off, nv);
+            store_round(k, rz, zero4, bnd);
+            if constexpr (UA) {
+                if (bnd) store_elems(rz, k * NT + tid, off, zero4);
+            }
+        }
         if (tid == 0) store_through(a.loss_tok + r, 0.0f);
     };
 
@@ -208,8 +268,13 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         // its gradient comes out as zeros
         const float scale = !valid ? 0.0f : (a.reduction == 0 ? (gout ? gout[row] : 1.0f) : red_scale);
 
+        // the window's geometry (unaligned rows: elements of the row before
+        // in the first vector, vectors in all, the round of the last one)
+        const int off = row_off(row);
+        const int nv = row_nv(off);
+        const int k_last = (nv - 1) / NT;
         // where the target element lives: round ky, thread ty, element ey
-        const int vy = y / E, ey = y % E, ky = vy / NT, ty = vy % NT;
+        const int vy = (y + off) / E, ey = (y + off) % E, ky = vy / NT, ty = vy % NT;
         const bool owner = tid == ty;
 
         // ---- pass A: online softmax statistics, argmax, sum z; the target
@@ -236,89 +301,122 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         int64_t ynx = 0;
         if constexpr (!ARGMAX)
             if (tid == 0 && nx < n) ynx = a.labels[nx];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
+        // one round of pass A; MK: the round may hold a boundary vector of an
+        // unaligned row's window (its first or last round), whose elements of
+        // other rows are masked
+        auto pa_round = [&](auto mk, int k, const u32x4 &vk) {
+            constexpr bool MK = decltype(mk)::value;
             const int idx = k * NT + tid;
-            // whole rounds need no per-lane test (uniform check first)
-            if ((k + 1) * NT <= nvec || idx < nvec) {
-                const u32x4 vk = round_vec(k);
-                // z = x, or with the softcap z = T - 2 T r (r = 1 / (1 + e^{2x/T})):
-                // then the exponent of z is one fma on r and max z = z(min r)
-                // (the fma is monotone in r), so z itself is never formed
-                float x[E], z[E];
+            // unaligned rows: the elements of this vector that belong to the
+            // row (all but in the first and the last vector of the window)
+            unsigned vmask = (1u << E) - 1u;
+            if constexpr (MK) {
+                int p0 = idx * E - off;   // row position of element 0 (opaque: not hoisted per round)
+                asm volatile("" : "+v"(p0));
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    x[e] = EL::get(vk, e);
-                    z[e] = SOFTCAP ? cap.r_of(x[e]) : x[e];
+                for (int e = 0; e < E; ++e)
+                    if (p0 + e < 0 || p0 + e >= Vi) vmask &= ~(1u << e);
+            }
+            // z = x, or with the softcap z = T - 2 T r (r = 1 / (1 + e^{2x/T})):
+            // then the exponent of z is one fma on r and max z = z(min r)
+            // (the fma is monotone in r), so z itself is never formed.
+            // Masked elements take x = -inf (r = +inf): no weight, never the max.
+            float x[E], z[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool in = !MK || ((vmask >> e) & 1u);
+                x[e] = in ? EL::get(vk, e) : -INFINITY;
+                z[e] = SOFTCAP ? (in ? cap.r_of(x[e]) : INFINITY) : x[e];
+            }
+            float rmax = z[0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) rmax = SOFTCAP ? fminf(rmax, z[e]) : fmaxf(rmax, z[e]);
+            if constexpr (SOFTCAP) rmax = cap.z_of_r(rmax);
+            if constexpr (ARGMAX) {
+                float xmax = x[0];
+                if constexpr (SOFTCAP) {
+#pragma unroll
+                    for (int e = 1; e < E; ++e) xmax = fmaxf(xmax, x[e]);
+                } else {
+                    xmax = rmax;
                 }
-                float rmax = z[0];
+                if (xmax > amv) {                 // rounds come in index order: keep the first
+                    // (rare once the running maximum has settled: the search
+                    // for the element runs only then)
+                    int first = E - 1;
 #pragma unroll
-                for (int e = 1; e < E; ++e) rmax = SOFTCAP ? fminf(rmax, z[e]) : fmaxf(rmax, z[e]);
-                if constexpr (SOFTCAP) rmax = cap.z_of_r(rmax);
-                if constexpr (ARGMAX) {
-                    float xmax = x[0];
-                    if constexpr (SOFTCAP) {
-#pragma unroll
-                        for (int e = 1; e < E; ++e) xmax = fmaxf(xmax, x[e]);
-                    } else {
-                        xmax = rmax;
-                    }
-                    if (xmax > amv) {                 // rounds come in index order: keep the first
-                        // (rare once the running maximum has settled: the search
-                        // for the element runs only then)
-                        int first = E - 1;
-#pragma unroll
-                        for (int e = E - 2; e >= 0; --e)
-                            if (x[e] == xmax) first = e;
-                        amv = xmax;
-                        am_k = k;
-                        am_e = first;
-                    }
+                    for (int e = E - 2; e >= 0; --e)
+                        if (x[e] == xmax) first = e;
+                    amv = xmax;
+                    am_k = k;
+                    am_e = first;
                 }
-                if constexpr (SMOOTH) {
+            }
+            if constexpr (SMOOTH) {
+                if constexpr (MK) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if ((vmask >> e) & 1u) t += SOFTCAP ? fmaf(-2.0f * a.softcap, z[e], a.softcap) : z[e];
+                    zs += t;
+                } else {
                     float t = z[0];
 #pragma unroll
                     for (int e = 1; e < E; ++e) t += z[e];
                     zs += SOFTCAP ? fmaf(-2.0f * a.softcap, t, E * a.softcap) : t;
                 }
-                const float mn = fmaxf(m, rmax);
-                const float mnL = mn * kLog2e;
-                float part = 0.0f;
-                float ex[E];
-                if constexpr (SOFTCAP) {
-                    const float b = fmaf(a.softcap, kLog2e, -mnL);
+            }
+            const float mn = fmaxf(m, rmax);
+            const float mnL = mn * kLog2e;
+            float part = 0.0f;
+            float ex[E];
+            if constexpr (SOFTCAP) {
+                const float b = fmaf(a.softcap, kLog2e, -mnL);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], capk, b));
-                } else if constexpr (BF16) {
+                for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], capk, b));
+            } else if constexpr (BF16) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], kLog2e, -mnL));
+                for (int e = 0; e < E; ++e) ex[e] = exp2_fast(fmaf(z[e], kLog2e, -mnL));
+            } else {
+                // fp32 rows: every weight relative to the running max itself
+                // (z - m is exact where the weight matters), not to an fp32
+                // rounding of m log2 e
+#pragma unroll
+                for (int e = 0; e < E; ++e) ex[e] = exp2_fast((z[e] - mn) * kLog2e);
+            }
+            if (k == ky) {
+                // the target's round (uniform branch, taken once per row); the
+                // asm keeps it a branch instead of per-element selects everywhere
+                asm volatile("");
+                if (owner) {
+                    float sel = x[0];
+#pragma unroll
+                    for (int e = 1; e < E; ++e)
+                        if (e == ey) sel = x[e];
+                    sh_xy[pb] = sel;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (e == ey) ex[e] = 0.0f;
+                }
+            }
+            part = ex[0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) part += ex[e];
+            s = fmaf(s, exp2_fast(BF16 || SOFTCAP ? fmaf(m, kLog2e, -mnL) : (m - mn) * kLog2e), part);
+            m = mn;
+        };
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int idx = k * NT + tid;
+            // whole rounds need no per-lane test (uniform check first)
+            if ((k + 1) * NT <= nv || idx < nv) {
+                const u32x4 vk = round_vec(k);
+                if constexpr (UA) {
+                    if (k == 0 || k == k_last) pa_round(std::true_type{}, k, vk);
+                    else pa_round(std::false_type{}, k, vk);
                 } else {
-                    // fp32 rows: every weight relative to the running max itself
-                    // (z - m is exact where the weight matters), not to an fp32
-                    // rounding of m log2 e
-#pragma unroll
-                    for (int e = 0; e < E; ++e) ex[e] = exp2_fast((z[e] - mn) * kLog2e);
+                    pa_round(std::false_type{}, k, vk);
                 }
-                if (k == ky) {
-                    // the target's round (uniform branch, taken once per row); the
-                    // asm keeps it a branch instead of per-element selects everywhere
-                    asm volatile("");
-                    if (owner) {
-                        float sel = x[0];
-#pragma unroll
-                        for (int e = 1; e < E; ++e)
-                            if (e == ey) sel = x[e];
-                        sh_xy[pb] = sel;
-#pragma unroll
-                        for (int e = 0; e < E; ++e)
-                            if (e == ey) ex[e] = 0.0f;
-                    }
-                }
-                part = ex[0];
-#pragma unroll
-                for (int e = 1; e < E; ++e) part += ex[e];
-                s = fmaf(s, exp2_fast(BF16 || SOFTCAP ? fmaf(m, kLog2e, -mnL) : (m - mn) * kLog2e), part);
-                m = mn;
             }
         }
         // combine the threads' (m, s) pairs, then the argmax and sum z
@@ -330,7 +428,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
                 sh_s[pb][tid >> 6] = sw;
             }
             if constexpr (ARGMAX) {
-                am = am_k < 0 ? 0x7fffffff : (am_k * NT + tid) * E + am_e;
+                am = am_k < 0 ? 0x7fffffff : (am_k * NT + tid) * E + am_e - off;
                 wave_argmax_dpp(amv, am);
                 if ((tid & 63) == 0) {
                     sh_z[pb][tid >> 6] = amv;
@@ -415,7 +513,10 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         // would store -0 here, while the end-of-call zeroing stores +0)
         if (!valid) gy = 0.0f;
         opaque_regs(v);
-        auto grad_round = [&](int k) {
+        // one round of pass B; MK as in pass A: a boundary vector's lane stores
+        // the row's own elements of it one at a time
+        auto grad_round_mk = [&](auto mk, int k) {
+            constexpr bool MK = decltype(mk)::value;
             const u32x4 vk = round_vec(k);
             float g[E];
 #pragma unroll
@@ -438,11 +539,19 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) g[e] = -g[e];
             }
-            store_round(k, rp, EL::pack(g));
+            if constexpr (MK) {
+                const bool bnd = boundary(k * NT + tid, off, nv);
+                const u32x4 pk = EL::pack(g);
+                store_round(k, rp, pk, bnd);
+                if (bnd) store_elems(rp, k * NT + tid, off, pk);
+            } else {
+                store_round(k, rp, EL::pack(g));
+            }
             // keep the rounds in order: hoisted loads or conversions of later
             // rounds would hold extra row data in registers
             __builtin_amdgcn_sched_barrier(0);
         };
+        auto grad_round = [&](int k) { grad_round_mk(std::integral_constant<bool, UA>{}, k); };
         // the LDS rounds, then the next row's LDS rounds go out (this wave read
         // its slots before computing the stores above, and no other wave uses them).
         // Without the softcap the workgroup first lets its LDS-round stores
@@ -474,7 +583,7 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         }
         // the target element's own gradient replaces what its round stored
         // (one thread, after that round's store, to the same address)
-        if (owner) EL::template store_one<kNonTemporal>(rp, y, gy);
+        if (owner) EL::template store_one<kNonTemporal>(rp, y + off, gy);
         if (tid == 0) {
             store_through(a.loss_tok + row, loss);
             if constexpr (ARGMAX) a.argmax_out[row] = am;
@@ -579,12 +688,12 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
 
 // Host-side launch of one (dtype, KR, KL) family: picks the feature variant and
 // sizes the persistent grid to the workgroups the CUs hold at once.
-template <bool BF16, int KR, int KL, bool S, bool A, bool M>
+template <bool BF16, int KR, int KL, bool S, bool A, bool M, bool UA>
 hipError_t launch_variant(const CEArgs &a, int max_groups, hipStream_t st) {
     static int per_cu = 0;   // resident workgroups per CU (same for every gfx950 device)
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ce_rows_kernel<BF16, KR, KL, S, A, M>, NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ce_rows_kernel<BF16, KR, KL, S, A, M, UA>, NT, 0) !=
                 hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
@@ -592,15 +701,15 @@ hipError_t launch_variant(const CEArgs &a, int max_groups, hipStream_t st) {
     int64_t grid = static_cast<int64_t>(max_groups) * per_cu;
     if (grid > a.n) grid = a.n;
     if (grid > kMaxRowGroups) grid = kMaxRowGroups;
-    hipLaunchKernelGGL((ce_rows_kernel<BF16, KR, KL, S, A, M>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, st,
-                       a);
+    hipLaunchKernelGGL((ce_rows_kernel<BF16, KR, KL, S, A, M, UA>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
+                       st, a);
     return hipGetLastError();
 }
 
-template <bool BF16, int KR, int KL>
+template <bool BF16, int KR, int KL, bool UA>
 hipError_t launch_rows(const CEArgs &a, int max_groups, hipStream_t st) {
     const bool sc = a.softcap > 0.0f, am = a.argmax_out != nullptr, sm = a.eps != 0.0f;
-#define LCE_ROWS(S, A, M) return launch_variant<BF16, KR, KL, S, A, M>(a, max_groups, st)
+#define LCE_ROWS(S, A, M) return launch_variant<BF16, KR, KL, S, A, M, UA>(a, max_groups, st)
     if (sc) {
         if (am) { if (sm) LCE_ROWS(true, true, true); else LCE_ROWS(true, true, false); }
         else    { if (sm) LCE_ROWS(true, false, true); else LCE_ROWS(true, false, false); }

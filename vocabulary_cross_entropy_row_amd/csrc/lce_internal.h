@@ -62,9 +62,10 @@ hipError_t launch_ce_argmax(const void *logits, int64_t ld, bool is_bf16, const 
 // Whether a shape takes the half-row kernel, and its rounds of 960 vectors per half.
 bool ce_half_plan(const void *logits, int64_t ld, bool is_bf16, int64_t n, int64_t V, int *kh);
 
-// Which row kernel a shape takes: rounds in VGPRs (*kr) and LDS (*kl), or
-// false for the generic streaming kernel.
-bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl);
+// Which row kernel a shape takes: rounds in VGPRs (*kr) and LDS (*kl), whether
+// its rows are read through aligned windows (*ua), or false for the generic
+// streaming kernel.
+bool ce_resident_plan(const void *logits, int64_t ld, bool is_bf16, int64_t V, int *kr, int *kl, bool *ua);
 
 // counts = {n_valid, 0, n_bad} over labels[0, n); clears the three counter words at
 // ticket and *loss_out when given.
