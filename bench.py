@@ -596,9 +596,9 @@ SPLIT_METRIC = "split CE (stats, combine, gradient) ms and HBM GB/s (% peak), bf
 
 
 def bench_split(args, w) -> int:
-    """One step = lce_ce_stats on every shard + lce_ce_combine + lce_ce_grad on every shard, the shards being
-    column slices of one resident matrix (the per-rank work of a vocabulary-parallel layout, or with one shard
-    a forward / deferred-backward pair).  Algorithmic bytes: one read for the statistics and one read + write
+    """One step = lce_ce_stats on every shard + lce_ce_combine + lce_ce_grad on every shard, each shard its
+    own contiguous [N, V / tp] tensor as a rank of a vocabulary-parallel layout holds it (with one shard a
+    forward / deferred-backward pair).  Algorithmic bytes: one read for the statistics and one read + write
     for the gradient, 3 N V b, plus the records and row outputs."""
     import numpy as np
     import torch
@@ -609,15 +609,17 @@ def bench_split(args, w) -> int:
     torch.cuda.set_device(dev)
     y = synth.labels(w)
     x = synth.logits(w, y)
-    pristine = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-    labels = torch.from_numpy(y).to(dev)
-    nbuf = args.warmup + args.steps
-    bufs = [pristine.clone() for _ in range(nbuf)]
     tp = args.tp
     if w.V % (8 * tp):
         print(f"V = {w.V} does not split into {tp} shards of whole 16-byte vectors", file=sys.stderr)
         return 2
     ws = w.V // tp
+    full = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    pristine = [full[:, k * ws:(k + 1) * ws].contiguous() for k in range(tp)]   # shard k: columns [k ws, (k+1) ws)
+    del full
+    labels = torch.from_numpy(y).to(dev)
+    nbuf = args.warmup + args.steps
+    bufs = [[p.clone() for p in pristine] for _ in range(nbuf)]
     stats = torch.empty((tp, w.n, 8), dtype=torch.float32, device=dev)
     grad_out = torch.full((1,), w.grad_out, dtype=torch.float32, device=dev)
     fv = lambda: torch.empty(w.n, dtype=torch.float32, device=dev)  # noqa: E731
@@ -631,14 +633,13 @@ def bench_split(args, w) -> int:
         mark = (lambda i: e[i].record(stream)) if timed else (lambda i: None)  # noqa: E731
         mark(0)
         for k in range(tp):
-            lce.lce_ce_stats(buf[:, k * ws:(k + 1) * ws], labels, v_offset=k * ws, softcap=w.softcap, stats=stats[k],
-                             stream=stream)
+            lce.lce_ce_stats(buf[k], labels, v_offset=k * ws, softcap=w.softcap, stats=stats[k], stream=stream)
         mark(1)
         rows = lce.lce_ce_combine(stats, labels, w.V, label_smoothing=w.label_smoothing, reduction=w.reduction,
                                   out=rows_out, stream=stream)
         mark(2)
         for k in range(tp):
-            lce.lce_ce_grad(buf[:, k * ws:(k + 1) * ws], labels, w.V, rows, v_offset=k * ws,
+            lce.lce_ce_grad(buf[k], labels, w.V, rows, v_offset=k * ws,
                             label_smoothing=w.label_smoothing, softcap=w.softcap, reduction=w.reduction,
                             grad_out=grad_out, stream=stream)
         mark(3)
@@ -660,7 +661,8 @@ def bench_split(args, w) -> int:
     ms_per_step = wall * 1e3 / args.steps
     # phase and call durations: the same steps again on restored logits, HIP events between the phases
     for i in range(args.steps):
-        bufs[args.warmup + i].copy_(pristine)
+        for b, p in zip(bufs[args.warmup + i], pristine):
+            b.copy_(p)
     torch.cuda.synchronize()
     whole = [step(bufs[args.warmup + i], True) for i in range(args.steps)]
     torch.cuda.synchronize()
@@ -674,6 +676,7 @@ def bench_split(args, w) -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "V": w.V, "shards": tp, "shard_V": ws, "logits_dtype": w.dtype,
+                   "shard_layout": "contiguous [n, V / tp] per shard",
                    "parallelism": f"vocabulary split into {tp} shards on one GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -743,7 +746,7 @@ def collect_profiles_split(workload: str, tp: int) -> int:
     _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "5", "--warmup", "2"], 180)
     _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "5", "--warmup", "2"], 180)
     stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
-    copy_kib = w.n * w.V * w.elem_bytes / 1024.0          # the pristine copy made for each step
+    copy_kib = w.n * (w.V // tp) * w.elem_bytes / 1024.0   # the pristine copy of one shard (one per shard and step)
 
     def counter(sub: str, cname: str):
         rows = [r for r in csv.DictReader(open(os.path.join(raw, sub, "run_counter_collection.csv")))
@@ -764,8 +767,9 @@ def collect_profiles_split(workload: str, tp: int) -> int:
         f"#   rocprofv3 --kernel-trace --stats -f csv -d <raw>/ktrace -o run -- python bench.py {b} --steps 10 --warmup 3",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <raw>/fetch -o run -- python bench.py {b} --steps 5 --warmup 2",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <raw>/write -o run -- python bench.py {b} --steps 5 --warmup 2",
-        "# Counter scale: what each counter reads for the plain copy (__amd_rocclr_copyBuffer) of the pristine",
-        f"# logits -- a known {copy_kib:.0f} KiB read + {copy_kib:.0f} KiB write -- divided into that size.",
+        "# Counter scale: what each counter reads for the plain copy (__amd_rocclr_copyBuffer) of a pristine",
+        f"# shard -- a known {copy_kib:.0f} KiB read + {copy_kib:.0f} KiB write -- divided into that size.",
+        "# Each shard is its own contiguous [n, V / tp] tensor.",
         "# kernel trace (--stats), nanoseconds per launch (13 steps; stats and grad launch once per shard):",
     ]
     for r in stats:

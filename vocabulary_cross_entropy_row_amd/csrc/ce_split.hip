@@ -88,9 +88,19 @@ __device__ __forceinline__ void wave_part(Part &p) {
     p.zs = r[0].zs;
 }
 
-constexpr int kStatsThreads = 256;                    // four waves per row: several rows per CU
+#ifndef LCE_STATS_THREADS
+#define LCE_STATS_THREADS 256
+#endif
+#ifndef LCE_STATS_AHEAD
+#define LCE_STATS_AHEAD 4
+#endif
+#ifndef LCE_GRAD_PER
+#define LCE_GRAD_PER 4
+#endif
+constexpr int kStatsThreads = LCE_STATS_THREADS;      // four waves per row: several rows per CU
 constexpr int kStatsWaves = kStatsThreads / 64;
-constexpr int kStatsAhead = 4;                        // 16-byte vectors per batch; two batches in flight
+constexpr int kStatsAhead = LCE_STATS_AHEAD;          // 16-byte vectors per batch; two batches in flight
+constexpr int kGradPer = LCE_GRAD_PER;                // 16-byte vectors per thread of the gradient (shards < 8192 vectors)
 
 template <bool BF16, bool SOFTCAP>
 __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *logits, int64_t ld, int64_t Vs,
@@ -555,7 +565,7 @@ hipError_t launch_ce_grad(void *logits, int64_t ld, bool is_bf16, const int64_t 
     // eight vectors per thread on long shards (fewer, larger workgroups: measured faster at 16384
     // vectors, slower at 2048), else four
     const bool wide = nvec >= 8192;
-    const int per = wide ? 8 : 4;
+    const int per = wide ? 8 : kGradPer;
     const int bpr = static_cast<int>((nvec + 256 * per - 1) / (256 * per));
     const dim3 grid(static_cast<unsigned>(n * bpr)), block(256);
     const bool sc = softcap > 0.0f, sm = eps != 0.0f;
@@ -565,7 +575,8 @@ hipError_t launch_ce_grad(void *logits, int64_t ld, bool is_bf16, const int64_t 
             hipLaunchKernelGGL((ce_grad_kernel<B, S, M, 8>), grid, block, 0, st, logits, ld, Vs, v0, V, labels,    \
                                ignore_index, eps, softcap, reduction, grad_out, lse, q, counts, bpr);              \
         else                                                                                                       \
-            hipLaunchKernelGGL((ce_grad_kernel<B, S, M, 4>), grid, block, 0, st, logits, ld, Vs, v0, V, labels,    \
+            hipLaunchKernelGGL((ce_grad_kernel<B, S, M, kGradPer>), grid, block, 0, st, logits, ld, Vs, v0, V,      \
+                               labels,                                                                              \
                                ignore_index, eps, softcap, reduction, grad_out, lse, q, counts, bpr);              \
     } while (0)
     if (is_bf16) {

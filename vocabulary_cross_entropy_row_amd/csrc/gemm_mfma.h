@@ -51,10 +51,15 @@ namespace gemm {
 #ifndef LCE_GEMM_NSTAGE
 #define LCE_GEMM_NSTAGE 2
 #endif
+#ifndef LCE_GEMM_NWAVES
+#define LCE_GEMM_NWAVES 8
+#endif
 constexpr int BM = 256, BN = 256, BK = LCE_GEMM_BK;
 constexpr int NSTAGE = LCE_GEMM_NSTAGE;              // LDS stages; NSTAGE - 1 steps of loads in flight
-constexpr int NWAVES = 8, NTHR = 64 * NWAVES;
-constexpr int WI = 2;                                // A fragments (32 rows each) per wave
+constexpr int NWAVES = LCE_GEMM_NWAVES, NTHR = 64 * NWAVES;
+constexpr int WPS = NWAVES / 4;                      // waves per SIMD
+constexpr int WI = BM / 32 / (NWAVES / 2);           // A fragments (32 rows each) per wave
+constexpr int WROWS = WI * 32;                       // tile rows per wave (two waves per row band)
 constexpr int CPR = BK / 8;                          // 16-byte K chunks per tile row
 constexpr int TILE_BYTES = BM * BK * 2;              // one operand tile of one stage
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;          // A | B
@@ -64,6 +69,7 @@ constexpr int LOADS = NBLK / NWAVES;                 // per wave per operand per
 constexpr int KK = BK / 16;                          // MFMA K sub-steps per step
 constexpr int kBufWord3 = 0x00020000;                // gfx9-family buffer descriptor word 3
 static_assert(LDS_BYTES <= 160 * 1024 && LOADS >= 1 && (CPR == 4 || CPR == 8), "unsupported GEMM staging");
+static_assert(NWAVES == 8 || NWAVES == 4, "two wave columns of 128 and 4 or 2 wave rows");
 
 enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_ACC = 2, OUT_STATS = 3, OUT_GRAD = 4 };
 
@@ -146,7 +152,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, ui
 // Epilogue layout: lane l of wave (wm, wn) holds tile column wn * 128 + j * 32 + l % 32
 // of tile rows wm * 64 + i * 32 + (r / 4) * 8 + (l / 32) * 4 + r % 4.
 __device__ __forceinline__ int epi_row(int wm, int i, int r, int lane) {
-    return wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    return wm * WROWS + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
 // One stats record per row of the tile (columns [n0, n0 + 256) of the vocabulary).
@@ -350,7 +356,7 @@ __device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI]
 // KTAIL: K is not a multiple of BK, so each load checks its K column; otherwise
 // the K position rides in the scalar offset and the per-lane offsets are fixed.
 template <int MODE, bool KTAIL, bool SOFTCAP = false, bool A_KM = false, bool B_KN = false>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_nt_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))) void gemm_nt_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
     // XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs;
@@ -443,9 +449,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
             if constexpr (A_KM) {
-                af[i] = km_frag(At, kk, wm * 64 + i * 32, lane);
+                af[i] = km_frag(At, kk, wm * WROWS + i * 32, lane);
             } else {
-                const int r = wm * 64 + i * 32 + (lane & 31);
+                const int r = wm * WROWS + i * 32 + (lane & 31);
                 af[i] = *reinterpret_cast<const bf8 *>(At + (r * CPR + (c ^ swz(r))) * 16);
             }
         }
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
             // spread the fragment reads (and in sub-step 0 the global loads) between the MFMAs
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < WI * 4; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
                 if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
@@ -550,7 +556,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // epilogue: lane holds column n0 + wn*128 + j*32 + lane%32 of rows
     // m0 + wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4
     const int col_base = n0 + wn * 128 + (lane & 31);
-    const int row_base = m0 + wm * 64 + (lane >> 5) * 4;
+    const int row_base = m0 + wm * WROWS + (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
 #pragma unroll
