@@ -197,9 +197,20 @@ def kernel_source_hash(workload: str = "") -> str:
     return h.hexdigest()[:16]
 
 
-def profile_path(workload: str, resident: bool = False) -> str:
-    kind = ("flce_resident_gemm" if resident else "flce_gemm") if workload.startswith("flce") else "ce_rows_kernel"
-    return os.path.join(PROFILES, f"{kind}__{workload}.txt")
+# the cross-entropy kernels a plain call may run (its profile is named for the one it ran)
+CE_KERNELS = ("ce_half_kernel", "ce_rows_mr_kernel", "ce_rows_kernel", "ce_row_generic")
+
+
+def profile_path(workload: str, resident: bool = False, kernel: str | None = None) -> str:
+    if workload.startswith("flce"):
+        return os.path.join(PROFILES, f"{'flce_resident_gemm' if resident else 'flce_gemm'}__{workload}.txt")
+    if kernel is None:   # whichever cross-entropy kernel's summary exists for this workload
+        for k in CE_KERNELS:
+            p = os.path.join(PROFILES, f"{k}__{workload}.txt")
+            if os.path.exists(p):
+                return p
+        kernel = CE_KERNELS[-1]
+    return os.path.join(PROFILES, f"{kernel}__{workload}.txt")
 
 
 def read_profile(workload: str, resident: bool = False) -> dict | None:
@@ -248,7 +259,7 @@ def collect_profiles(workload: str) -> int:
     w = synth.ALL_CE_WORKLOADS[workload]
     raw = os.path.join(RAW_PROFILES, workload)
     os.makedirs(raw, exist_ok=True)
-    base = ["--workload", workload, "--no-cpu-baseline"]
+    base = ["--workload", workload, "--no-cpu-baseline", "--no-pages-protocol"]
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
     _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "5", "--warmup", "2"], 180)
     _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "5", "--warmup", "2"], 180)
@@ -314,9 +325,15 @@ def collect_profiles(workload: str) -> int:
         f"kernel_source_sha256_16: {kernel_source_hash(workload)}",
     ]
     os.makedirs(PROFILES, exist_ok=True)
-    with open(profile_path(workload), "w") as f:
+    kname = next((k for k in CE_KERNELS if ours and k in ours[0]["Name"]), CE_KERNELS[-1])
+    for k in CE_KERNELS:   # one summary per workload, named for the kernel that ran
+        old = profile_path(workload, kernel=k)
+        if k != kname and os.path.exists(old):
+            os.remove(old)
+    path = profile_path(workload, kernel=kname)
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(open(profile_path(workload)).read(), flush=True)
+    print(open(path).read(), flush=True)
     return 0
 
 
@@ -494,7 +511,7 @@ def collect_profiles_flce(workload: str, resident: bool = False) -> int:
     _rocprof(["--pmc", "TCC_HIT_sum", "TCC_MISS_sum"], os.path.join(raw, "l2"), base + ["--steps", "1", "--warmup", "1"],
              600)
     stats = list(csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_stats.csv"))))
-    calls = 4   # warmup + steps of the trace run
+    calls = 5   # the trace run's calls: 1 warmup, the memory-measuring call, 3 steps
     ref_kib = (256 << 20) * 4 / 1024.0
     ours = ("gemm_nt_kernel", "transpose_bf16_kernel", "splitk_fold_kernel", "ce_rows_kernel", "ce_count_kernel",
             "loss_fold_kernel", "fill_zero_f32_kernel", "ce_row_generic", "ce_combine")
@@ -504,8 +521,9 @@ def collect_profiles_flce(workload: str, resident: bool = False) -> int:
         rows = [r for r in rows if r["Counter_Name"] == cname]
         k = [float(r["Counter_Value"]) for r in rows if any(o in r["Kernel_Name"] for o in ours)]
         c = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        # per call: the run makes 2 calls (1 warmup + 1 step); the reference copy is the largest copy
-        return sum(k) / 2.0, max(c), len(k)
+        # per call: the run makes 3 calls (1 warmup, the memory-measuring call, 1 step); the reference
+        # copy is the largest copy
+        return sum(k) / 3.0, max(c), len(k)
 
     fk, fc, nfk = counter("fetch", "FETCH_SIZE")
     wk, wc, nwk = counter("write", "WRITE_SIZE")
