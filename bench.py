@@ -771,7 +771,7 @@ def collect_profiles_split(workload: str, tp: int) -> int:
                 if r["Counter_Name"] == cname]
         ours = sum(float(r["Counter_Value"]) for r in rows if any(k in r["Kernel_Name"] for k in SPLIT_KERNELS))
         c = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 4096]
-        return ours / 7.0, sum(c) / len(c)   # 2 warmup + 5 timed steps
+        return ours / 12.0, sum(c) / len(c)   # 2 warmup steps, 5 timed back to back, 5 again with events
 
     fk, fc = counter("fetch", "FETCH_SIZE")
     wk, wc = counter("write", "WRITE_SIZE")
