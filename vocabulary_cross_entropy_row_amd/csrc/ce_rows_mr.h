@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
     __shared__ int sh_flag;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: row numbers stay in SGPRs
     const int grp = wave / P;            // row group of this wave
     const int gl = tid - grp * GT;       // lane within the row group
     const int nvec = static_cast<int>(a.V / E);
@@ -65,8 +65,33 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const unsigned tag = launch_tag();
     auto valid_label = [&](int64_t y) { return y != a.ignore_index && y >= 0 && y < a.V; };
 
-    // the label counts: kFold labels per thread in flight, then one LDS exchange
+    // The label counts: kFold labels per thread in flight, then one LDS exchange.
+    // The first batch of labels is requested first, then this workgroup's first
+    // row set, so counting that batch waits for its own loads only and the row
+    // loads overlap the count.
     constexpr int kFold = 8;
+    const uint32_t row_bytes = static_cast<uint32_t>(nvec) * 16u;
+    int64_t yl0[kFold];
+#pragma unroll
+    for (int u = 0; u < kFold; ++u) {
+        const int64_t i = u * kMrThreads + tid;
+        yl0[u] = i < a.count_n ? a.count_labels[i] : a.ignore_index;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 v[KV];
+    {
+        const int64_t row = static_cast<int64_t>(blockIdx.x) * R + grp;
+        const bool live = row < n;
+        const int64_t y64 = live ? lab[row] : a.ignore_index;
+        const bool read = live && (ARGMAX || valid_label(y64));
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<char *>(a.logits) + (read ? row : 0) * a.ld * EL::bytes, 0, read ? row_bytes : 0u,
+            kBufferWord3);
+#pragma unroll
+        for (int k = 0; k < KV; ++k)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (gl + k * GT) * 16, 0, kNonTemporal);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     long long n_valid = 0, n_bad = 0;
     {
         long long cv = 0, cb = 0;
@@ -75,7 +100,7 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
             for (int u = 0; u < kFold; ++u) {
                 const int64_t i = i0 + u * kMrThreads + tid;
-                yl[u] = i < a.count_n ? a.count_labels[i] : a.ignore_index;
+                yl[u] = i0 == 0 ? yl0[u] : (i < a.count_n ? a.count_labels[i] : a.ignore_index);
             }
 #pragma unroll
             for (int u = 0; u < kFold; ++u)
@@ -99,7 +124,6 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
     const float g_all = (a.reduction != 0 && gout) ? gout[0] : 1.0f;
     const float red_scale = a.reduction == 1 ? (n_valid > 0 ? g_all / static_cast<float>(n_valid) : 0.0f) : g_all;
-    const uint32_t row_bytes = static_cast<uint32_t>(nvec) * 16u;
     long long correct = 0;
 
     int pb = 0;
@@ -117,10 +141,11 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
         const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
             static_cast<char *>(a.logits) + (read ? row : 0) * a.ld * EL::bytes, 0, read ? row_bytes : 0u,
             kBufferWord3);
-        u32x4 v[KV];
+        if (base != static_cast<int64_t>(blockIdx.x) * R) {   // the first set's rows were requested above
 #pragma unroll
-        for (int k = 0; k < KV; ++k)
-            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (gl + k * GT) * 16, 0, kNonTemporal);
+            for (int k = 0; k < KV; ++k)
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (gl + k * GT) * 16, 0, kNonTemporal);
+        }
         const int vy = y / E, ey = y % E, ky = vy / GT, ty = vy % GT;
         const bool owner = gl == ty;
 
