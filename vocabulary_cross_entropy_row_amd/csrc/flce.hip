@@ -177,11 +177,15 @@ hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, i
     return hipGetLastError();
 }
 
+// The K-contiguous GEMMs request B two steps ahead (five LDS slots, 160 KB).  The GEMM that
+// reads B k-major keeps two stages (128 KB): it runs while the gradient transposes of the
+// second stream fill the rest of each CU's LDS.
 template <int MODE, bool SOFTCAP = false, bool B_KN = false>
 void launch_gemm(const GemmArgs &g, bool ktail, hipStream_t st) {
+    constexpr int R = B_KN ? gemm::kRingKn : gemm::kRingDefault;
     const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u), block(gemm::NTHR);
-    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true, SOFTCAP, false, B_KN>), grid, block, 0, st, g);
-    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false, SOFTCAP, false, B_KN>), grid, block, 0, st, g);
+    if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true, SOFTCAP, false, B_KN, R>), grid, block, 0, st, g);
+    else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false, SOFTCAP, false, B_KN, R>), grid, block, 0, st, g);
 }
 
 // C (+)= A B^T over [M, N] with K split into `splits` ranges; the cross-entropy

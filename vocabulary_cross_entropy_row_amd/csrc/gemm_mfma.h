@@ -11,8 +11,10 @@
 // 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane), so a
 // SIMD always has a second wave to issue MFMAs while one waits.  K advances in
 // steps of 64.  Each step's A and B tiles (32 KB each) are fetched by
-// buffer->LDS loads into one of two stages; the loads of step s+1 are issued
-// at the start of step s, and one barrier per step hands the next stage over.
+// buffer->LDS loads into LDS slots: with two stages the loads of step s+1 are
+// issued at the start of step s; with the five-slot ring the streamed operand
+// (B) of step s+2 goes out at the start of step s as well, into the fifth slot,
+// so it has two steps to arrive.  One barrier per step hands the slots over.
 // Fragment reads for sub-step kk+1 are issued while the MFMAs of kk run.
 //
 // LDS tile layout: row r holds its eight 16-byte K-chunks at positions
@@ -54,6 +56,12 @@ namespace gemm {
 #ifndef LCE_GEMM_NWAVES
 #define LCE_GEMM_NWAVES 8
 #endif
+#ifndef LCE_GEMM_RING
+#define LCE_GEMM_RING 1
+#endif
+#ifndef LCE_GEMM_RING_KN
+#define LCE_GEMM_RING_KN 0
+#endif
 constexpr int BM = 256, BN = 256, BK = LCE_GEMM_BK;
 constexpr int NSTAGE = LCE_GEMM_NSTAGE;              // LDS stages; NSTAGE - 1 steps of loads in flight
 constexpr int NWAVES = LCE_GEMM_NWAVES, NTHR = 64 * NWAVES;
@@ -63,12 +71,21 @@ constexpr int WROWS = WI * 32;                       // tile rows per wave (two 
 constexpr int CPR = BK / 8;                          // 16-byte K chunks per tile row
 constexpr int TILE_BYTES = BM * BK * 2;              // one operand tile of one stage
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;          // A | B
-constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+// The operand tiles live in LDS slots of TILE_BYTES.  Two stages (ring 0): four
+// slots, both operands of step s+1 requested at the start of step s.  Ring 1 (B)
+// or 2 (A): five slots, that operand requested two steps before it is used and
+// the other one step before.
+constexpr int kRingDefault = LCE_GEMM_RING;   // the ring of the K-contiguous GEMMs
+constexpr int kRingKn = LCE_GEMM_RING_KN;      // ... and of the GEMM that reads B k-major
+constexpr int nslots(int ring) { return ring ? 5 : 2 * NSTAGE; }
+constexpr int lds_bytes(int ring) { return nslots(ring) * TILE_BYTES; }
 constexpr int NBLK = TILE_BYTES / 1024;              // one-KB load blocks per operand tile
 constexpr int LOADS = NBLK / NWAVES;                 // per wave per operand per step
 constexpr int KK = BK / 16;                          // MFMA K sub-steps per step
 constexpr int kBufWord3 = 0x00020000;                // gfx9-family buffer descriptor word 3
-static_assert(LDS_BYTES <= 160 * 1024 && LOADS >= 1 && (CPR == 4 || CPR == 8), "unsupported GEMM staging");
+static_assert(lds_bytes(0) <= 160 * 1024 && lds_bytes(1) <= 160 * 1024 && LOADS >= 1 && (CPR == 4 || CPR == 8),
+              "unsupported GEMM staging");
+static_assert(kRingDefault == 0 || NSTAGE == 2, "the ring replaces the two stages");
 static_assert(NWAVES == 8 || NWAVES == 4, "two wave columns of 128 and 4 or 2 wave rows");
 
 enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_ACC = 2, OUT_STATS = 3, OUT_GRAD = 4 };
@@ -355,9 +372,10 @@ __device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI]
 
 // KTAIL: K is not a multiple of BK, so each load checks its K column; otherwise
 // the K position rides in the scalar offset and the per-lane offsets are fixed.
-template <int MODE, bool KTAIL, bool SOFTCAP = false, bool A_KM = false, bool B_KN = false>
+template <int MODE, bool KTAIL, bool SOFTCAP = false, bool A_KM = false, bool B_KN = false, int RING = 0>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))) void gemm_nt_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
+    constexpr int NSLOT = nslots(RING);
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[lds_bytes(RING)];
 
     // XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs;
     // each XCD walks a contiguous range of the logical tile order.  That order
@@ -423,9 +441,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
         }
     }
 
-    // load j of one operand of step `step` into stage `st`
-    auto issue = [&](int step, int st, int j, bool isB) {
-        unsigned char *dst = lds + st * STAGE_BYTES + (isB ? TILE_BYTES : 0) + (j * NWAVES + wave) * 1024;
+    // load j of one operand of step `step` into operand slot `slot`
+    auto issue = [&](int step, int slot, int j, bool isB) {
+        unsigned char *dst = lds + slot * TILE_BYTES + (j * NWAVES + wave) * 1024;
         const int k0 = step * BK;
         if ((isB && B_KN) || (!isB && A_KM)) {
             // k-major: the step's rows are k0 .. k0 + 63 (past K: outside the descriptor)
@@ -442,9 +460,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
                                                      k0 * 2, 0, 0);
         }
     };
-    auto read_frags = [&](int st, int kk, bf8 *af, bf8 *bfr) {
-        const unsigned char *At = lds + st * STAGE_BYTES;
-        const unsigned char *Bt = At + TILE_BYTES;
+    auto read_frags = [&](int slot_a, int slot_b, int kk, bf8 *af, bf8 *bfr) {
+        const unsigned char *At = lds + slot_a * TILE_BYTES;
+        const unsigned char *Bt = lds + slot_b * TILE_BYTES;
         const int c = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
@@ -475,75 +493,141 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L) : "memory");
     };
 
+    const int nsteps = kend - kbeg;
     f16v acc[WI][4];
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f16v){};
-
-    const int nsteps = kend - kbeg;
-    constexpr int D = NSTAGE - 1;   // steps of loads in flight ahead of the one being consumed
-    static_assert(D >= 1 && D <= 4, "wait_steps covers up to three outstanding steps");
     bf8 af0[WI], bf0[4], af1[WI], bf1[4];
-    if (nsteps > 0) {
-        for (int p = 0; p < D && p < nsteps; ++p) {
+    if constexpr (RING != 0) {
+        // Operand tiles in request order: T(2s) is the early operand of step s (B for RING 1, A for 2),
+        // T(2s+1) the other; T(i) lives in slot i mod 5.  At the start of step s the slots of step s-1
+        // are free and take T(2s+3) (the late operand of step s+1) and T(2s+4) (the early operand of
+        // step s+2): the early operand is requested two steps before it is used, the late one one step.
+        constexpr bool EARLY_B = RING == 1;
+        auto issue_tile = [&](int step, int slot, bool isB) {
 #pragma unroll
-            for (int j = 0; j < LOADS; ++j) {
-                issue(kbeg + p, p, j, false);
-                issue(kbeg + p, p, j, true);
+            for (int j = 0; j < LOADS; ++j) issue(step, slot, j, isB);
+        };
+        auto wrap = [](int x) { return x >= NSLOT ? x - NSLOT : x; };
+        if (nsteps > 0) {
+            issue_tile(kbeg, 0, EARLY_B);
+            issue_tile(kbeg, 1, !EARLY_B);
+            if (nsteps > 1) {
+                issue_tile(kbeg + 1, 2, EARLY_B);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");   // T(0), T(1)
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
+            asm volatile("s_barrier" ::: "memory");
+            read_frags(EARLY_B ? 1 : 0, EARLY_B ? 0 : 1, 0, af0, bf0);
         }
-        wait_steps(min(D, nsteps) - 1);                // this wave's loads of the first step
-        asm volatile("s_barrier" ::: "memory");       // ... and every wave's
-        read_frags(0, 0, af0, bf0);
-    }
-    // settle the scalar loads so the LDS waits inside the loop count precisely
-    // (s_waitcnt lgkmcnt(0), vmcnt and expcnt left open)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-
-    int st = 0;   // stage of step s
-    for (int s = 0; s < nsteps; ++s) {
-        const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        int base = 0;   // slot of T(2s)
+        for (int s = 0; s < nsteps; ++s) {
+            const int s1 = wrap(base + 1), s2 = wrap(base + 2), s3 = wrap(base + 3), s4 = wrap(base + 4);
+            const int sa = EARLY_B ? s1 : base, sb = EARLY_B ? base : s1;        // this step's A and B
+            const int na = EARLY_B ? s3 : s2, nb = EARLY_B ? s2 : s3;            // step s+1's
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            bf8 *ac = (kk & 1) ? af1 : af0, *bc = (kk & 1) ? bf1 : bf0;
-            bf8 *an = (kk & 1) ? af0 : af1, *bn = (kk & 1) ? bf0 : bf1;
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk == 0 && s + D < nsteps) {
-                // the stage of step s+D was last read in step s-1, which every wave
-                // finished before the barrier that ended it
-                const int st_issue = st == 0 ? NSTAGE - 1 : st - 1;
+            for (int kk = 0; kk < KK; ++kk) {
+                bf8 *ac = (kk & 1) ? af1 : af0, *bc = (kk & 1) ? bf1 : bf0;
+                bf8 *an = (kk & 1) ? af0 : af1, *bn = (kk & 1) ? bf0 : bf1;
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk == 0) {
+                    // s3 and s4 held step s-1's tiles, which every wave read before the barrier that ended it
+                    if (s + 1 < nsteps) issue_tile(kbeg + s + 1, s3, !EARLY_B);
+                    if (s + 2 < nsteps) issue_tile(kbeg + s + 2, s4, EARLY_B);
+                }
+                if (kk + 1 < KK) {
+                    read_frags(sa, sb, kk + 1, an, bn);
+                } else {
+                    // step s+1's tiles have landed for this wave (only T(2s+4) may be outstanding);
+                    // after the barrier, for every wave
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    if (s + 2 < nsteps) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+                    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    asm volatile("s_barrier" ::: "memory");
+                    read_frags(na, nb, 0, an, bn);
+                }
 #pragma unroll
-                for (int j = 0; j < LOADS; ++j) {
-                    issue(kbeg + s + D, st_issue, j, false);
-                    issue(kbeg + s + D, st_issue, j, true);
+                for (int i = 0; i < WI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < WI * 4; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+                    if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
+                    if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
                 }
             }
-            if (kk + 1 < KK) {
-                read_frags(st, kk + 1, an, bn);
-            } else {
-                // this wave's fragments of stage st are in registers and its loads
-                // of step s+1 have landed; after the barrier so are everyone's
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                wait_steps(min(s + D, nsteps - 1) - (s + 1));
-                asm volatile("s_barrier" ::: "memory");
-                read_frags(st_next, 0, an, bn);
-            }
-#pragma unroll
-            for (int i = 0; i < WI; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
-            // spread the fragment reads (and in sub-step 0 the global loads) between the MFMAs
-#pragma unroll
-            for (int q = 0; q < WI * 4; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
-                if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
-                if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-            }
+            base = s2;
         }
-        st = st_next;
+    } else {
+        constexpr int D = NSTAGE - 1;   // steps of loads in flight ahead of the one being consumed
+        static_assert(D >= 1 && D <= 4, "wait_steps covers up to three outstanding steps");
+        if (nsteps > 0) {
+            for (int p = 0; p < D && p < nsteps; ++p) {
+#pragma unroll
+                for (int j = 0; j < LOADS; ++j) {
+                    issue(kbeg + p, 2 * p, j, false);
+                    issue(kbeg + p, 2 * p + 1, j, true);
+                }
+            }
+            wait_steps(min(D, nsteps) - 1);                // this wave's loads of the first step
+            asm volatile("s_barrier" ::: "memory");       // ... and every wave's
+            read_frags(0, 1, 0, af0, bf0);
+        }
+        // settle the scalar loads so the LDS waits inside the loop count precisely
+        // (s_waitcnt lgkmcnt(0), vmcnt and expcnt left open)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+
+        int st = 0;   // stage of step s
+        for (int s = 0; s < nsteps; ++s) {
+            const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                bf8 *ac = (kk & 1) ? af1 : af0, *bc = (kk & 1) ? bf1 : bf0;
+                bf8 *an = (kk & 1) ? af0 : af1, *bn = (kk & 1) ? bf0 : bf1;
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk == 0 && s + D < nsteps) {
+                    // the stage of step s+D was last read in step s-1, which every wave
+                    // finished before the barrier that ended it
+                    const int st_issue = st == 0 ? NSTAGE - 1 : st - 1;
+#pragma unroll
+                    for (int j = 0; j < LOADS; ++j) {
+                        issue(kbeg + s + D, 2 * st_issue, j, false);
+                        issue(kbeg + s + D, 2 * st_issue + 1, j, true);
+                    }
+                }
+                if (kk + 1 < KK) {
+                    read_frags(2 * st, 2 * st + 1, kk + 1, an, bn);
+                } else {
+                    // this wave's fragments of stage st are in registers and its loads
+                    // of step s+1 have landed; after the barrier so are everyone's
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    wait_steps(min(s + D, nsteps - 1) - (s + 1));
+                    asm volatile("s_barrier" ::: "memory");
+                    read_frags(2 * st_next, 2 * st_next + 1, 0, an, bn);
+                }
+#pragma unroll
+                for (int i = 0; i < WI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
+                // spread the fragment reads (and in sub-step 0 the global loads) between the MFMAs
+#pragma unroll
+                for (int q = 0; q < WI * 4; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+                    if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
+                    if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                }
+            }
+            st = st_next;
+        }
     }
 
     if constexpr (MODE == OUT_STATS) {
