@@ -493,6 +493,25 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L) : "memory");
     };
 
+    // Spread the fragment reads of the next sub-step (and in sub-step 0 the global loads) between this
+    // sub-step's MFMAs: all reads go out in the first NM - 2 MFMA slots, two to a slot where there are
+    // more reads than slots (the transposing reads of k-major operands), so the last ones have two
+    // MFMAs to land before the next sub-step needs them.
+    auto interleave = [&](int kk) {
+        constexpr int NM = WI * 4;                                      // MFMAs per sub-step
+        constexpr int NR = (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4);       // LDS reads per sub-step
+        constexpr int NS = NM - 2;
+        static_assert(NR <= 2 * NS, "at most two reads per MFMA slot");
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+            const int nr = q < NS ? NR / NS + (q < NR % NS ? 1 : 0) : 0;
+            if (nr == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                   // LDS reads
+            else if (nr == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+    };
+
     const int nsteps = kend - kbeg;
     f16v acc[WI][4];
 #pragma unroll
@@ -555,13 +574,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-                for (int q = 0; q < WI * 4; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
-                    if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
-                    if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-                }
+                interleave(kk);
             }
             base = s2;
         }
@@ -617,14 +630,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
-                // spread the fragment reads (and in sub-step 0 the global loads) between the MFMAs
-#pragma unroll
-                for (int q = 0; q < WI * 4; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
-                    if (q < (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4))
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
-                    if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-                }
+                interleave(kk);
             }
             st = st_next;
         }
