@@ -8,8 +8,9 @@
 //
 // Tiling: a 512-thread workgroup (8 waves, two per SIMD) computes a 256 x 256
 // tile; wave w owns rows 64 (w / 2) .. +64 and columns 128 (w % 2) .. +128 =
-// 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane), so a
-// SIMD always has a second wave to issue MFMAs while one waits.  K advances in
+// 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane; with a
+// k-major B, 128 rows x 64 columns = 4 x 2 tiles), so a SIMD always has a
+// second wave to issue MFMAs while one waits.  K advances in
 // steps of 64.  Each step's A and B tiles (32 KB each) are fetched by
 // buffer->LDS loads into LDS slots: with two stages the loads of step s+1 are
 // issued at the start of step s; with the five-slot ring the streamed operand
@@ -66,7 +67,7 @@ constexpr int BM = 256, BN = 256, BK = LCE_GEMM_BK;
 constexpr int NSTAGE = LCE_GEMM_NSTAGE;              // LDS stages; NSTAGE - 1 steps of loads in flight
 constexpr int NWAVES = LCE_GEMM_NWAVES, NTHR = 64 * NWAVES;
 constexpr int WPS = NWAVES / 4;                      // waves per SIMD
-constexpr int WI = BM / 32 / (NWAVES / 2);           // A fragments (32 rows each) per wave
+constexpr int WI = BM / 32 / (NWAVES / 2);           // A fragments (32 rows each) per wave, K-contiguous B
 constexpr int WROWS = WI * 32;                       // tile rows per wave (two waves per row band)
 constexpr int CPR = BK / 8;                          // 16-byte K chunks per tile row
 constexpr int TILE_BYTES = BM * BK * 2;              // one operand tile of one stage
@@ -375,6 +376,15 @@ __device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI]
 template <int MODE, bool KTAIL, bool SOFTCAP = false, bool A_KM = false, bool B_KN = false, int RING = 0>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))) void gemm_nt_kernel(GemmArgs g) {
     constexpr int NSLOT = nslots(RING);
+    // Wave tile: WIK A fragments x WJ B fragments of 32 x 32.  A k-major B costs two transposing
+    // LDS reads per fragment, which take longer than one plain read of the same bytes, so its waves
+    // take half as many B fragments (64 columns) and twice as many A fragments (128 rows).
+    constexpr int WJ = B_KN ? 2 : 4;                    // B fragments per wave
+    constexpr int WAVES_N = BN / (WJ * 32);             // waves across the tile's columns
+    constexpr int WIK = BM / 32 / (NWAVES / WAVES_N);   // A fragments per wave
+    constexpr int WRK = WIK * 32;                       // tile rows per wave
+    static_assert(NWAVES % WAVES_N == 0 && WIK >= 1, "wave tiling");
+    static_assert(!B_KN || (MODE != OUT_STATS && MODE != OUT_GRAD), "the epilogues take 64 x 128 wave tiles");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[lds_bytes(RING)];
 
     // XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs;
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     // K-contiguous operands: the descriptors cover exactly the tile's valid rows, so rows past M or N
     // read as zeros.  k-major operands ([K][rows], A_KM / B_KN): the descriptor starts at the tile's
     // first column and covers rows k < K, so rows past K read as zeros; columns past M or N are masked
@@ -465,20 +475,20 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
         const unsigned char *Bt = lds + slot_b * TILE_BYTES;
         const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < WI; ++i) {
+        for (int i = 0; i < WIK; ++i) {
             if constexpr (A_KM) {
-                af[i] = km_frag(At, kk, wm * WROWS + i * 32, lane);
+                af[i] = km_frag(At, kk, wm * WRK + i * 32, lane);
             } else {
-                const int r = wm * WROWS + i * 32 + (lane & 31);
+                const int r = wm * WRK + i * 32 + (lane & 31);
                 af[i] = *reinterpret_cast<const bf8 *>(At + (r * CPR + (c ^ swz(r))) * 16);
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < WJ; ++j) {
             if constexpr (B_KN) {
-                bfr[j] = km_frag(Bt, kk, wn * 128 + j * 32, lane);
+                bfr[j] = km_frag(Bt, kk, wn * WJ * 32 + j * 32, lane);
             } else {
-                const int r = wn * 128 + j * 32 + (lane & 31);
+                const int r = wn * WJ * 32 + j * 32 + (lane & 31);
                 bfr[j] = *reinterpret_cast<const bf8 *>(Bt + (r * CPR + (c ^ swz(r))) * 16);
             }
         }
@@ -498,8 +508,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
     // more reads than slots (the transposing reads of k-major operands), so the last ones have two
     // MFMAs to land before the next sub-step needs them.
     auto interleave = [&](int kk) {
-        constexpr int NM = WI * 4;                                      // MFMAs per sub-step
-        constexpr int NR = (A_KM ? 2 * WI : WI) + (B_KN ? 8 : 4);       // LDS reads per sub-step
+        constexpr int NM = WIK * WJ;                                    // MFMAs per sub-step
+        constexpr int NR = (A_KM ? 2 * WIK : WIK) + (B_KN ? 2 * WJ : WJ);   // LDS reads per sub-step
         constexpr int NS = NM - 2;
         static_assert(NR <= 2 * NS, "at most two reads per MFMA slot");
 #pragma unroll
@@ -513,12 +523,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
     };
 
     const int nsteps = kend - kbeg;
-    f16v acc[WI][4];
+    f16v acc[WIK][WJ];
 #pragma unroll
-    for (int i = 0; i < WI; ++i)
+    for (int i = 0; i < WIK; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (f16v){};
-    bf8 af0[WI], bf0[4], af1[WI], bf1[4];
+        for (int j = 0; j < WJ; ++j) acc[i][j] = (f16v){};
+    bf8 af0[WIK], bf0[WJ], af1[WIK], bf1[WJ];
     if constexpr (RING != 0) {
         // Operand tiles in request order: T(2s) is the early operand of step s (B for RING 1, A for 2),
         // T(2s+1) the other; T(i) lives in slot i mod 5.  At the start of step s the slots of step s-1
@@ -570,9 +580,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
                     read_frags(na, nb, 0, an, bn);
                 }
 #pragma unroll
-                for (int i = 0; i < WI; ++i)
+                for (int i = 0; i < WIK; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < WJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
                 interleave(kk);
             }
@@ -626,9 +636,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
                     read_frags(2 * st_next, 2 * st_next + 1, 0, an, bn);
                 }
 #pragma unroll
-                for (int i = 0; i < WI; ++i)
+                for (int i = 0; i < WIK; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < WJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i], bc[j], acc[i][j], 0, 0, 0);
                 interleave(kk);
             }
@@ -643,14 +653,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
         grad_epilogue<SOFTCAP>(g, acc, lds, m0, n0, wm, wn, lane);
         return;
     }
-    // epilogue: lane holds column n0 + wn*128 + j*32 + lane%32 of rows
-    // m0 + wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4
-    const int col_base = n0 + wn * 128 + (lane & 31);
-    const int row_base = m0 + wm * WROWS + (lane >> 5) * 4;
+    // epilogue: lane holds column n0 + wn*32 WJ + j*32 + lane%32 of rows
+    // m0 + wm*32 WIK + i*32 + (r/4)*8 + (lane/32)*4 + r%4
+    const int col_base = n0 + wn * WJ * 32 + (lane & 31);
+    const int row_base = m0 + wm * WRK + (lane >> 5) * 4;
 #pragma unroll
-    for (int i = 0; i < WI; ++i) {
+    for (int i = 0; i < WIK; ++i) {
 #pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
+        for (int jh = 0; jh < WJ / 2; ++jh) {
             float old[2][16];
             if constexpr (MODE == OUT_F32_ACC) {
                 // all loads of this group are issued before any of its stores
