@@ -8,14 +8,16 @@
 //
 // Layout of the work: a row of at most 4096 16-byte vectors (bf16 V <= 32768,
 // fp32 V <= 16384) is held by P waves, KV vectors per lane, in VGPRs; a
-// 1024-thread workgroup (16 waves, one per CU) holds 16 / P rows at a time.
+// 512-thread workgroup (8 waves, two per CU) holds 8 / P rows at a time.
 // With all 1024 threads on one row, as the long-row kernel does, a row this
 // short keeps most threads idle and pays a workgroup-wide combine per few
 // kilobytes.  Here a row's statistics combine with DPP exchanges inside its
 // waves, plus (P > 1) one LDS exchange between its waves per row step; with
 // P = 1 the waves never wait for each other inside the row loop.  Row sets are
-// walked statically (workgroup b takes row sets b, b + G, ...).  One workgroup
-// per CU keeps the per-call label count and completion ticket to one per CU.
+// walked statically (workgroup b takes row sets b, b + G, ...).  Two workgroups
+// per CU: while one waits for its row set's loads the other computes and
+// stores (one 1024-thread workgroup per CU was 3-6% slower on 134 MB calls);
+// few enough that every workgroup counting all the labels stays cheap.
 //
 // Every workgroup counts the labels itself first (the mean's scale needs
 // n_valid before any gradient is written; the labels are read from L2).  The
@@ -29,7 +31,10 @@
 namespace lce {
 namespace dev {
 
-constexpr int kMrThreads = 1024;
+#ifndef LCE_MR_THREADS
+#define LCE_MR_THREADS 512
+#endif
+constexpr int kMrThreads = LCE_MR_THREADS;
 constexpr int kMrWaves = kMrThreads / 64;
 
 template <bool BF16, int P, int KV, bool SOFTCAP, bool ARGMAX, bool SMOOTH>
