@@ -183,7 +183,7 @@ hipError_t transpose(const void *in, int64_t ld_in, void *out, int64_t ld_out, i
 template <int MODE, bool SOFTCAP = false, bool B_KN = false>
 void launch_gemm(const GemmArgs &g, bool ktail, hipStream_t st) {
     constexpr int R = B_KN ? gemm::kRingKn : gemm::kRingDefault;
-    const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u), block(gemm::NTHR);
+    const dim3 grid(static_cast<unsigned>(g.tiles_per_xcd) * 8u), block(64 * gemm::waves_of(B_KN));
     if (ktail) hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, true, SOFTCAP, false, B_KN, R>), grid, block, 0, st, g);
     else hipLaunchKernelGGL((gemm::gemm_nt_kernel<MODE, false, SOFTCAP, false, B_KN, R>), grid, block, 0, st, g);
 }

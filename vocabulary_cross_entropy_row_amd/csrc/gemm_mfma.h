@@ -8,10 +8,10 @@
 //
 // Tiling: a 512-thread workgroup (8 waves, two per SIMD) computes a 256 x 256
 // tile; wave w owns rows 64 (w / 2) .. +64 and columns 128 (w % 2) .. +128 =
-// 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane; with a
-// k-major B, 128 rows x 64 columns = 4 x 2 tiles), so a SIMD always has a
-// second wave to issue MFMAs while one waits.  K advances in
-// steps of 64.  Each step's A and B tiles (32 KB each) are fetched by
+// 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane), so a
+// SIMD always has a second wave to issue MFMAs while one waits.  With a k-major
+// B the workgroup has 1024 threads (16 waves, four per SIMD) of 64 x 64 = 2 x 2
+// tiles.  K advances in steps of 64.  Each step's A and B tiles (32 KB each) are fetched by
 // buffer->LDS loads into LDS slots: with two stages the loads of step s+1 are
 // issued at the start of step s; with the five-slot ring the streamed operand
 // (B) of step s+2 goes out at the start of step s as well, into the fifth slot,
@@ -57,6 +57,9 @@ namespace gemm {
 #ifndef LCE_GEMM_NWAVES
 #define LCE_GEMM_NWAVES 8
 #endif
+#ifndef LCE_GEMM_NWAVES_KN
+#define LCE_GEMM_NWAVES_KN 16
+#endif
 #ifndef LCE_GEMM_RING
 #define LCE_GEMM_RING 1
 #endif
@@ -65,8 +68,9 @@ namespace gemm {
 #endif
 constexpr int BM = 256, BN = 256, BK = LCE_GEMM_BK;
 constexpr int NSTAGE = LCE_GEMM_NSTAGE;              // LDS stages; NSTAGE - 1 steps of loads in flight
-constexpr int NWAVES = LCE_GEMM_NWAVES, NTHR = 64 * NWAVES;
-constexpr int WPS = NWAVES / 4;                      // waves per SIMD
+constexpr int NWAVES = LCE_GEMM_NWAVES;              // waves of a K-contiguous GEMM's workgroup
+constexpr int NWAVES_KN = LCE_GEMM_NWAVES_KN;        // ... and of one that reads B k-major
+constexpr int waves_of(bool b_kn) { return b_kn ? NWAVES_KN : NWAVES; }
 constexpr int WI = BM / 32 / (NWAVES / 2);           // A fragments (32 rows each) per wave, K-contiguous B
 constexpr int WROWS = WI * 32;                       // tile rows per wave (two waves per row band)
 constexpr int CPR = BK / 8;                          // 16-byte K chunks per tile row
@@ -81,13 +85,12 @@ constexpr int kRingKn = LCE_GEMM_RING_KN;      // ... and of the GEMM that reads
 constexpr int nslots(int ring) { return ring ? 5 : 2 * NSTAGE; }
 constexpr int lds_bytes(int ring) { return nslots(ring) * TILE_BYTES; }
 constexpr int NBLK = TILE_BYTES / 1024;              // one-KB load blocks per operand tile
-constexpr int LOADS = NBLK / NWAVES;                 // per wave per operand per step
 constexpr int KK = BK / 16;                          // MFMA K sub-steps per step
 constexpr int kBufWord3 = 0x00020000;                // gfx9-family buffer descriptor word 3
-static_assert(lds_bytes(0) <= 160 * 1024 && lds_bytes(1) <= 160 * 1024 && LOADS >= 1 && (CPR == 4 || CPR == 8),
+static_assert(lds_bytes(0) <= 160 * 1024 && lds_bytes(1) <= 160 * 1024 && NBLK >= NWAVES_KN && (CPR == 4 || CPR == 8),
               "unsupported GEMM staging");
 static_assert(kRingDefault == 0 || NSTAGE == 2, "the ring replaces the two stages");
-static_assert(NWAVES == 8 || NWAVES == 4, "two wave columns of 128 and 4 or 2 wave rows");
+static_assert((NWAVES == 8 || NWAVES == 4) && (NWAVES_KN == 16 || NWAVES_KN == 8), "wave counts");
 
 enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_ACC = 2, OUT_STATS = 3, OUT_GRAD = 4 };
 
@@ -374,16 +377,18 @@ __device__ __forceinline__ void grad_epilogue(const GemmArgs &g, f16v (&acc)[WI]
 // KTAIL: K is not a multiple of BK, so each load checks its K column; otherwise
 // the K position rides in the scalar offset and the per-lane offsets are fixed.
 template <int MODE, bool KTAIL, bool SOFTCAP = false, bool A_KM = false, bool B_KN = false, int RING = 0>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))) void gemm_nt_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * waves_of(B_KN)) __attribute__((amdgpu_waves_per_eu(waves_of(B_KN) / 4, waves_of(B_KN) / 4))) void gemm_nt_kernel(GemmArgs g) {
     constexpr int NSLOT = nslots(RING);
-    // Wave tile: WIK A fragments x WJ B fragments of 32 x 32.  A k-major B costs two transposing
-    // LDS reads per fragment, which take longer than one plain read of the same bytes, so its waves
-    // take half as many B fragments (64 columns) and twice as many A fragments (128 rows).
+    constexpr int NW = waves_of(B_KN);                  // waves of this workgroup
+    constexpr int LOADS = NBLK / NW;                    // 1 KB loads per wave per operand per step
+    // Wave tile: WIK A fragments x WJ B fragments of 32 x 32.  With a k-major B (two transposing
+    // LDS reads per fragment) the workgroup has four waves per SIMD of 2 x 2 fragments: measured
+    // faster there, slower for the K-contiguous GEMMs.
     constexpr int WJ = B_KN ? 2 : 4;                    // B fragments per wave
     constexpr int WAVES_N = BN / (WJ * 32);             // waves across the tile's columns
-    constexpr int WIK = BM / 32 / (NWAVES / WAVES_N);   // A fragments per wave
+    constexpr int WIK = BM / 32 / (NW / WAVES_N);       // A fragments per wave
     constexpr int WRK = WIK * 32;                       // tile rows per wave
-    static_assert(NWAVES % WAVES_N == 0 && WIK >= 1, "wave tiling");
+    static_assert(NW % WAVES_N == 0 && WIK >= 1 && LOADS >= 1, "wave tiling");
     static_assert(!B_KN || (MODE != OUT_STATS && MODE != OUT_GRAD), "the epilogues take 64 x 128 wave tiles");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[lds_bytes(RING)];
 
@@ -429,17 +434,21 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
 
     // this wave's load blocks: byte offsets at k = 0 and their K columns (K-contiguous), or their
     // column validity (k-major: block b holds k-rows 2b, 2b+1 of 32 swizzled 16-byte chunks)
-    uint32_t voffA[LOADS], voffB[LOADS];
-    int kcol[LOADS];
-    bool okA[LOADS], okB[LOADS];
+    // (arrays of a bound that does not depend on the template arguments: with a dependent
+    // bound the host pass leaves some instantiations' launch stubs undefined)
+    constexpr int kMaxLoads = NBLK / 4;
+    static_assert(LOADS <= kMaxLoads, "load slots");
+    uint32_t voffA[kMaxLoads], voffB[kMaxLoads];
+    int kcol[kMaxLoads];
+    bool okA[kMaxLoads], okB[kMaxLoads];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-        const int r = (j * NWAVES + wave) * (64 / CPR) + lane / CPR;
+        const int r = (j * NW + wave) * (64 / CPR) + lane / CPR;
         const int c = (lane % CPR) ^ swz(r);
         kcol[j] = c * 8;
         voffA[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(g.lda) * 2u + c * 16u;
         voffB[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(g.ldb) * 2u + c * 16u;
-        const int kr = 2 * (j * NWAVES + wave) + (lane >> 5);
+        const int kr = 2 * (j * NW + wave) + (lane >> 5);
         const int kc = (lane & 31) ^ kmswz(kr);
         if constexpr (A_KM) {
             voffA[j] = (static_cast<uint32_t>(kr) * static_cast<uint32_t>(g.lda) + kc * 8u) * 2u;
@@ -453,7 +462,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
 
     // load j of one operand of step `step` into operand slot `slot`
     auto issue = [&](int step, int slot, int j, bool isB) {
-        unsigned char *dst = lds + slot * TILE_BYTES + (j * NWAVES + wave) * 1024;
+        unsigned char *dst = lds + slot * TILE_BYTES + (j * NW + wave) * 1024;
         const int k0 = step * BK;
         if ((isB && B_KN) || (!isB && A_KM)) {
             // k-major: the step's rows are k0 .. k0 + 63 (past K: outside the descriptor)
@@ -511,12 +520,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(WPS, WPS))
         constexpr int NM = WIK * WJ;                                    // MFMAs per sub-step
         constexpr int NR = (A_KM ? 2 * WIK : WIK) + (B_KN ? 2 * WJ : WJ);   // LDS reads per sub-step
         constexpr int NS = NM - 2;
-        static_assert(NR <= 2 * NS, "at most two reads per MFMA slot");
+        static_assert(NR <= 4 * NS, "at most four reads per MFMA slot");
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
             const int nr = q < NS ? NR / NS + (q < NR % NS ? 1 : 0) : 0;
-            if (nr == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                   // LDS reads
+            if (nr == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                   // LDS reads
+            else if (nr == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            else if (nr == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             else if (nr == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             if (kk == 0 && q < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
         }
