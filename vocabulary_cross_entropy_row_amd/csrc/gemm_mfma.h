@@ -176,6 +176,36 @@ __device__ __forceinline__ int epi_row(int wm, int i, int r, int lane) {
     return wm * WROWS + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
+// Reductions over the 32 lanes of each half-wave (the lanes that share an accumulator row):
+// four DPP steps leave every 16-lane row holding its row's result, then one swizzle exchanges
+// rows 0 and 1 (2 and 3) of each half; every lane ends with its half's result.
+constexpr int kSwzXor16 = 0x401F;   // ds_swizzle bit mode: lane ^ 16 within each 32
+__device__ __forceinline__ float swz16_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwzXor16));
+}
+__device__ __forceinline__ float half_max(float v) {
+    v = fmaxf(v, dev::dpp_f<dev::kDppXor1>(v));
+    v = fmaxf(v, dev::dpp_f<dev::kDppXor2>(v));
+    v = fmaxf(v, dev::dpp_f<dev::kDppHalfMirror>(v));
+    v = fmaxf(v, dev::dpp_f<dev::kDppMirror>(v));
+    return fmaxf(v, swz16_f(v));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    v += dev::dpp_f<dev::kDppXor1>(v);
+    v += dev::dpp_f<dev::kDppXor2>(v);
+    v += dev::dpp_f<dev::kDppHalfMirror>(v);
+    v += dev::dpp_f<dev::kDppMirror>(v);
+    return v + swz16_f(v);
+}
+// (value, first index) of each half-wave, larger value first, then smaller index
+__device__ __forceinline__ void half_argmax(float &v, int &i) {
+    dev::argmax_step<dev::kDppXor1>(v, i);
+    dev::argmax_step<dev::kDppXor2>(v, i);
+    dev::argmax_step<dev::kDppHalfMirror>(v, i);
+    dev::argmax_step<dev::kDppMirror>(v, i);
+    dev::argmax_combine(v, i, swz16_f(v), __builtin_amdgcn_ds_swizzle(i, kSwzXor16));
+}
+
 // One stats record per row of the tile (columns [n0, n0 + 256) of the vocabulary).
 template <bool SOFTCAP>
 __device__ __forceinline__ void stats_epilogue(const GemmArgs &g, f16v (&acc)[WI][4], unsigned char *lds, int m0,
@@ -227,14 +257,10 @@ __device__ __forceinline__ void stats_epilogue(const GemmArgs &g, f16v (&acc)[WI
             }
             // over the 32 lanes that share each row
 #pragma unroll
-            for (int o = 16; o > 0; o >>= 1)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    lm[u] = fmaxf(lm[u], __shfl_xor(lm[u], o, 64));
-                    const float v2 = __shfl_xor(lx[u], o, 64);
-                    const int i2 = __shfl_xor(li[u], o, 64);
-                    dev::argmax_combine(lx[u], li[u], v2, i2);
-                }
+            for (int u = 0; u < 8; ++u) {
+                lm[u] = half_max(lm[u]);
+                half_argmax(lx[u], li[u]);
+            }
             float sx[8], se[8], sz[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -260,13 +286,11 @@ __device__ __forceinline__ void stats_epilogue(const GemmArgs &g, f16v (&acc)[WI
                 }
             }
 #pragma unroll
-            for (int o = 16; o > 0; o >>= 1)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    sx[u] += __shfl_xor(sx[u], o, 64);
-                    se[u] += __shfl_xor(se[u], o, 64);
-                    sz[u] += __shfl_xor(sz[u], o, 64);
-                }
+            for (int u = 0; u < 8; ++u) {
+                sx[u] = half_sum(sx[u]);
+                se[u] = half_sum(se[u]);
+                sz[u] = half_sum(sz[u]);
+            }
             if ((lane & 31) == 0) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
