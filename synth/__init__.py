@@ -83,13 +83,16 @@ FLCE_WORKLOADS = {w.name: w for w in (C5, C5_SMALL)}
 
 # The vocabulary sweep of the cross-entropy op (bench only): sequence 2048 x batch 4 tokens over
 # vocabularies from 4K to 128K (the Liger CE micro-bench's setup), one vocabulary-parallel rank's
-# shard of the 128K vocabulary at 8 ranks ([2048, 16384]), and an odd vocabulary (50257, the GPT-2
-# tokenizer's size), whose rows do not start on 16-byte boundaries.  sigma 2, 5% ignored, mean reduction.
+# shard of the 128K vocabulary at 8, 4 and 2 ranks ([2048, 16384], [2048, 32768], [2048, 65536]),
+# and an odd vocabulary (50257, the GPT-2 tokenizer's size), whose rows do not start on 16-byte
+# boundaries.  sigma 2, 5% ignored, mean reduction.
 SWEEP = {w.name: w for w in (
     [CEWorkload(f"ce_bf16_8192x{v}", 1100 + i, 8192, v, "bf16", 2.0, 0.05)
      for i, v in enumerate((4096, 16384, 32768, 65536, 131072))]
     + [CEWorkload("ce_bf16_2048x16384", 1110, 2048, 16384, "bf16", 2.0, 0.05),
-       CEWorkload("ce_bf16_2048x50257", 1111, 2048, 50257, "bf16", 2.0, 0.05)])}
+       CEWorkload("ce_bf16_2048x50257", 1111, 2048, 50257, "bf16", 2.0, 0.05),
+       CEWorkload("ce_bf16_2048x32768", 1112, 2048, 32768, "bf16", 2.0, 0.05),
+       CEWorkload("ce_bf16_2048x65536", 1113, 2048, 65536, "bf16", 2.0, 0.05)])}
 ALL_CE_WORKLOADS = {**WORKLOADS, **SWEEP}
 
 
