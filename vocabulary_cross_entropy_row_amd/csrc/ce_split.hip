@@ -125,16 +125,18 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
     Part p;
     float zy = 0.0f;
     // two batches of loads in flight: the next batch goes out before this one is used
-    // (past the row, on the last pass too, the descriptor returns zeros without a memory access)
+    // (past the row, on the last pass too, the descriptor returns zeros without a memory access).
+    // Default cache policy, not non-temporal: the shard may stay in the 256 MB Infinity Cache for
+    // the gradient pass, which reads it again.
     u32x4 v[kStatsAhead];
 #pragma unroll
     for (int u = 0; u < kStatsAhead; ++u)
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (u * NTS + tid) * 16, 0, 2);
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (u * NTS + tid) * 16, 0, 0);
     for (int base = 0; base < nvec; base += NTS * kStatsAhead) {
         u32x4 nx[kStatsAhead];
 #pragma unroll
         for (int u = 0; u < kStatsAhead; ++u)
-            nx[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + (kStatsAhead + u) * NTS + tid) * 16, 0, 2);
+            nx[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + (kStatsAhead + u) * NTS + tid) * 16, 0, 0);
 #pragma unroll
         for (int u = 0; u < kStatsAhead; ++u) {
             const int vi = base + u * NTS + tid;
