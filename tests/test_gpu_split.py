@@ -196,6 +196,49 @@ def test_split_edge_cases():
     assert rows.counts.cpu().tolist() == [0, 0, 0] and float(rows.loss_out.cpu()[0]) == 0.0
 
 
+@pytest.mark.parametrize("n,widths", [(1025, [32, 32]), (3000, [24, 40, 64]), (2048, [16] * 8),
+                                        (4099, [8] * 16), (16385, [64]), (20000, [32, 32])])
+def test_split_combine_many_rows(n, widths):
+    """More rows than one workgroup covers in a pass (the combine then spreads over many workgroups
+    and the last one folds the counts and the loss): every output against the oracle, on the one- and
+    many-workgroup forms (the first runs when argmax is not asked for), with counts holding stale and
+    arbitrary words before the call, twice in a row, the second call smaller."""
+    rng = np.random.default_rng([n, len(widths)])
+    V = int(sum(widths))
+    offs = np.concatenate([[0], np.cumsum(widths)]).astype(int)
+    orc = oracle.default()
+    for m, fill in ((n, [-1, -1, -1]), (n - 517, [3, 12345, 9])):
+        x = synth.f32_to_bf16_bits((rng.standard_normal((m, V)) * 3).astype(np.float32))
+        y = _labels(rng, m, V, bad=6)
+        buf, lab = to_dev(x), torch.from_numpy(y).to(DEV)
+        stats = torch.stack([lce.lce_ce_stats(buf[:, offs[k]:offs[k + 1]], lab, v_offset=int(offs[k]))
+                             for k in range(len(widths))]).contiguous()
+        f = lambda: torch.empty(m, dtype=torch.float32, device=DEV)  # noqa: E731
+        res = []
+        for with_argmax in (True, True, False):
+            out = lce.SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=DEV), f(), f(),
+                                torch.empty(m, dtype=torch.int64, device=DEV) if with_argmax else None,
+                                torch.tensor(fill, dtype=torch.int64, device=DEV))
+            res.append(lce.lce_ce_combine(stats, lab, V, label_smoothing=0.05, out=out))
+        torch.cuda.synchronize()
+        o = orc.ce(x, y, V=V, label_smoothing=0.05, want_grad=False)
+        st = orc.row_stats(x, y, V=V)
+        nv, nb = orc.count(y, V)
+        for r in res:
+            check_loss(r.loss_tok.cpu().numpy(), o["loss_tok"], "loss_tok")
+            check_loss(r.lse.cpu().numpy(), st["lse"], "lse")
+            check_loss(r.logprob.cpu().numpy(), st["logp"], "logprob")
+            ent = r.entropy.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(ent - st["entropy"]) <= 1e-4 * np.maximum(1.0, np.abs(st["lse"])))
+            check_loss(float(r.loss_out.cpu()[0]), o["loss_out"], "loss_out")
+            assert r.counts.cpu().tolist() == [nv, int(o["counts"][1]), nb]
+        assert np.array_equal(res[0].argmax.cpu().numpy(), o["argmax"]), "argmax differs"
+        for name in ("lse", "one_minus_py", "loss_tok", "logprob", "entropy", "argmax", "loss_out"):
+            assert torch.equal(getattr(res[0], name), getattr(res[1], name)), f"{name} differs between calls"
+        for name in ("lse", "one_minus_py", "loss_tok", "logprob", "entropy"):
+            assert torch.equal(getattr(res[0], name), getattr(res[2], name)), f"{name}: forms differ"
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("tp", [1, 8])
 def test_split_full_size(tp):

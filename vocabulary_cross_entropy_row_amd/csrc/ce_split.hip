@@ -284,6 +284,67 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float *stats, int
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One row's results from its records over at most a few shards: eight shards'
+// records in flight at a time (clamped to the last shard), merged in ascending
+// shard order.
+struct RowOut {
+    float lse, q, loss, logp, ent;
+    int64_t am;
+    bool valid;
+};
+__device__ __forceinline__ RowOut combine_row(const float *stats, int64_t shards, int64_t shard_stride,
+                                              int64_t row_stride, int64_t i, int64_t y, int64_t V,
+                                              int64_t ignore_index, float eps) {
+    Part t;
+    float zy = 0.0f;
+    bool has = false;
+    int64_t am = -1;
+    const float4 *rec = reinterpret_cast<const float4 *>(stats + i * row_stride * 8);
+    const int64_t step = shard_stride * 2;   // float4s per shard
+    constexpr int kBatch = 8;
+    for (int64_t k0 = 0; k0 < shards; k0 += kBatch) {
+        float4 ra[kBatch], rb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t k = k0 + u < shards ? k0 + u : shards - 1;
+            ra[u] = rec[k * step];
+            rb[u] = rec[k * step + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (k0 + u >= shards) break;
+            combine(t, ra[u].x, ra[u].y, ra[u].z);
+            t.zs += ra[u].w;
+            if (rb[u].x > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
+                t.amv = rb[u].x;
+                am = __float_as_int(rb[u].y);
+            }
+            if (rb[u].w != 0.0f) {
+                zy = rb[u].z;
+                has = true;
+            }
+        }
+    }
+    RowOut o;
+    o.valid = y != ignore_index && y >= 0 && y < V;
+    const float ey = has ? dev::exp2_fast((zy - t.m) * kLog2e) : 0.0f;
+    const float S = t.s + ey;
+    o.lse = t.m + logf(S);
+    o.q = o.valid ? t.s / S : 0.0f;
+    o.loss = o.valid ? o.lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
+    o.logp = o.valid ? zy - o.lse : 0.0f;
+    o.ent = o.lse - fmaf(ey, zy, t.e) / S;   // -sum p log p = lse - sum p z
+    o.am = am;
+    return o;
+}
+
+// reduction 1 (mean over valid labels), 2 (sum), else 0
+__device__ __forceinline__ float reduce_loss(double tot, long long n_valid, int reduction) {
+    if (reduction == 1) return n_valid > 0 ? static_cast<float>(tot / static_cast<double>(n_valid)) : 0.0f;
+    if (reduction == 2) return static_cast<float>(tot);
+    return 0.0f;
+}
+
 // The whole combine in one workgroup, for up to kCombineOneMaxRows rows of a
 // few shards: row outputs, label counts, n_correct and the reduced loss, with
 // no atomics and no second launch.  Thread t takes rows t, t + 1024, ...; the
@@ -301,55 +362,20 @@ __global__ __launch_bounds__(kCombineOneThreads) void ce_combine_one_kernel(
     double acc = 0.0;
     long long nv = 0, nc = 0, nb = 0;
     for (int64_t i = tid; i < n; i += kCombineOneThreads) {
-        Part t;
-        float zy = 0.0f;
-        bool has = false;
-        int64_t am = -1;
-        const float4 *rec = reinterpret_cast<const float4 *>(stats + i * row_stride * 8);
-        const int64_t step = shard_stride * 2;   // float4s per shard
         const int64_t y = labels[i];
-        // eight shards' records in flight at a time (clamped to the last shard), merged in order
-        constexpr int kBatch = 8;
-        for (int64_t k0 = 0; k0 < shards; k0 += kBatch) {
-            float4 ra[kBatch], rb[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t k = k0 + u < shards ? k0 + u : shards - 1;
-                ra[u] = rec[k * step];
-                rb[u] = rec[k * step + 1];
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                if (k0 + u >= shards) break;
-                combine(t, ra[u].x, ra[u].y, ra[u].z);
-                t.zs += ra[u].w;
-                if (rb[u].x > t.amv) {   // shards in ascending vocabulary order: ties keep the earlier
-                    t.amv = rb[u].x;
-                    am = __float_as_int(rb[u].y);
-                }
-                if (rb[u].w != 0.0f) {
-                    zy = rb[u].z;
-                    has = true;
-                }
-            }
-        }
-        const bool valid = y != ignore_index && y >= 0 && y < V;
+        const RowOut o = combine_row(stats, shards, shard_stride, row_stride, i, y, V, ignore_index, eps);
         if (y != ignore_index) {
-            if (valid) ++nv;
+            if (o.valid) ++nv;
             else ++nb;
         }
-        const float ey = has ? dev::exp2_fast((zy - t.m) * kLog2e) : 0.0f;
-        const float S = t.s + ey;
-        const float lse = t.m + logf(S);
-        const float loss = valid ? lse - (1.0f - eps) * zy - eps / static_cast<float>(V) * t.zs : 0.0f;
-        lse_out[i] = lse;
-        if (q_out) q_out[i] = valid ? t.s / S : 0.0f;
-        if (loss_tok) loss_tok[i] = loss;
-        if (logp_out) logp_out[i] = valid ? zy - lse : 0.0f;
-        if (ent_out) ent_out[i] = lse - fmaf(ey, zy, t.e) / S;
-        if (argmax_out) argmax_out[i] = am;
-        if (valid && am == y) ++nc;
-        acc += static_cast<double>(loss);
+        lse_out[i] = o.lse;
+        if (q_out) q_out[i] = o.q;
+        if (loss_tok) loss_tok[i] = o.loss;
+        if (logp_out) logp_out[i] = o.logp;
+        if (ent_out) ent_out[i] = o.ent;
+        if (argmax_out) argmax_out[i] = o.am;
+        if (o.valid && o.am == y) ++nc;
+        acc += static_cast<double>(o.loss);
     }
     acc = dev::wave_sum_d(acc);
     nv = dev::wave_sum_ll(nv);
@@ -372,12 +398,109 @@ __global__ __launch_bounds__(kCombineOneThreads) void ce_combine_one_kernel(
         counts[0] = c[0];
         counts[1] = c[1];
         counts[2] = c[2];
-        if (loss_out) {
-            float out = 0.0f;
-            if (reduction == 1) out = c[0] > 0 ? static_cast<float>(tot / static_cast<double>(c[0])) : 0.0f;
-            else if (reduction == 2) out = static_cast<float>(tot);
-            *loss_out = out;
+        if (loss_out) *loss_out = reduce_loss(tot, c[0], reduction);
+    }
+}
+
+// The same over many workgroups, one row per thread, for more rows than one
+// workgroup covers in a pass (it needs argmax_out, and loss_tok when loss_out is
+// asked for).  The workgroups count their completions in counts[1] (a tagged
+// word, so whatever it held before does not matter; the call overwrites it with
+// n_correct at the end).  The last workgroup to finish counts the labels,
+// compares the stored argmax with them for n_correct, and folds the per-token
+// losses in a fixed order, so the result does not depend on which workgroup is
+// last.  What it reads back (loss_tok, argmax_out) is stored at system scope
+// and acknowledged before the count is drawn, so it reads them past its own L2.
+#ifndef LCE_COMBINE_PAR_THREADS
+#define LCE_COMBINE_PAR_THREADS 256
+#endif
+constexpr int kCombineParThreads = LCE_COMBINE_PAR_THREADS;
+constexpr int kCombineParFold = 8;   // rows per thread in flight in the fold
+__global__ __launch_bounds__(kCombineParThreads) void ce_combine_par_kernel(
+    const float *stats, int64_t shards, int64_t shard_stride, int64_t row_stride, const int64_t *labels, int64_t n,
+    int64_t V, int64_t ignore_index, float eps, int reduction, float *lse_out, float *q_out, float *loss_tok,
+    float *loss_out, float *logp_out, float *ent_out, int64_t *argmax_out, int64_t *counts) {
+    constexpr int NTH = kCombineParThreads;
+    constexpr int NW = NTH / 64;
+    __shared__ double sh_d[NW];
+    __shared__ long long sh_c[3][NW];
+    __shared__ int sh_last;
+    const int tid = threadIdx.x;
+    const unsigned tag = dev::launch_tag();
+    unsigned long long *ticket = reinterpret_cast<unsigned long long *>(counts + 1);
+    if (tid == 0) dev::tagged_claim(ticket, tag);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * NTH + tid;
+    if (i < n) {
+        const int64_t y = labels[i];
+        const RowOut o = combine_row(stats, shards, shard_stride, row_stride, i, y, V, ignore_index, eps);
+        lse_out[i] = o.lse;
+        if (q_out) q_out[i] = o.q;
+        if (logp_out) logp_out[i] = o.logp;
+        if (ent_out) ent_out[i] = o.ent;
+        if (loss_tok) dev::store_through(loss_tok + i, o.loss);
+        __hip_atomic_store(reinterpret_cast<unsigned long long *>(argmax_out + i),
+                           static_cast<unsigned long long>(o.am), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) sh_last = dev::tagged_draw(ticket, tag) == gridDim.x - 1u;
+    __syncthreads();
+    if (!sh_last) return;
+    // fixed order: thread t takes rows t, t + NTH, ... (kCombineParFold in flight), then the
+    // waves in order
+    double acc = 0.0;
+    long long nv = 0, nc = 0, nb = 0;
+    for (int64_t r0 = 0; r0 < n; r0 += kCombineParFold * NTH) {
+        int64_t yv[kCombineParFold];
+        unsigned long long av[kCombineParFold];
+        float lv[kCombineParFold];
+#pragma unroll
+        for (int u = 0; u < kCombineParFold; ++u) {
+            int64_t r = r0 + u * NTH + tid;
+            r = r < n ? r : n - 1;
+            yv[u] = labels[r];
+            av[u] = __hip_atomic_load(reinterpret_cast<unsigned long long *>(argmax_out + r), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
+            lv[u] = loss_tok ? __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned *>(loss_tok) + r,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+                             : 0.0f;
         }
+#pragma unroll
+        for (int u = 0; u < kCombineParFold; ++u) {
+            if (r0 + u * NTH + tid >= n) break;
+            const int64_t y = yv[u];
+            if (y == ignore_index) continue;
+            if (y >= 0 && y < V) {
+                ++nv;
+                if (static_cast<int64_t>(av[u]) == y) ++nc;
+            } else {
+                ++nb;
+            }
+            acc += static_cast<double>(lv[u]);
+        }
+    }
+    acc = dev::wave_sum_d(acc);
+    nv = dev::wave_sum_ll(nv);
+    nc = dev::wave_sum_ll(nc);
+    nb = dev::wave_sum_ll(nb);
+    if ((tid & 63) == 0) {
+        sh_d[tid >> 6] = acc;
+        sh_c[0][tid >> 6] = nv;
+        sh_c[1][tid >> 6] = nc;
+        sh_c[2][tid >> 6] = nb;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        long long c[3] = {0, 0, 0};
+        for (int w = 0; w < NW; ++w) {
+            tot += sh_d[w];
+            for (int j = 0; j < 3; ++j) c[j] += sh_c[j][w];
+        }
+        counts[0] = c[0];
+        counts[2] = c[2];
+        if (loss_out) *loss_out = reduce_loss(tot, c[0], reduction);
+        counts[1] = c[1];   // replaces the completion count
     }
 }
 
@@ -533,6 +656,16 @@ hipError_t launch_ce_combine(const float *stats, int64_t shards, int64_t shard_s
                              float *q, float *loss_tok, float *loss_out, float *logp, float *ent,
                              int64_t *argmax_out, int64_t *counts, hipStream_t st) {
     hipError_t e;
+    // many workgroups for several shards beyond one pass of the one-workgroup form (with one
+    // shard, whose rows are cheap to merge, its two passes cost less than the completion count
+    // and the fold), and for every shape past that form's row limit
+    if (shards <= 16 && argmax_out && (n > kCombineOneMaxRows || (shards > 1 && n > kCombineOneThreads))) {
+        const dim3 grid(static_cast<unsigned>((n + kCombineParThreads - 1) / kCombineParThreads));
+        hipLaunchKernelGGL(ce_combine_par_kernel, grid, dim3(kCombineParThreads), 0, st, stats, shards, shard_stride,
+                           row_stride, labels, n, V, ignore_index, eps, reduction, lse, q, loss_tok, loss_out, logp,
+                           ent, argmax_out, counts);
+        return hipGetLastError();
+    }
     if (shards <= 16 && n <= kCombineOneMaxRows) {
         // one launch does everything (n == 0 included: counts and loss_out become 0)
         hipLaunchKernelGGL(ce_combine_one_kernel, dim3(1), dim3(kCombineOneThreads), 0, st, stats, shards,
