@@ -255,6 +255,20 @@ def test_schedule_many_rows_and_edges(n, V, feat):
         run_and_check(x, y, V, eps=0.1, T=20.0, red="sum", grad_out=[0.7], want_argmax=True)
 
 
+@pytest.mark.parametrize("V,ld", [(30000, 30000), (60000, 60000), (90000, 90000), (110000, 110000),
+                                  (155000, 155000), (170000, 170000), (202048, 202048), (60001, 60003),
+                                  (110001, 110005)])
+def test_softcap_families_many_rows(V, ld):
+    """Softcap rows of every resident family (aligned and unaligned), more rows than workgroups: each
+    round's load for a workgroup's next row goes out right after the round's gradient store, so every
+    row after a workgroup's first is checked element by element."""
+    rng = np.random.default_rng([V, ld, 7])
+    n = 520
+    x = make_logits(rng, n, V, ld, "bf16", sigma=6.0)
+    y = _labels(rng, n, V, ignore_frac=0.05)
+    run_and_check(x, y, V, eps=0.05, T=30.0, red="mean", want_argmax=True)
+
+
 @pytest.mark.parametrize("V,dt", [(8 * 1024 * 18 + 8 * 5, "bf16"), (131072, "bf16"), (60000, "f32")],
                          ids=["bf16-147496", "bf16-131072", "f32-60000"])
 def test_labels_at_round_boundaries(V, dt):

@@ -239,6 +239,65 @@ def test_split_combine_many_rows(n, widths):
             assert torch.equal(getattr(res[0], name), getattr(res[2], name)), f"{name}: forms differ"
 
 
+def test_split_graph_replay():
+    """Eight shards' stats, the many-workgroup combine and the gradients captured in one graph: every
+    replay (fresh logits, counts holding other words in between) gives the eager result bit for bit."""
+    rng = np.random.default_rng(31)
+    n, tp, ws = 2048, 8, 1024
+    V = tp * ws
+    x = synth.f32_to_bf16_bits((rng.standard_normal((n, V)) * 3).astype(np.float32))
+    y = _labels(rng, n, V, bad=4)
+    pristine, lab = to_dev(x), torch.from_numpy(y).to(DEV)
+    bufs = [torch.empty((n, ws), dtype=torch.bfloat16, device=DEV) for _ in range(tp)]
+    stats = torch.empty((tp, n, 8), dtype=torch.float32, device=DEV)
+    f = lambda: torch.empty(n, dtype=torch.float32, device=DEV)  # noqa: E731
+    rows = lce.SplitRows(f(), f(), f(), torch.empty(1, dtype=torch.float32, device=DEV), f(), f(),
+                         torch.empty(n, dtype=torch.int64, device=DEV), torch.empty(3, dtype=torch.int64, device=DEV))
+    go = torch.full((1,), 0.5, dtype=torch.float32, device=DEV)
+
+    def reset():
+        for k in range(tp):
+            bufs[k].copy_(pristine[:, k * ws:(k + 1) * ws])
+        rows.counts.fill_(-1)
+
+    def call():
+        st = torch.cuda.current_stream()
+        for k in range(tp):
+            lce.lce_ce_stats(bufs[k], lab, v_offset=k * ws, stats=stats[k], stream=st)
+        lce.lce_ce_combine(stats, lab, V, label_smoothing=0.1, out=rows, stream=st)
+        for k in range(tp):
+            lce.lce_ce_grad(bufs[k], lab, V, rows, v_offset=k * ws, label_smoothing=0.1, grad_out=go, stream=st)
+
+    def snapshot():
+        return [from_dev(b) for b in bufs] + [getattr(rows, a).cpu().numpy() for a in
+                                              ("lse", "one_minus_py", "loss_tok", "loss_out", "logprob", "entropy",
+                                               "argmax", "counts")]
+
+    reset()
+    call()
+    torch.cuda.synchronize()
+    want = snapshot()
+    o = oracle.ce(x, y, V=V, label_smoothing=0.1, want_grad=False)
+    check_loss(float(want[tp + 3][0]), o["loss_out"], "loss_out")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        call()   # warm-up on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(want, snapshot()):
+            assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("tp", [1, 8])
 def test_split_full_size(tp):

@@ -556,15 +556,25 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         // its slots before computing the stores above, and no other wave uses them).
         // Without the softcap the workgroup first lets its LDS-round stores
         // drain and meets at a barrier, so the next row's loads leave together
-        // (1.3% faster on the label-smoothing workload); the softcap variants
-        // are VALU-heavy and lose 5% to the same barrier, so they skip it.
-#pragma unroll
-        for (int k = 0; k < KL; ++k) grad_round(k);
-        if constexpr (KL > 0 && !SOFTCAP) __syncthreads();
+        // (1.3% faster on the label-smoothing workload).  The softcap variants
+        // are VALU-bound: they lose 5% to that barrier, and there each round's
+        // load for the next row goes out right after the round's gradient store,
+        // so the next row arrives while this one is still being computed (2.5%
+        // faster at 4096 x 202048; on the memory-bound rows the grouped order is
+        // 1-5% faster).  Either order leaves 2 KR memory operations behind the
+        // last LDS-round load, which the wait at the top of pass A counts on.
 #pragma unroll
         for (int k = 0; k < KL; ++k) {
-            issue_round(k, rn);
-            __builtin_amdgcn_sched_barrier(0);
+            grad_round(k);
+            if constexpr (SOFTCAP) issue_round(k, rn);
+        }
+        if constexpr (KL > 0 && !SOFTCAP) __syncthreads();
+        if constexpr (!SOFTCAP) {
+#pragma unroll
+            for (int k = 0; k < KL; ++k) {
+                issue_round(k, rn);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // the row after the next (none to draw once the schedule has run out: a
         // draw still in flight would delay this workgroup's final publish)
@@ -575,11 +585,19 @@ __global__ __launch_bounds__(NT) void ce_rows_kernel(CEArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         // the register rounds, then the next row's register rounds
 #pragma unroll
-        for (int k = KL; k < K; ++k) grad_round(k);
-#pragma unroll
         for (int k = KL; k < K; ++k) {
-            issue_round(k, rn);   // in the order pass A consumes them
-            __builtin_amdgcn_sched_barrier(0);
+            grad_round(k);
+            if constexpr (SOFTCAP) {   // as for the LDS rounds
+                issue_round(k, rn);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (!SOFTCAP) {
+#pragma unroll
+            for (int k = KL; k < K; ++k) {
+                issue_round(k, rn);   // in the order pass A consumes them
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // the target element's own gradient replaces what its round stored
         // (one thread, after that round's store, to the same address)
