@@ -255,6 +255,7 @@ def valu_roofline(valu_insts: float, trans_insts: float, kernel_ns: float) -> di
 
 
 def collect_profiles(workload: str) -> int:
+    import numpy as np
     import synth
     w = synth.ALL_CE_WORKLOADS[workload]
     raw = os.path.join(RAW_PROFILES, workload)
@@ -282,6 +283,16 @@ def collect_profiles(workload: str) -> int:
     fscale, wscale = copy_kib / fc, copy_kib / wc
     traffic = (fk * fscale + wk * wscale) * 1024.0
     valu = {c: counter("valu", c)[0] for c in VALU_COUNTERS}
+    # per dispatch, in launch order: 3 warmup calls, the 10 back-to-back timed steps (what
+    # ms_per_step covers), then the 10 event-timed calls on logits restored just before them
+    trace = sorted((r for r in csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_trace.csv")))
+                    if _ours(r["Kernel_Name"])), key=lambda r: int(r["Start_Timestamp"]))
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace]
+    by_phase = []
+    if len(durs) == 3 + 2 * 10:
+        for name, d in (("warmup", durs[:3]), ("timed_steps", durs[3:13]), ("event_pass", durs[13:])):
+            by_phase.append(f"kernel_ns_{name}: avg {np.mean(d):.1f} median {np.median(d):.1f} "
+                            f"min {min(d)} max {max(d)}")
     kernel_ns = float(ours[0]["AverageNs"]) if ours else float("nan")
     vr = valu_roofline(valu["SQ_INSTS_VALU"], valu["SQ_INSTS_VALU_TRANS_F32"], kernel_ns)
     b = " ".join(base)
@@ -308,6 +319,7 @@ def collect_profiles(workload: str) -> int:
     lines += [
         f"kernel: {ours[0]['Name'] if ours else 'n/a'}",
         f"kernel_avg_ns: {float(ours[0]['AverageNs']):.1f}" if ours else "kernel_avg_ns: n/a",
+        *by_phase,
         f"fetch_kib_per_dispatch: {fk:.1f}   ({nfk} dispatches)",
         f"copy_fetch_kib_per_dispatch: {fc:.1f}   ({nfc} dispatches)",
         f"fetch_scale: {fscale:.4f}",
