@@ -278,6 +278,26 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
         float loss = lse - (1.0f - eps) * zy;
         if constexpr (SMOOTH) loss -= eps * invV * zs;
         if (!valid) loss = 0.0f;
+        // the row outputs go out before the gradient stores, and in the last row set
+        // also this workgroup's n_correct partial: the completion ticket then waits
+        // for these, not for the gradient (see the end of the kernel)
+        if (live && gl == 0) {
+            store_through(a.loss_tok + row, loss);
+            if constexpr (ARGMAX) a.argmax_out[row] = am;
+        }
+        if (base + G * R >= n) {   // this workgroup's last row set (uniform)
+            if constexpr (ARGMAX) correct = wave_sum_ll(correct);
+            if ((tid & 63) == 0) sh_c[2][wave] = ARGMAX ? correct : 0;
+            __syncthreads();
+            if (tid == 0) {
+                long long c = 0;
+#pragma unroll
+                for (int w = 0; w < kMrWaves; ++w) c += sh_c[2][w];
+                __hip_atomic_store(ws_correct(a.workspace) + blockIdx.x, c, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+        asm volatile("" ::: "memory");   // keep those stores ahead of the gradient's
 
         // ---- pass B: the gradient (the same evaluation as the long-row kernel)
         const float ascale = fabsf(scale);
@@ -325,25 +345,14 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
         }
         // the target element's own gradient (same thread, same address, after its vector)
         if (live && valid && owner) EL::template store_one<kNonTemporal>(rp, y, gy);
-        if (live && gl == 0) {
-            store_through(a.loss_tok + row, loss);
-            if constexpr (ARGMAX) a.argmax_out[row] = am;
-        }
     }
 
-    // ---- this workgroup's n_correct partial, then the ticket; the last workgroup
-    // folds the per-token losses and the partials.  Every wave's system-scope
-    // stores are acknowledged before the ticket is taken.
-    if constexpr (ARGMAX) correct = wave_sum_ll(correct);
-    if ((tid & 63) == 0) sh_c[2][wave] = ARGMAX ? correct : 0;
-    __syncthreads();
-    if (tid == 0) {
-        long long c = 0;
-#pragma unroll
-        for (int w = 0; w < kMrWaves; ++w) c += sh_c[2][w];
-        __hip_atomic_store(ws_correct(a.workspace) + blockIdx.x, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // ---- the ticket; the last workgroup folds the per-token losses and the
+    // n_correct partials.  Those were stored at system scope ahead of the last row
+    // set's KV gradient stores (and the target element's one), and a wave's
+    // memory operations complete in issue order, so once at most KV of this wave's
+    // are outstanding its share has landed; the gradient stores drain meanwhile.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KV) : "memory");
     __syncthreads();
     if (tid == 0) {
         tagged_claim(ws_ticket(a.workspace), tag);
