@@ -81,6 +81,9 @@ def parse():
                          "place), wt (also room for W^T), or lean (one chunk per grad_weight group)")
     ap.add_argument("--no-pages-protocol", action="store_true",
                     help="skip the extra per-call timing in the pages' protocol (10 warmups, 3 x 50 samples)")
+    ap.add_argument("--no-event-pass", action="store_true",
+                    help="(profiling runs) skip the event-timed calls of the CE path: the profiler times every "
+                         "kernel itself, and the per-call figures are then the back-to-back steps' average")
     return ap.parse_args()
 
 
@@ -260,7 +263,7 @@ def collect_profiles(workload: str) -> int:
     w = synth.ALL_CE_WORKLOADS[workload]
     raw = os.path.join(RAW_PROFILES, workload)
     os.makedirs(raw, exist_ok=True)
-    base = ["--workload", workload, "--no-cpu-baseline", "--no-pages-protocol"]
+    base = ["--workload", workload, "--no-cpu-baseline", "--no-pages-protocol", "--no-event-pass"]
     _rocprof(["--kernel-trace", "--stats"], os.path.join(raw, "ktrace"), base + ["--steps", "10", "--warmup", "3"], 300)
     _rocprof(["--pmc", "FETCH_SIZE"], os.path.join(raw, "fetch"), base + ["--steps", "5", "--warmup", "2"], 180)
     _rocprof(["--pmc", "WRITE_SIZE"], os.path.join(raw, "write"), base + ["--steps", "5", "--warmup", "2"], 180)
@@ -283,14 +286,14 @@ def collect_profiles(workload: str) -> int:
     fscale, wscale = copy_kib / fc, copy_kib / wc
     traffic = (fk * fscale + wk * wscale) * 1024.0
     valu = {c: counter("valu", c)[0] for c in VALU_COUNTERS}
-    # per dispatch, in launch order: 3 warmup calls, the 10 back-to-back timed steps (what
-    # ms_per_step covers), then the 10 event-timed calls on logits restored just before them
+    # per dispatch, in launch order: 3 warmup calls, then the 10 back-to-back timed steps (what
+    # ms_per_step covers); the profiled runs leave out the event-timed calls
     trace = sorted((r for r in csv.DictReader(open(os.path.join(raw, "ktrace", "run_kernel_trace.csv")))
                     if _ours(r["Kernel_Name"])), key=lambda r: int(r["Start_Timestamp"]))
     durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace]
     by_phase = []
-    if len(durs) == 3 + 2 * 10:
-        for name, d in (("warmup", durs[:3]), ("timed_steps", durs[3:13]), ("event_pass", durs[13:])):
+    if len(durs) == 3 + 10:
+        for name, d in (("warmup", durs[:3]), ("timed_steps", durs[3:13])):
             by_phase.append(f"kernel_ns_{name}: avg {np.mean(d):.1f} median {np.median(d):.1f} "
                             f"min {min(d)} max {max(d)}")
     kernel_ns = float(ours[0]["AverageNs"]) if ours else float("nan")
@@ -869,7 +872,9 @@ def main() -> int:
         # first launch and the final synchronisation (~0.1 ms) is spread thin
         per_buf = w.n * w.V * w.elem_bytes
         args.steps = int(min(100, max(20, 64e9 // per_buf - args.warmup)))
-    nbuf = args.warmup + args.steps
+    # the warmup calls, the back-to-back timed steps and the event-timed calls each get their own
+    # pristine copy, all made here, so no bulk restore runs between the two timed passes
+    nbuf = args.warmup + (1 if args.no_event_pass else 2) * args.steps
     bufs = [torch.empty_like(pristine) for _ in range(nbuf)]
     for b in bufs:
         b.copy_(pristine)
@@ -898,18 +903,20 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # per-call durations (the roofline's): the same steps again on restored logits, HIP events
-    # around each call on the stream it runs on
-    for i in range(args.steps):
-        bufs[args.warmup + i].copy_(pristine)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(bufs[args.warmup + i])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    # per-call durations (the roofline's): as many calls again on their own pristine copies, HIP
+    # events around each call on the stream it runs on
+    if args.no_event_pass:
+        per_call_ms = [ms_per_step]
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(bufs[args.warmup + args.steps + i])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        per_call_ms = [a.elapsed_time(b) for a, b in ev]
     call_ms = float(np.mean(per_call_ms))
     # context, after the timed region: a plain device copy of the same logits (one read + one write of
     # N V b bytes, the same traffic as one call), HIP events around each copy

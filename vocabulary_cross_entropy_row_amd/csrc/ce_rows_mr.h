@@ -364,7 +364,10 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
     // fixed order: thread t sums rows t, t + 256, ... in fp64 (kFold loads in flight), then the
     // waves' sums in wave order
     double acc = 0.0;
-    long long cor = 0;
+    // this thread's first n_correct partial goes out with the first batch of losses
+    // (clamped like them, masked when added)
+    long long cor = __hip_atomic_load(ws_correct(a.workspace) + (tid < G ? tid : 0), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
     for (int64_t r0 = 0; r0 < n; r0 += kFold * kMrThreads) {
         float lv[kFold];
 #pragma unroll
@@ -377,7 +380,8 @@ __global__ __launch_bounds__(kMrThreads) __attribute__((amdgpu_waves_per_eu(4)))
         for (int u = 0; u < kFold; ++u)
             if (r0 + u * kMrThreads + tid < n) acc += static_cast<double>(lv[u]);
     }
-    for (int64_t w = tid; w < G; w += kMrThreads)
+    if (tid >= G) cor = 0;
+    for (int64_t w = tid + kMrThreads; w < G; w += kMrThreads)
         cor += __hip_atomic_load(ws_correct(a.workspace) + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     acc = wave_sum_d(acc);
     cor = wave_sum_ll(cor);
