@@ -147,9 +147,10 @@ __global__ __launch_bounds__(kStatsThreads) void ce_stats_kernel(const void *log
             for (int k = 0; k < E; ++k) {
                 x[k] = EL::get(v[u], k);
                 z[k] = SOFTCAP ? cap.z_of_r(cap.r_of(x[k])) : x[k];
-                rmax = fmaxf(rmax, z[k]);
+                if constexpr (SOFTCAP) rmax = fmaxf(rmax, z[k]);
                 xmax = fmaxf(xmax, x[k]);
             }
+            if constexpr (!SOFTCAP) rmax = fmaxf(xmax, -FLT_MAX);   // z = x: one max chain
             if (xmax > p.amv) {   // vectors come in index order per thread: keep the first
                 int first = E - 1;
 #pragma unroll
