@@ -356,12 +356,14 @@ def test_argmax_entry_point(dt, V, ld):
 
 
 @pytest.mark.parametrize("want_argmax", [True, False], ids=["argmax", "plain"])
-def test_deterministic_replay(want_argmax):
-    """Rows go to workgroups dynamically (first come, first served), so which workgroup
-    handles a row changes from call to call; every output must still be bitwise the same.
-    1024 rows keep every workgroup drawing rows, and 10 % ignored rows exercise the skip."""
+@pytest.mark.parametrize("n,V", [(1024, 32768), (8192, 4096), (2048, 16384)], ids=["rows", "short1", "short4"])
+def test_deterministic_replay(want_argmax, n, V):
+    """Rows go to workgroups dynamically (first come, first served) in the long-row kernel, so which
+    workgroup handles a row changes from call to call, and in every kernel the last workgroup to
+    finish does the fold; every output must still be bitwise the same.  1024 rows of 32768 keep every
+    long-row workgroup drawing rows; 8192 x 4096 and 2048 x 16384 run the short-row kernel (one and
+    four waves per row); 10 % ignored rows exercise the skip."""
     rng = np.random.default_rng(10)
-    n, V = 1024, 32768
     x = make_logits(rng, n, V, V, "bf16")
     y = _labels(rng, n, V)
     ws = torch.zeros(lce.lce_ce_workspace_bytes(n, V), dtype=torch.uint8, device=DEV)
