@@ -112,6 +112,9 @@ SHAPES = [  # (n, V, ld, dtype): register path with full / partial last round, K
     (32, 8 * 1024 + 8 * 37, 8 * 1024 + 8 * 37, "bf16"),
     (16, 32768, 32768 + 64, "bf16"),
     (8, 131072, 131072, "bf16"),
+    (24, 65536, 65536, "bf16"),                                     # half rows of 5 rounds
+    (16, 61448, 61448 + 8, "bf16"),                                 # 5 rounds, the last of one vector
+    (24, 36000, 36000, "f32"),                                      # f32 half rows of 5 rounds
     (6, 8 * 1024 * 18 + 8 * 5, 8 * 1024 * 18 + 8 * 5, "bf16"),    # K=19 (template 20)
     (4, 202048, 202048, "bf16"),                                    # K=25 (template 26)
     (16, 4099, 4099, "bf16"),                                       # generic (V odd)
