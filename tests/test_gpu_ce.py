@@ -150,6 +150,8 @@ SHORT_ROWS = [
     (300, 2048, "bf16"), (300, 4096, "bf16"), (300, 4104, "bf16"), (300, 8192, "bf16"), (300, 8200, "bf16"),
     (300, 16384, "bf16"), (300, 16392, "bf16"), (300, 2048, "f32"), (300, 4096, "f32"), (300, 8192, "f32"),
     (300, 8196, "f32"), (1000, 64, "bf16"), (37, 520, "f32"),
+    # four waves of 16 vectors a lane (calls of at most 4096 rows): full, partial, two row sets
+    (300, 32768, "bf16"), (300, 24000, "bf16"), (1300, 32768, "bf16"), (300, 16384, "f32"), (300, 12000, "f32"),
 ]
 
 
