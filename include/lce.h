@@ -195,7 +195,10 @@ lce_status lce_ce_stats(const void *logits, int64_t ld, lce_dtype dtype, const i
  *   logprob       fp32 [n] or NULL: log p_y = z_y - lse (0 for ignored rows).
  *   entropy       fp32 [n] or NULL: -sum_j p_j log p_j (every row).
  *   argmax_out    int64 [n] or NULL: global first-index argmax.
- *   counts        int64 [3], required: {n_valid, n_correct, n_bad}.
+ *   counts        int64 [3], required: {n_valid, n_correct, n_bad}.  Its prior
+ *                 contents do not matter; while the call runs, counts[1] may
+ *                 hold the workgroups' completion count, replaced by n_correct
+ *                 at the end, so nothing else may use it meanwhile.
  */
 lce_status lce_ce_combine(const float *stats, int64_t shards, const int64_t *labels, int64_t n, int64_t V,
                           int64_t ignore_index, float label_smoothing, lce_reduction reduction, float *lse,
