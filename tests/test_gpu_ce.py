@@ -115,13 +115,18 @@ SHAPES = [  # (n, V, ld, dtype): register path with full / partial last round, K
     (24, 65536, 65536, "bf16"),                                     # half rows of 5 rounds
     (16, 61448, 61448 + 8, "bf16"),                                 # 5 rounds, the last of one vector
     (24, 36000, 36000, "f32"),                                      # f32 half rows of 5 rounds
+    (16, 92160, 92160, "bf16"),                                     # half rows of 6 rounds, exactly full
+    (12, 100352, 100352 + 8, "bf16"),                               # 7 rounds
+    (8, 115200, 115200, "bf16"),                                    # 8 rounds
+    (12, 50000, 50000, "f32"),                                      # f32, 7 rounds
     (6, 8 * 1024 * 18 + 8 * 5, 8 * 1024 * 18 + 8 * 5, "bf16"),    # K=19 (template 20)
     (4, 202048, 202048, "bf16"),                                    # K=25 (template 26)
     (16, 4099, 4099, "bf16"),                                       # generic (V odd)
     (16, 4096, 4100, "f32"),                                        # fast: ld multiple of 4
     (16, 4096, 4098, "bf16"),                                       # generic (ld not a multiple of 8)
     (16, 1000, 1000, "f32"),
-    (8, 60000, 60000, "f32"),                                       # f32 K=15
+    (8, 60000, 60000, "f32"),                                       # f32 half rows of 8 rounds
+    (6, 80000, 80000, "f32"),                                       # f32 resident row, K=20
     (4, 120000, 120000, "f32"),                                     # f32 too wide -> generic
     (2, 204800, 204800, "bf16"),                                    # widest resident bf16 row (K=25)
     (2, 204808, 204808, "bf16"),                                    # one vector more -> generic

@@ -31,6 +31,7 @@ CASES = [
     ("ce_rows_inst.hip", ["-DLCE_BF16=1", "-DLCE_KR=4", "-DLCE_KL=8", "-DLCE_UA=1"]),
     ("ce_rows_half.hip", ["-DLCE_BF16=1", "-DLCE_KH=9"]),
     ("ce_rows_half.hip", ["-DLCE_BF16=0", "-DLCE_KH=5"]),
+    ("ce_rows_half.hip", ["-DLCE_BF16=1", "-DLCE_KH=7"]),
     ("ce_rows_mr.hip", ["-DLCE_BF16=1", "-DLCE_P=4", "-DLCE_KV=8"]),
     ("ce_rows_mr.hip", ["-DLCE_BF16=1", "-DLCE_P=4", "-DLCE_KV=16"]),
     ("ce_split.hip", []),

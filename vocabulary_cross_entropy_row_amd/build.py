@@ -26,7 +26,7 @@ UA_FAMILIES = [(1, 0), (2, 0), (4, 0), (8, 0), (4, 8), (8, 8)]
 # Short-row kernel families (waves per row, 16-byte vectors per lane), ce_rows_mr.hip.
 MR_FAMILIES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 8), (4, 8), (4, 16)]
 # Half-row kernel families (rounds of 960 vectors per half row), ce_rows_half.hip.
-HALF_FAMILIES = [5, 9, 10]
+HALF_FAMILIES = [5, 6, 7, 8, 9, 10]
 UNITS = [("ce_kernels.hip", [], "ce_kernels"), ("flce.hip", [], "flce"), ("ce_split.hip", [], "ce_split"), ("lce_api.cpp", ["-x", "hip"], "lce_api")] + [
     ("ce_rows_inst.hip", [f"-DLCE_BF16={b}", f"-DLCE_KR={kr}", f"-DLCE_KL={kl}", "-DLCE_UA=0"], f"ce_rows_{b}_{kr}_{kl}")
     for b in (1, 0) for kr, kl in FAMILIES] + [

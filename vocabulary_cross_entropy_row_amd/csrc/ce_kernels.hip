@@ -320,7 +320,7 @@ LCE_MR_FAMILIES(LCE_MR_DECL)
 #undef LCE_MR_DECL
 
 // Half-row families compiled from ce_rows_half.hip: rounds of 960 vectors per half row.
-#define LCE_HALF_FAMILIES(X) X(5) X(9) X(10)
+#define LCE_HALF_FAMILIES(X) X(5) X(6) X(7) X(8) X(9) X(10)
 #define LCE_HALF_DECL(kh)                                                       \
     hipError_t launch_rows_half_0_##kh(const CEArgs &, int, hipStream_t);      \
     hipError_t launch_rows_half_1_##kh(const CEArgs &, int, hipStream_t);
@@ -390,9 +390,11 @@ bool ce_half_plan(const void *logits, int64_t ld, bool is_bf16, int64_t n, int64
 #define LCE_HALF_ENTRY(k) k,
     static const int fam[] = {LCE_HALF_FAMILIES(LCE_HALF_ENTRY)};
 #undef LCE_HALF_ENTRY
-    // Half rows of 5 rounds pay off only while a CU sees few rows (2048 x 65536: 100.8 against 104.4 us
-    // per call); with 32 rows per CU the persistent row kernel's dynamic walk is as fast.
-    if (need < 9 && n > 4096) return false;
+    // Half rows of 6-8 rounds beat the persistent row kernel at any row count (2048 x 92160: 143 against
+    // 152 us per call, 8192 x 100352: 552 against 562-579 us; 8 rounds about even), those of 5 rounds
+    // only while a CU sees few rows (2048 x 65536: 100.8 against 104.4 us); with 32 rows per CU the
+    // persistent kernel's dynamic walk is as fast there.
+    if (need == 5 && n > 4096) return false;
     for (int f : fam)
         if (f == need) {
             *kh = f;
